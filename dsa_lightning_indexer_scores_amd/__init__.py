@@ -1,0 +1,284 @@
+"""IndexCache over DSA lightning-indexer scores, native on AMD MI355X (gfx950).
+
+Thin Python binding of the C ABI in include/indexcache.h (libindexcache.so,
+built in-tree by ``python -m dsa_lightning_indexer_scores_amd.build_lib``).
+This module only marshals arguments: torch supplies device memory and the
+current HIP stream, and every step of the computation runs in the library's
+HIP kernels.  There is no fallback: if the library is missing, every call
+raises.
+
+Functions mirror the C entry points (without the ``ic_`` prefix):
+  indexer_topk(q_I, w, k_I, k)          -> idx [B, Lq, k] int32
+  indexer_scores(q_I, w, k_I)           -> scores [B, Lq, row_stride] fp32
+  topk_rows(scores, first_len, k)       -> idx [rows, k] int32
+  sparse_attn(q, kv, idx)               -> out [B, Lq, H, d] bf16
+  run_stack(pattern, layers, k)         -> (outs, idx_cache, stats)
+  decode_step(pattern, layers, seq_len, k) -> (outs, idx_cache, stats)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libindexcache.so")
+
+IC_OK, IC_ERR_ARG, IC_ERR_SHAPE, IC_ERR_DTYPE, IC_ERR_PATTERN = 0, 1, 2, 3, 4
+IC_ERR_NO_CACHED_INDICES, IC_ERR_WORKSPACE, IC_ERR_HIP = 5, 6, 7
+IC_BF16, IC_FP8_E4M3 = 0, 1
+IC_OP_INDEXER_TOPK, IC_OP_SPARSE_ATTN, IC_OP_RUN_STACK, IC_OP_DECODE_STEP, IC_OP_INDEXER_SCORES = 0, 1, 2, 3, 4
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "Lq", "Lk", "pos0", "H_I", "d_I", "k", "H", "d", "idx_dtype", "chunk")]
+
+
+class Layer(ctypes.Structure):
+    _fields_ = [("q_I", ctypes.c_void_p), ("w", ctypes.c_void_p), ("k_I", ctypes.c_void_p),
+                ("q", ctypes.c_void_p), ("kv", ctypes.c_void_p), ("out", ctypes.c_void_p)]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("layers", "indexer_calls", "attn_calls", "score_tiles")]
+
+    def as_dict(self) -> Dict[str, int]:
+        return {n: int(getattr(self, n)) for n, _ in self._fields_}
+
+
+class ICError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"ic status {status}: {msg}")
+        self.status = status
+
+
+class NoCachedIndices(ICError):
+    """An S layer came before any F layer (the pages' 'No cached indices available')."""
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libindexcache.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run `python -m dsa_lightning_indexer_scores_amd.build_lib`")
+    L = ctypes.CDLL(LIB_PATH, mode=ctypes.RTLD_GLOBAL)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    P = ctypes.POINTER
+    L.ic_workspace_size.argtypes = [P(Shape), ctypes.c_int]
+    L.ic_workspace_size.restype = sz
+    L.ic_indexer_topk.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
+    L.ic_indexer_scores.argtypes = [P(Shape), vp, vp, vp, vp, i64, vp]
+    L.ic_topk_rows.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+    L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
+    L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
+    L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
+    L.ic_get_stats.argtypes = [P(Stats)]
+    L.ic_last_error.restype = ctypes.c_char_p
+    L.ic_version.restype = i32
+    for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_sparse_attn", "ic_run_stack",
+               "ic_decode_step", "ic_get_stats"):
+        getattr(L, fn).restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return lib().ic_last_error().decode()
+
+
+def version() -> int:
+    return int(lib().ic_version())
+
+
+def _check(status: int):
+    if status != IC_OK:
+        msg = last_error()
+        if status == IC_ERR_NO_CACHED_INDICES:
+            raise NoCachedIndices(status, msg)
+        raise ICError(status, msg)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_IDX_DTYPES = (torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
+
+
+def _idx_dtype(t: torch.Tensor) -> int:
+    return IC_BF16 if t.dtype == torch.bfloat16 else IC_FP8_E4M3
+
+
+def make_shape(B, Lq, Lk, k, H=1, d=64, H_I=1, d_I=32, idx_dtype=IC_BF16, pos0=0, chunk=0) -> Shape:
+    return Shape(B, Lq, Lk, pos0, H_I, d_I, k, H, d, idx_dtype, chunk)
+
+
+def workspace_size(shape: Shape, op: int) -> int:
+    return int(lib().ic_workspace_size(ctypes.byref(shape), op))
+
+
+def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torch.Tensor]:
+    if nbytes == 0:
+        return ws
+    if ws is not None and ws.numel() >= nbytes and ws.data_ptr() % 256 == 0:
+        return ws
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _indexer_shape(q_I, w, k_I, k, pos0, chunk, H=1, d=64) -> Shape:
+    _need(q_I, "q_I", _IDX_DTYPES, 4)
+    _need(w, "w", (torch.float32,), 3)
+    _need(k_I, "k_I", _IDX_DTYPES, 3)
+    if k_I.dtype != q_I.dtype:
+        raise TypeError("q_I and k_I must have the same dtype")
+    B, Lq, H_I, d_I = q_I.shape
+    if tuple(w.shape) != (B, Lq, H_I) or k_I.shape[0] != B or k_I.shape[2] != d_I:
+        raise ValueError(f"inconsistent shapes q_I {tuple(q_I.shape)}, w {tuple(w.shape)}, k_I {tuple(k_I.shape)}")
+    return make_shape(B, Lq, k_I.shape[1], k, H, d, H_I, d_I, _idx_dtype(q_I), pos0, chunk)
+
+
+def indexer_topk(q_I, w, k_I, k: int, pos0: int = 0, chunk: int = 0, idx=None, ws=None, stream=None):
+    """Lightning-indexer scores + per-query top-k of one F layer -> idx [B, Lq, k] int32."""
+    s = _indexer_shape(q_I, w, k_I, k, pos0, chunk)
+    if idx is None:
+        idx = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=q_I.device)
+    ws = _workspace(workspace_size(s, IC_OP_INDEXER_TOPK), q_I.device, ws)
+    _check(lib().ic_indexer_topk(ctypes.byref(s), _ptr(q_I), _ptr(w), _ptr(k_I), _ptr(idx), _ptr(ws),
+                                 0 if ws is None else ws.numel(), _stream(stream)))
+    return idx
+
+
+def indexer_scores(q_I, w, k_I, pos0: int = 0, row_stride: Optional[int] = None, scores=None, stream=None):
+    """Raw fp32 indexer scores [B, Lq, row_stride]; row t is valid for keys 0..pos0+t."""
+    s = _indexer_shape(q_I, w, k_I, 1, pos0, 0)
+    row_stride = s.pos0 + s.Lq if row_stride is None else row_stride
+    if scores is None:
+        scores = torch.full((s.B, s.Lq, row_stride), float("nan"), dtype=torch.float32, device=q_I.device)
+    _check(lib().ic_indexer_scores(ctypes.byref(s), _ptr(q_I), _ptr(w), _ptr(k_I), _ptr(scores),
+                                   row_stride, _stream(stream)))
+    return scores
+
+
+def topk_rows(scores, first_len: int, k: int, idx=None, stream=None):
+    """Top-k of score rows [rows, row_stride]; row r has first_len + r visible entries."""
+    _need(scores, "scores", (torch.float32,), 2)
+    rows, stride = scores.shape
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    _check(lib().ic_topk_rows(_ptr(scores), stride, rows, first_len, k, _ptr(idx), _stream(stream)))
+    return idx
+
+
+def _attn_shape(q, kv, k, pos0=0) -> Shape:
+    _need(q, "q", (torch.bfloat16,), 4)
+    _need(kv, "kv", (torch.bfloat16,), 4)
+    B, Lq, H, d = q.shape
+    if kv.shape[0] != B or kv.shape[2] != 2 or kv.shape[3] != d:
+        raise ValueError(f"kv must be [B, Lk, 2, d]; got {tuple(kv.shape)} for q {tuple(q.shape)}")
+    return make_shape(B, Lq, kv.shape[1], k, H, d, pos0=pos0)
+
+
+def sparse_attn(q, kv, idx, out=None, stream=None):
+    """Sparse attention over the selected rows -> out [B, Lq, H, d] bf16."""
+    _need(idx, "idx", (torch.int32,), 3)
+    s = _attn_shape(q, kv, idx.shape[2], pos0=max(0, kv.shape[1] - q.shape[1]))
+    if tuple(idx.shape[:2]) != (s.B, s.Lq):
+        raise ValueError("idx must be [B, Lq, k]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check(lib().ic_sparse_attn(ctypes.byref(s), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), None, 0, _stream(stream)))
+    return out
+
+
+def _layers_struct(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], outs: List[torch.Tensor]):
+    arr = (Layer * len(layers))()
+    for i, lay in enumerate(layers):
+        arr[i] = Layer(_ptr(lay.get("q_I")), _ptr(lay.get("w")), _ptr(lay.get("k_I")), _ptr(lay["q"]),
+                       _ptr(lay["kv"]), _ptr(outs[i]))
+    return arr
+
+
+def _stack_shape(pattern, layers, k, chunk, pos0):
+    first_f = next((l for c, l in zip(pattern, layers) if c in "F1" and "q_I" in l), None)
+    q = layers[0]["q"]
+    s = _attn_shape(q, layers[0]["kv"], k, pos0)
+    if first_f is not None:
+        si = _indexer_shape(first_f["q_I"], first_f["w"], first_f["k_I"], k, pos0, chunk)
+        s.H_I, s.d_I, s.idx_dtype, s.chunk = si.H_I, si.d_I, si.idx_dtype, si.chunk
+        if si.Lk != s.Lk:
+            raise ValueError("k_I and kv must have the same row capacity")
+    for lay in layers:
+        _need(lay["q"], "q", (torch.bfloat16,), 4)
+        _need(lay["kv"], "kv", (torch.bfloat16,), 4)
+        if tuple(lay["q"].shape) != tuple(q.shape) or tuple(lay["kv"].shape) != tuple(layers[0]["kv"].shape):
+            raise ValueError("every layer must have the same q and kv shapes")
+    return s
+
+
+def run_stack(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, chunk: int = 0, pos0: int = 0,
+              outs: Optional[List[torch.Tensor]] = None, idx_cache=None, ws=None, stream=None):
+    """Prefill an F/S stack.  layers[l]: q, kv (+ q_I, w, k_I on F layers)."""
+    s = _stack_shape(pattern, layers, k, chunk, pos0)
+    dev = layers[0]["q"].device
+    if outs is None:
+        outs = [torch.empty_like(l["q"]) for l in layers]
+    if idx_cache is None:
+        idx_cache = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_size(s, IC_OP_RUN_STACK), dev, ws)
+    arr = _layers_struct(pattern, layers, outs)
+    st = Stats()
+    _check(lib().ic_run_stack(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(idx_cache), _ptr(ws),
+                              0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
+    return outs, idx_cache, st.as_dict()
+
+
+def decode_step(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], seq_len: torch.Tensor, k: int,
+                outs: Optional[List[torch.Tensor]] = None, idx_cache=None, ws=None, stream=None):
+    """One decode step.  layers[l]: q [B,1,H,d], kv [B,cap,2,d] (+ q_I [B,1,H_I,d_I], w [B,1,H_I], k_I [B,cap,d_I])."""
+    _need(seq_len, "seq_len", (torch.int32,), 1)
+    s = _stack_shape(pattern, layers, k, 0, 0)
+    s.pos0 = 0
+    dev = layers[0]["q"].device
+    if outs is None:
+        outs = [torch.empty_like(l["q"]) for l in layers]
+    if idx_cache is None:
+        idx_cache = torch.empty((s.B, 1, k), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_size(s, IC_OP_DECODE_STEP), dev, ws)
+    arr = _layers_struct(pattern, layers, outs)
+    st = Stats()
+    _check(lib().ic_decode_step(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(seq_len), _ptr(idx_cache),
+                                _ptr(ws), 0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
+    return outs, idx_cache, st.as_dict()
+
+
+def get_stats() -> Dict[str, int]:
+    st = Stats()
+    _check(lib().ic_get_stats(ctypes.byref(st)))
+    return st.as_dict()

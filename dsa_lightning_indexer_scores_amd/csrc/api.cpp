@@ -1,0 +1,385 @@
+// C ABI of the IndexCache hot path: argument validation, workspace sizing,
+// the F/S layer-stack driver (prefill and decode) and the index cache.
+//
+// Stack semantics ("Indexcache Sparse Attention Acceleration", Step 3, and
+// "When the Optimizer Becomes the Bottleneck", "The Redundancy That Was
+// Sitting There"): an F layer computes fresh top-k indices and overwrites the
+// one cached index tensor; an S layer reuses whatever the nearest preceding F
+// layer left there; an S layer with nothing cached is an error; the cache is
+// per call (cleared between sequences, as the skill page's Common Pitfalls
+// ask).  The per-layer branch is the only difference between F and S layers.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/indexcache.h"
+#include "common.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local ic_stats g_stats = {0, 0, 0, 0};
+
+constexpr int kDefaultChunk = 4096;
+constexpr int kMaxK = 4096;
+
+ic_status fail(ic_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+ic_status fail(ic_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+ic_status hip_fail(hipError_t e, const char* what) {
+    return fail(IC_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int chunk_of(const ic_shape& s) { return s.chunk == 0 ? kDefaultChunk : s.chunk; }
+
+// Sizes the kernels support; `decode` relaxes the prefill position checks.
+ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode) {
+    if (!sp) return fail(IC_ERR_ARG, "shape is NULL");
+    const ic_shape& s = *sp;
+    if (s.B < 1 || s.Lq < 1 || s.Lk < 1) return fail(IC_ERR_SHAPE, "B, Lq, Lk must be >= 1 (got %d, %d, %d)", s.B, s.Lq, s.Lk);
+    if (decode) {
+        if (s.Lq != 1) return fail(IC_ERR_SHAPE, "decode needs Lq == 1 (got %d)", s.Lq);
+    } else {
+        if (s.pos0 < 0) return fail(IC_ERR_SHAPE, "pos0 must be >= 0 (got %d)", s.pos0);
+        if ((int64_t)s.pos0 + s.Lq > s.Lk)
+            return fail(IC_ERR_SHAPE, "pos0 + Lq (%lld) exceeds Lk (%d)", (long long)s.pos0 + s.Lq, s.Lk);
+    }
+    if (s.k < 1 || s.k > kMaxK) return fail(IC_ERR_SHAPE, "k must be in 1..%d (got %d)", kMaxK, s.k);
+    if (s.H < 1 || s.H > 4096) return fail(IC_ERR_SHAPE, "H must be in 1..4096 (got %d)", s.H);
+    if (s.d != 64 && s.d != 128) return fail(IC_ERR_SHAPE, "d must be 64 or 128 (got %d)", s.d);
+    if (need_indexer) {
+        if (s.idx_dtype != IC_BF16 && s.idx_dtype != IC_FP8_E4M3)
+            return fail(IC_ERR_DTYPE, "idx_dtype must be IC_BF16 or IC_FP8_E4M3 (got %d)", s.idx_dtype);
+        if (s.H_I < 1 || s.H_I > 64) return fail(IC_ERR_SHAPE, "H_I must be in 1..64 (got %d)", s.H_I);
+        if (s.d_I != 32 && s.d_I != 64 && s.d_I != 128)
+            return fail(IC_ERR_SHAPE, "d_I must be 32, 64 or 128 (got %d)", s.d_I);
+        if (s.chunk != 0 && (s.chunk < 16 || s.chunk > 65536 || s.chunk % 16 != 0))
+            return fail(IC_ERR_SHAPE, "chunk must be 0 or a multiple of 16 in 16..65536 (got %d)", s.chunk);
+    }
+    return IC_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+// Score tile of the prefill indexer: chunk rows x (pos0 + Lq) columns, fp32.
+size_t indexer_ws(const ic_shape& s) {
+    const int64_t rows = std::min<int64_t>(chunk_of(s), s.Lq);
+    return (size_t)round_up(rows * round_up((int64_t)s.pos0 + s.Lq, 4) * 4, 256);
+}
+
+int decode_splits(const ic_shape& s) {
+    const int HG = (s.H + 15) / 16;
+    int want = (1024 + s.B * HG - 1) / (s.B * HG);
+    int cap = std::max(1, s.k / 128);
+    return std::max(1, std::min(want, cap));
+}
+
+size_t decode_ws(const ic_shape& s) {
+    const size_t scores = (size_t)round_up((int64_t)s.B * s.Lk * 4, 256);
+    return scores + round_up(sparse_attn_ws_bytes(s.B, s.H, s.d, decode_splits(s)), 256);
+}
+
+ic_status check_ws(const void* ws, size_t have, size_t need) {
+    if (need == 0) return IC_OK;
+    if (!ws) return fail(IC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return fail(IC_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (have < need) return fail(IC_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", have, need);
+    return IC_OK;
+}
+
+size_t elem_bytes(int dtype) { return dtype == IC_FP8_E4M3 ? 1 : 2; }
+
+// a1 + a2 for every sequence of the call: score tiles of <= chunk queries, then top-k into idx.
+ic_status run_indexer_topk(const ic_shape& s, const void* q_I, const float* w, const void* k_I, int32_t* idx,
+                           void* ws, hipStream_t st, int64_t* tiles) {
+    const int chunk = chunk_of(s);
+    const size_t eb = elem_bytes(s.idx_dtype);
+    float* tile = static_cast<float*>(ws);
+    for (int b = 0; b < s.B; ++b) {
+        const uint8_t* qb = static_cast<const uint8_t*>(q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
+        const float* wb = w + (size_t)b * s.Lq * s.H_I;
+        const uint8_t* kb = static_cast<const uint8_t*>(k_I) + (size_t)b * s.Lk * s.d_I * eb;
+        for (int c0 = 0; c0 < s.Lq; c0 += chunk) {
+            const int nq = std::min(chunk, s.Lq - c0);
+            const int64_t stride = round_up((int64_t)s.pos0 + c0 + nq, 4);
+            ic_indexer_args a;
+            a.q_I = qb;
+            a.w = wb;
+            a.k_I = kb;
+            a.scores = tile;
+            a.row_stride = stride;
+            a.q_begin = c0;
+            a.nq = nq;
+            a.pos_begin = s.pos0 + c0;
+            a.H_I = s.H_I;
+            a.d_I = s.d_I;
+            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+            hipError_t e = launch_indexer_prefill(a, st);
+            if (e != hipSuccess) return hip_fail(e, "indexer launch");
+            ic_topk_args t;
+            t.scores = tile;
+            t.row_stride = stride;
+            t.rows = nq;
+            t.first_len = s.pos0 + c0 + 1;
+            t.seq_len = nullptr;
+            t.k = s.k;
+            t.idx = idx + ((size_t)b * s.Lq + c0) * s.k;
+            t.max_len = s.pos0 + c0 + nq;
+            e = launch_topk(t, st);
+            if (e != hipSuccess) return hip_fail(e, "top-k launch");
+            if (tiles) ++*tiles;
+        }
+    }
+    return IC_OK;
+}
+
+ic_status run_attn(const ic_shape& s, int nq_per_seq, const void* q, const void* kv, const int32_t* idx, void* out,
+                   int nsplit, float* part, hipStream_t st) {
+    ic_attn_args a;
+    a.q = q;
+    a.kv = kv;
+    a.idx = idx;
+    a.out = out;
+    a.kv_seq_stride = (int64_t)s.Lk * 2 * s.d;
+    a.Lk = s.Lk;
+    a.nq = s.B * nq_per_seq;
+    a.q_per_seq = nq_per_seq;
+    a.H = s.H;
+    a.d = s.d;
+    a.k = s.k;
+    a.nsplit = nsplit;
+    a.ws = part;
+    hipError_t e = launch_sparse_attn(a, st);
+    if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+    return IC_OK;
+}
+
+// Pattern check shared by prefill and decode: charset, length, S before any F.
+ic_status check_stack(const char* pattern, int32_t n_layers, const ic_layer* layers) {
+    if (!pattern) return fail(IC_ERR_ARG, "pattern is NULL");
+    if (n_layers < 1) return fail(IC_ERR_ARG, "n_layers must be >= 1 (got %d)", n_layers);
+    if (!layers) return fail(IC_ERR_ARG, "layers is NULL");
+    const size_t len = strnlen(pattern, (size_t)n_layers + 1);
+    if (len != (size_t)n_layers)
+        return fail(IC_ERR_PATTERN, "pattern length %zu != n_layers %d", len, n_layers);
+    bool cached = false;
+    for (int l = 0; l < n_layers; ++l) {
+        const char c = pattern[l];
+        const bool full = (c == 'F' || c == '1');
+        if (!full && c != 'S' && c != '0')
+            return fail(IC_ERR_PATTERN, "pattern[%d] = '%c' is not one of F, S, 1, 0", l, c);
+        if (!full && !cached)
+            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available: layer %d is S before any F layer", l);
+        if (full) {
+            cached = true;
+            if (!layers[l].q_I || !layers[l].w || !layers[l].k_I)
+                return fail(IC_ERR_ARG, "F layer %d needs q_I, w and k_I", l);
+        }
+        if (!layers[l].q || !layers[l].kv || !layers[l].out)
+            return fail(IC_ERR_ARG, "layer %d needs q, kv and out", l);
+    }
+    return IC_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ic_workspace_size(const ic_shape* shape, int op) {
+    switch (op) {
+        case IC_OP_INDEXER_TOPK:
+        case IC_OP_RUN_STACK:
+            if (check_shape(shape, true, false) != IC_OK) return 0;
+            return indexer_ws(*shape);
+        case IC_OP_SPARSE_ATTN:
+        case IC_OP_INDEXER_SCORES:
+            if (check_shape(shape, op == IC_OP_INDEXER_SCORES, false) != IC_OK) return 0;
+            return 0;
+        case IC_OP_DECODE_STEP:
+            if (check_shape(shape, true, true) != IC_OK) return 0;
+            return decode_ws(*shape);
+        default:
+            fail(IC_ERR_ARG, "unknown op %d", op);
+            return 0;
+    }
+}
+
+ic_status ic_indexer_topk(const ic_shape* shape, const void* q_I, const float* w, const void* k_I, int32_t* idx,
+                          void* ws, size_t ws_bytes, void* stream) {
+    ic_status r = check_shape(shape, true, false);
+    if (r != IC_OK) return r;
+    if (!q_I || !w || !k_I || !idx) return fail(IC_ERR_ARG, "q_I, w, k_I and idx must be non-NULL");
+    if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
+    return run_indexer_topk(*shape, q_I, w, k_I, idx, ws, (hipStream_t)stream, nullptr);
+}
+
+ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I, float* scores,
+                            int64_t row_stride, void* stream) {
+    ic_status r = check_shape(shape, true, false);
+    if (r != IC_OK) return r;
+    if (!q_I || !w || !k_I || !scores) return fail(IC_ERR_ARG, "q_I, w, k_I and scores must be non-NULL");
+    const ic_shape& s = *shape;
+    if (row_stride < (int64_t)s.pos0 + s.Lq) return fail(IC_ERR_SHAPE, "row_stride %lld < pos0 + Lq", (long long)row_stride);
+    const size_t eb = elem_bytes(s.idx_dtype);
+    for (int b = 0; b < s.B; ++b) {
+        ic_indexer_args a;
+        a.q_I = static_cast<const uint8_t*>(q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
+        a.w = w + (size_t)b * s.Lq * s.H_I;
+        a.k_I = static_cast<const uint8_t*>(k_I) + (size_t)b * s.Lk * s.d_I * eb;
+        a.scores = scores + (size_t)b * s.Lq * row_stride;
+        a.row_stride = row_stride;
+        a.q_begin = 0;
+        a.nq = s.Lq;
+        a.pos_begin = s.pos0;
+        a.H_I = s.H_I;
+        a.d_I = s.d_I;
+        a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+        hipError_t e = launch_indexer_prefill(a, (hipStream_t)stream);
+        if (e != hipSuccess) return hip_fail(e, "indexer launch");
+    }
+    return IC_OK;
+}
+
+ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len, int32_t k,
+                       int32_t* idx, void* stream) {
+    if (!scores || !idx) return fail(IC_ERR_ARG, "scores and idx must be non-NULL");
+    if (rows < 1 || first_len < 1 || k < 1 || k > kMaxK)
+        return fail(IC_ERR_SHAPE, "need rows >= 1, first_len >= 1, 1 <= k <= %d", kMaxK);
+    if ((int64_t)first_len + rows - 1 > row_stride)
+        return fail(IC_ERR_SHAPE, "last row length %lld exceeds row_stride %lld",
+                    (long long)first_len + rows - 1, (long long)row_stride);
+    ic_topk_args t;
+    t.scores = scores;
+    t.row_stride = row_stride;
+    t.rows = rows;
+    t.first_len = first_len;
+    t.seq_len = nullptr;
+    t.k = k;
+    t.idx = idx;
+    t.max_len = first_len + rows - 1;
+    hipError_t e = launch_topk(t, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return IC_OK;
+}
+
+ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    ic_status r = check_shape(shape, false, false);
+    if (r != IC_OK) return r;
+    if (!q || !kv || !idx || !out) return fail(IC_ERR_ARG, "q, kv, idx and out must be non-NULL");
+    return run_attn(*shape, shape->Lq, q, kv, idx, out, 1, nullptr, (hipStream_t)stream);
+}
+
+ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape* shape,
+                       int32_t* idx_cache, void* ws, size_t ws_bytes, ic_stats* stats, void* stream) {
+    ic_status r = check_shape(shape, true, false);
+    if (r != IC_OK) return r;
+    if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
+    if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
+    hipStream_t st = (hipStream_t)stream;
+    ic_stats cnt = {0, 0, 0, 0};
+    bool cached = false;                       // the index cache starts empty on every call
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        if (pattern[l] == 'F' || pattern[l] == '1') {
+            r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles);
+            if (r != IC_OK) return r;
+            cached = true;
+            ++cnt.indexer_calls;
+        } else if (!cached) {
+            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available");
+        }
+        r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
+        if (r != IC_OK) return r;
+        ++cnt.attn_calls;
+        ++cnt.layers;
+    }
+    g_stats = cnt;
+    if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape* shape,
+                         const int32_t* seq_len, int32_t* idx_cache, void* ws, size_t ws_bytes, ic_stats* stats,
+                         void* stream) {
+    ic_status r = check_shape(shape, true, true);
+    if (r != IC_OK) return r;
+    if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
+    if (!seq_len || !idx_cache) return fail(IC_ERR_ARG, "seq_len and idx_cache must be non-NULL");
+    if ((r = check_ws(ws, ws_bytes, decode_ws(*shape))) != IC_OK) return r;
+    const ic_shape& s = *shape;
+    hipStream_t st = (hipStream_t)stream;
+    float* scores = static_cast<float*>(ws);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((int64_t)s.B * s.Lk * 4, 256));
+    const int nsplit = decode_splits(s);
+    ic_stats cnt = {0, 0, 0, 0};
+    bool cached = false;
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        if (pattern[l] == 'F' || pattern[l] == '1') {
+            ic_indexer_decode_args a;
+            a.q_I = L.q_I;
+            a.w = L.w;
+            a.k_I = L.k_I;
+            a.seq_len = seq_len;
+            a.scores = scores;
+            a.B = s.B;
+            a.Lk = s.Lk;
+            a.H_I = s.H_I;
+            a.d_I = s.d_I;
+            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+            hipError_t e = launch_indexer_decode(a, st);
+            if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
+            ic_topk_args t;
+            t.scores = scores;
+            t.row_stride = s.Lk;
+            t.rows = s.B;
+            t.first_len = 0;
+            t.seq_len = seq_len;
+            t.k = s.k;
+            t.idx = idx_cache;
+            t.max_len = s.Lk;
+            e = launch_topk(t, st);
+            if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
+            cached = true;
+            ++cnt.indexer_calls;
+            ++cnt.score_tiles;
+        } else if (!cached) {
+            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available");
+        }
+        r = run_attn(s, 1, L.q, L.kv, idx_cache, L.out, nsplit, part, st);
+        if (r != IC_OK) return r;
+        ++cnt.attn_calls;
+        ++cnt.layers;
+    }
+    g_stats = cnt;
+    if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+ic_status ic_get_stats(ic_stats* out) {
+    if (!out) return fail(IC_ERR_ARG, "out is NULL");
+    *out = g_stats;
+    return IC_OK;
+}
+
+const char* ic_last_error(void) { return g_err.c_str(); }
+
+int32_t ic_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,266 @@
+// Sparse gather attention over the top-k rows, on gfx950 MFMA.
+//
+// "IndexCache: Accelerating Sparse Attention via Cross-Layer Index Reuse"
+// (arXiv abstract): with the indexer's top-k, core attention runs over k
+// tokens instead of L.  Per query and head,
+//     out = sum_s softmax_s(q . K[s] / sqrt(d)) V[s],   s over idx (-1 skipped),
+// with one KV head shared by all query heads; a token's row is [K | V].
+//
+// One wave owns one (query, group of 16 heads[, key split]).  Per step of 32
+// selected rows:
+//   S^T (32 keys x 16 heads) = K Q^T : K fragments are gathered straight
+//       from HBM (16 contiguous bytes per lane, 64 bytes per row per load);
+//   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
+//       lane % 16) is also the layout of O^T below, so the running max and
+//       rescale never leave the lane;
+//   O^T (d x 16 heads) += V^T P^T : V rows are gathered with coalesced
+//       16-byte loads into the wave's LDS tile and read back transposed with
+//       ds_read_b64_tr_b16; P^T is the S^T accumulator packed to bf16 (its
+//       k order matches the transposed read, so no shuffle is needed).
+// Decode splits a query's rows over several waves (split-K) and merges the
+// partial (max, sum, O) in a fixed order, so results are deterministic.
+#include "common.h"
+
+using namespace ic;
+
+namespace {
+
+constexpr int ATT_NW = 4;
+constexpr int KT = 32;                  // selected rows per step
+
+template <int D>
+struct AttGeom {
+    static constexpr int NDC = D / 32;  // K=32 chunks of the QK^T contraction
+    static constexpr int NDT = D / 16;  // 16-wide d tiles of the output
+    static constexpr int VSTR = 2 * D + 16;   // LDS bytes per V row (padded)
+    static constexpr int VPIECES = KT * D * 2 / 16;  // 16-byte pieces per V tile
+    static constexpr int VPL = VPIECES / 64;          // per lane
+    static constexpr int PPR = D * 2 / 16;            // pieces per V row
+};
+
+__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+template <int D>
+__global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    uint16_t* __restrict__ out, float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
+    int H, int k, int nsplit, float scale_log2) {
+    using G = AttGeom<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t vlds_all[ATT_NW][KT * G::VSTR];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    const int HG = (H + 15) / 16;
+    const int64_t item = (int64_t)blockIdx.x * ATT_NW + wv;
+    const int sp = (int)(item % nsplit);
+    const int hg = (int)((item / nsplit) % HG);
+    const int64_t qi = item / ((int64_t)nsplit * HG);
+    if (qi >= nq) return;
+    uint8_t* vlds = vlds_all[wv];
+
+    const int seq = (int)(qi / q_per_seq);
+    const uint16_t* kvs = kv + (int64_t)seq * kv_seq_stride;
+    const int32_t* irow = idx + qi * k;
+    const int head = 16 * hg + n;
+
+    // Q^T fragments (B operand): lane (n, g) holds head n, d = 32*dc + 8g .. +7.
+    i32x4 qf[G::NDC];
+#pragma unroll
+    for (int dc = 0; dc < G::NDC; ++dc) {
+        i32x4 v = {0, 0, 0, 0};
+        if (head < H) v = *reinterpret_cast<const i32x4*>(q + (qi * H + head) * D + 32 * dc + 8 * g);
+        qf[dc] = v;
+    }
+
+    // This split's slice of the idx row, in steps of KT.
+    const int per = ((k + nsplit - 1) / nsplit + KT - 1) / KT * KT;
+    const int j_begin = sp * per;
+    const int j_end = min(k, j_begin + per);
+
+    f32x4 o[G::NDT];
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int j0 = j_begin; j0 < j_end; j0 += KT) {
+        const int jl = j0 + (lane & 31);
+        int my_idx = (jl < j_end) ? irow[jl] : -1;
+        if (my_idx >= Lk) my_idx = -1;                       // never read past the KV rows
+        const unsigned long long vb = __ballot(my_idx >= 0);
+        const uint32_t valid = (uint32_t)vb;                 // bit e: entry j0+e is a real row
+        if (valid == 0u) break;                              // -1 padding runs to the row's end
+        const int safe_idx = my_idx >= 0 ? my_idx : 0;
+
+        // Gather V rows of the tile into LDS: piece c -> row c / PPR, byte (c % PPR) * 16.
+        i32x4 vst[G::VPL];
+#pragma unroll
+        for (int i = 0; i < G::VPL; ++i) {
+            const int c = lane + 64 * i;
+            const int key = c / G::PPR;
+            const int row = __shfl(safe_idx, key);
+            vst[i] = *reinterpret_cast<const i32x4*>(kvs + ((int64_t)row * 2 + 1) * D + (c % G::PPR) * 8);
+        }
+        // K fragments (A operand of S^T): lane (m, g) -> key 16*kt + m, d = 32*dc + 8g.
+        i32x4 kf[2][G::NDC];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            const int row = __shfl(safe_idx, 16 * kt + n);
+            const uint16_t* kp = kvs + (int64_t)row * 2 * D + 8 * g;
+#pragma unroll
+            for (int dc = 0; dc < G::NDC; ++dc) kf[kt][dc] = *reinterpret_cast<const i32x4*>(kp + 32 * dc);
+        }
+#pragma unroll
+        for (int i = 0; i < G::VPL; ++i) {
+            const int c = lane + 64 * i;
+            *reinterpret_cast<i32x4*>(vlds + (c / G::PPR) * G::VSTR + (c % G::PPR) * 16) = vst[i];
+        }
+
+        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e.
+        f32x4 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < G::NDC; ++dc) acc = mfma_bf16_k32(kf[kt][dc], qf[dc], acc);
+            s[kt] = acc;
+        }
+        float x[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 16 * kt + 4 * g + e;
+                const float v = ((valid >> j) & 1u) ? s[kt][e] * scale_log2 : -INFINITY;
+                x[4 * kt + e] = v;
+                tmax = fmaxf(tmax, v);
+            }
+        tmax = max_xor16(tmax);
+        tmax = max_xor32(tmax);
+        const float m_new = fmaxf(m_run, tmax);              // finite: the tile has a valid row
+        const float alpha = exp2f(m_run - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            x[e] = exp2f(x[e] - m_new);
+            psum += x[e];
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) o[dt] *= alpha;
+        // P^T fragment: slots 0..3 = keys 4g+e, slots 4..7 = keys 16+4g+e.
+        i32x4 pf;
+        pf[0] = (int)pack_bf16x2(x[0], x[1]);
+        pf[1] = (int)pack_bf16x2(x[2], x[3]);
+        pf[2] = (int)pack_bf16x2(x[4], x[5]);
+        pf[3] = (int)pack_bf16x2(x[6], x[7]);
+
+        lds_wave_sync();
+        // O^T += V^T P^T.  Transposed LDS reads: within each 16-lane row g, lane src
+        // points at V[4g + src/4 (+16)][16dt + 4*(src%4)], and receives V[keys][d = 16dt + src].
+        const int src = n;
+        const uint8_t* vr0 = vlds + (4 * g + (src >> 2)) * G::VSTR + (4 * (src & 3)) * 2;
+        const uint8_t* vr1 = vr0 + 16 * G::VSTR;
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) {
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr0 + 32 * dt));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr1 + 32 * dt));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, a0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, a1);
+            const i32x4 vf = {(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1]};
+            o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
+        }
+        lds_wave_sync();
+    }
+
+    l_run = sum_xor16(l_run);
+    l_run = sum_xor32(l_run);
+    if (nsplit == 1) {
+        if (head < H) {
+            const float inv = 1.f / l_run;
+            uint16_t* op = out + (qi * H + head) * D + 4 * g;
+#pragma unroll
+            for (int dt = 0; dt < G::NDT; ++dt) {
+                uint2 v;
+                v.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+                v.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+                *reinterpret_cast<uint2*>(op + 16 * dt) = v;
+            }
+        }
+    } else {
+        // partial: O^T unnormalised [16 heads][D], then (m, l) per head
+        const int64_t pidx = item;                           // ((qi*HG + hg)*nsplit + sp)
+        float* po = part + pidx * (16 * D + 32);
+        float4* dst = reinterpret_cast<float4*>(po + n * D + 4 * g);
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) dst[4 * dt] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+        if (g == 0) {
+            po[16 * D + 2 * n] = m_run;
+            po[16 * D + 2 * n + 1] = l_run;
+        }
+    }
+}
+
+// Merge the nsplit partials of each (query, head group) in split order.
+template <int D>
+__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                          int nq, int H, int nsplit) {
+    const int HG = (H + 15) / 16;
+    const int64_t grp = blockIdx.x;                      // qi * HG + hg
+    const int64_t qi = grp / HG;
+    const int hg = (int)(grp % HG);
+    const float* base = part + grp * nsplit * (16 * D + 32);
+    for (int e = threadIdx.x; e < 16 * D; e += 256) {
+        const int hn = e / D, dd = e % D;
+        const int head = 16 * hg + hn;
+        if (head >= H) continue;
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, base[sp * (16 * D + 32) + 16 * D + 2 * hn]);
+        float num = 0.f, den = 0.f;
+        for (int sp = 0; sp < nsplit; ++sp) {
+            const float* ps = base + sp * (16 * D + 32);
+            const float l = ps[16 * D + 2 * hn + 1];
+            if (l == 0.f) continue;                          // split with no selected rows
+            const float c = exp2f(ps[16 * D + 2 * hn] - M);
+            num += c * ps[hn * D + dd];
+            den += c * l;
+        }
+        const float v = num / den;
+        uint32_t u = __float_as_uint(v);
+        u += 0x7FFFu + ((u >> 16) & 1u);
+        out[(qi * H + head) * D + dd] = (uint16_t)(u >> 16);
+    }
+}
+
+template <int D>
+hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
+    const int HG = (a.H + 15) / 16;
+    const int64_t items = (int64_t)a.nq * HG * a.nsplit;
+    const int64_t blocks = (items + ATT_NW - 1) / ATT_NW;
+    const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
+    hipLaunchKernelGGL((sparse_attn_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.ws,
+                       a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, a.nsplit, scale_log2);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nsplit == 1) return e;
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((int64_t)a.nq * HG)), dim3(256), 0, st,
+                       a.ws, (uint16_t*)a.out, a.nq, a.H, a.nsplit);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit) {
+    if (nsplit <= 1) return 0;
+    const int64_t HG = (H + 15) / 16;
+    return (size_t)nq * HG * nsplit * (16 * d + 32) * sizeof(float);
+}
+
+hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st) {
+    if (a.nq <= 0) return hipSuccess;
+    if (a.d == 128) return attn_launch<128>(a, st);
+    if (a.d == 64) return attn_launch<64>(a, st);
+    return hipErrorInvalidValue;
+}

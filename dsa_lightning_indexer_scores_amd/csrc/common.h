@@ -1,0 +1,123 @@
+// Shared device-side helpers for the gfx950 (CDNA4) kernels: vector types,
+// MFMA wrappers, cross-lane reductions and the launch interface between the
+// C-ABI host code and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ic {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int WAVE = 64;
+
+// ---- MFMA tiles (16 x 16 output; lane l holds column l%16, rows 4*(l/16)+0..3) ----
+// A operand: lane l holds row l%16 and a 1/4 slice of K selected by l/16;
+// B operand: lane l holds column l%16 and the same K slice.  Any consistent
+// lane->K assignment for A and B gives the same contraction.
+
+__device__ __forceinline__ f32x4 mfma_bf16_k32(const i32x4& a, const i32x4& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// fp8 e4m3 x fp8 e4m3, K = 128 (32 bytes per lane); unit block scales.
+__device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// ---- cross-lane sums over the four 16-lane rows of a wave ----
+// x + x from the row 16 lanes away (rows 0<->1, 2<->3).
+__device__ __forceinline__ float sum_xor16(float x) {
+    u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// x + x from the lane 32 away.
+__device__ __forceinline__ float sum_xor32(float x) {
+    u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+    u32x2 r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+    u32x2 r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Order-preserving map of an fp32 score to u32 (larger float -> larger key).
+// -0.0 is folded onto +0.0 first so that the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float f) {
+    f = f + 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    // round-to-nearest-even fp32 -> bf16 (inputs are finite)
+    uint32_t a = __float_as_uint(lo), b = __float_as_uint(hi);
+    a += 0x7FFFu + ((a >> 16) & 1u);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (a >> 16) | (b & 0xFFFF0000u);
+}
+
+}  // namespace ic
+
+// ---- host-side launchers implemented in the .hip files ----
+struct ic_indexer_args {
+    const void* q_I;      // [Lq_total, H_I, d_I] of this sequence, row 0 = first query of the call
+    const float* w;       // [Lq_total, H_I]
+    const void* k_I;      // [Lk, d_I]
+    float* scores;        // tile rows: [nq, row_stride]
+    int64_t row_stride;
+    int32_t q_begin;      // first query (index into q_I / w) of this tile
+    int32_t nq;           // queries in this tile
+    int32_t pos_begin;    // absolute position of query q_begin
+    int32_t H_I, d_I;
+    int32_t fp8;
+};
+hipError_t launch_indexer_prefill(const ic_indexer_args& a, hipStream_t st);
+
+struct ic_indexer_decode_args {
+    const void* q_I;      // [B, H_I, d_I]
+    const float* w;       // [B, H_I]
+    const void* k_I;      // [B, Lk, d_I]
+    const int32_t* seq_len;  // [B] device
+    float* scores;        // [B, Lk]
+    int32_t B, Lk, H_I, d_I, fp8;
+};
+hipError_t launch_indexer_decode(const ic_indexer_decode_args& a, hipStream_t st);
+
+struct ic_topk_args {
+    const float* scores;  // [rows, row_stride]
+    int64_t row_stride;
+    int32_t rows;
+    int32_t first_len;    // visible entries of row 0; row r has first_len + r (when seq_len == NULL)
+    const int32_t* seq_len;  // optional device [rows]: row r has seq_len[r] visible entries
+    int32_t k;
+    int32_t* idx;         // [rows, k]
+    int32_t max_len;      // upper bound of any row's visible length (host-known)
+};
+hipError_t launch_topk(const ic_topk_args& a, hipStream_t st);
+
+struct ic_attn_args {
+    const void* q;        // [nq, H, d] bf16
+    const void* kv;       // per sequence [Lk, 2, d] bf16; sequence of query i = i / q_per_seq
+    const int32_t* idx;   // [nq, k]
+    void* out;            // [nq, H, d] bf16
+    int64_t kv_seq_stride;   // elements between sequences in kv
+    int32_t Lk;              // KV rows per sequence (idx entries >= Lk are ignored)
+    int32_t nq, q_per_seq, H, d, k;
+    // split-K (decode): nsplit > 1 writes partials to ws and combines
+    int32_t nsplit;
+    float* ws;
+};
+hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st);
+size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit);

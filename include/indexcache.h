@@ -1,0 +1,194 @@
+/*
+ * indexcache.h -- C ABI of the IndexCache / DSA hot path on AMD MI355X (gfx950).
+ *
+ * What the library computes (page titles and sections, as cited throughout):
+ *
+ *  - "IndexCache: Accelerating Sparse Attention via Cross-Layer Index Reuse",
+ *    arXiv abstract: DeepSeek Sparse Attention's lightweight lightning
+ *    indexer picks the top-k tokens per query, so core attention costs O(Lk);
+ *    the indexer itself stays O(L^2) and runs at every layer.  IndexCache
+ *    splits layers into Full layers, which run their own indexer, and Shared
+ *    layers, which reuse the nearest Full layer's top-k indices.
+ *  - "Indexcache Sparse Attention Acceleration" (agent skill page), Step 3:
+ *    an IndexCacheManager driven by a binary pattern ('1' = F, '0' = S);
+ *    F computes and caches, S returns the cached indices, and an S layer
+ *    with nothing cached is an error.  Practical Guidance, Common Pitfalls:
+ *    the cache must be cleared between sequences.
+ *  - "When the Optimizer Becomes the Bottleneck: A Close Look at IndexCache"
+ *    (blog), "The Redundancy That Was Sitting There": the inference change is
+ *    one conditional branch, and the cache is a single index tensor that is
+ *    overwritten at every F layer (no memory beyond what DSA allocates).
+ *
+ * The indexer score is the DSA lightning indexer's head-weighted ReLU dot
+ * product (named but not written out on the pages):
+ *     I[t,s] = sum_j w[t,j] * max(0, q_I[t,j,:] . k_I[s,:]),   s <= p(t)
+ * with H_I indexer heads sharing one key vector per token, and p(t) the
+ * absolute position of query t (a query sees itself).  Top-k keeps the k
+ * highest scores per query; ties go to the lower key index; each idx row
+ * lists the chosen positions in ascending order, padded with -1 when fewer
+ * than k keys are visible.  Sparse attention is, per head,
+ *     out = softmax_s(q . K[s] / sqrt(d)) V[s]  over s in idx (-1 skipped),
+ * with one KV head shared by all H query heads.
+ *
+ * Conventions for every call:
+ *  - Every tensor argument is a DEVICE pointer owned by the caller.  The
+ *    library never frees, keeps or reallocates it, and never allocates on
+ *    the hot path: scratch space is the caller's workspace `ws`, at least
+ *    ic_workspace_size() bytes, 256-byte aligned.
+ *  - Tensors are dense and row-major in the layouts given below.
+ *      bf16 = IEEE binary32 upper half; fp8 = OCP E4M3FN byte codes.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
+ *    work and return; nothing synchronises the host.
+ *  - Arguments are validated before any launch; a failing call returns a
+ *    non-zero ic_status, launches nothing and leaves outputs untouched.
+ *    ic_last_error() then describes the failure (thread-local string).
+ *    A fault inside a kernel surfaces later, at the caller's next sync.
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef INDEXCACHE_H
+#define INDEXCACHE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ic_status {
+    IC_OK = 0,
+    IC_ERR_ARG = 1,               /* NULL pointer or out-of-range scalar */
+    IC_ERR_SHAPE = 2,             /* sizes outside what the kernels support, or inconsistent */
+    IC_ERR_DTYPE = 3,             /* unknown indexer dtype */
+    IC_ERR_PATTERN = 4,           /* pattern char not in {F,S,1,0}, or length != n_layers */
+    IC_ERR_NO_CACHED_INDICES = 5, /* an S layer precedes every F layer (skill page, Step 3) */
+    IC_ERR_WORKSPACE = 6,         /* workspace NULL, misaligned or smaller than required */
+    IC_ERR_HIP = 7                /* a HIP runtime call failed */
+} ic_status;
+
+typedef enum ic_dtype {
+    IC_BF16 = 0,                  /* q_I / k_I stored as bf16 */
+    IC_FP8_E4M3 = 1               /* q_I / k_I stored as OCP e4m3fn codes */
+} ic_dtype;
+
+/* Sizes of one call.  Limits: B >= 1; 1 <= Lq; pos0 >= 0; pos0 + Lq <= Lk
+ * (prefill); H_I in 1..64; d_I in {32, 64, 128}; k in 1..4096; H >= 1;
+ * d in {64, 128}; chunk 0 (= 4096) or 16..65536 in steps of 16. */
+typedef struct ic_shape {
+    int32_t B;          /* sequences in the batch */
+    int32_t Lq;         /* queries per sequence in this call (decode: 1) */
+    int32_t Lk;         /* row capacity of k_I and kv per sequence (token stride) */
+    int32_t pos0;       /* absolute position of query 0 (prefill; 0 for a fresh prompt) */
+    int32_t H_I;        /* indexer heads */
+    int32_t d_I;        /* indexer head dim */
+    int32_t k;          /* top-k per query */
+    int32_t H;          /* attention query heads (all share one KV head) */
+    int32_t d;          /* attention head dim */
+    int32_t idx_dtype;  /* ic_dtype of q_I and k_I */
+    int32_t chunk;      /* queries per indexer score tile (0 = 4096) */
+} ic_shape;
+
+/* One layer of a stack.  Layouts (per call; B sequences):
+ *   q_I [B, Lq, H_I, d_I] idx_dtype   (F layers; may be NULL on S layers)
+ *   w   [B, Lq, H_I]      fp32        (F layers; may be NULL on S layers)
+ *   k_I [B, Lk, d_I]      idx_dtype   (F layers; may be NULL on S layers)
+ *   q   [B, Lq, H, d]     bf16
+ *   kv  [B, Lk, 2, d]     bf16        (token row = K[d] then V[d])
+ *   out [B, Lq, H, d]     bf16        (written) */
+typedef struct ic_layer {
+    const void*  q_I;
+    const float* w;
+    const void*  k_I;
+    const void*  q;
+    const void*  kv;
+    void*        out;
+} ic_layer;
+
+/* Counters of the last ic_run_stack / ic_decode_step on this thread. */
+typedef struct ic_stats {
+    int64_t layers;          /* layers run */
+    int64_t indexer_calls;   /* F layers whose indexer + top-k ran (== pattern count of F) */
+    int64_t attn_calls;      /* sparse-attention launches (one per layer) */
+    int64_t score_tiles;     /* indexer score tiles (query chunks x sequences) launched */
+} ic_stats;
+
+/* Operation codes for ic_workspace_size. */
+enum {
+    IC_OP_INDEXER_TOPK = 0,
+    IC_OP_SPARSE_ATTN = 1,
+    IC_OP_RUN_STACK = 2,
+    IC_OP_DECODE_STEP = 3,
+    IC_OP_INDEXER_SCORES = 4
+};
+
+/* Bytes of workspace the operation needs for this shape (0 if none).
+ * Returns 0 and sets ic_last_error() for an invalid shape or op. */
+size_t ic_workspace_size(const ic_shape* shape, int op);
+
+/* Lightning indexer + top-k of one F layer (arXiv abstract; agent skill page,
+ * Step 1 gives the (batch, seq_len, k) shape of the result).
+ * Queries t = 0..Lq-1 of every sequence sit at positions pos0 + t and see
+ * keys 0..pos0+t of k_I.  Writes idx [B, Lq, k] int32: the chosen key
+ * positions of each query in ascending order, -1 padded.  The scores are
+ * produced in query chunks of shape.chunk rows inside `ws`; no L x L buffer
+ * is ever formed. */
+ic_status ic_indexer_topk(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+                          int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* The raw fp32 indexer scores of one F layer, for verification and
+ * measurement: scores [B, Lq, row_stride], row t holding keys 0..pos0+t
+ * (entries beyond are not written).  row_stride >= pos0 + Lq.  No workspace. */
+ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+                            float* scores, int64_t row_stride, void* stream);
+
+/* Top-k of caller-supplied score rows with the same rule as ic_indexer_topk:
+ * scores [rows, row_stride] fp32, row r has n_r = first_len + r visible
+ * entries (first_len >= 1, n_r <= row_stride); writes idx [rows, k] int32.
+ * Used to test the selection on chosen inputs (ties, -0.0, k >= n). */
+ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len,
+                       int32_t k, int32_t* idx, void* stream);
+
+/* Sparse attention of one layer (arXiv abstract: core attention over the k
+ * selected tokens): out [B, Lq, H, d] bf16 from q, kv and idx [B, Lq, k]
+ * (entries < 0 are skipped; every row must hold at least one entry >= 0 and
+ * every entry must be < Lk).  Softmax scale 1/sqrt(d), fp32 accumulation. */
+ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx,
+                         void* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Prefill through an F/S layer stack (agent skill page, Step 3; blog, "The
+ * Redundancy That Was Sitting There").  pattern[l] in {'F','1'} runs the
+ * indexer + top-k of layer l into idx_cache; {'S','0'} reuses idx_cache as
+ * the nearest preceding F layer left it.  Every layer then runs sparse
+ * attention with idx_cache into layers[l].out.  The cache is reset at entry
+ * (each call is a fresh sequence batch), so a pattern whose first layer is
+ * S fails with IC_ERR_NO_CACHED_INDICES before any launch.
+ * idx_cache: [B, Lq, k] int32, caller-owned, holds the last F layer's
+ * indices on return.  stats (may be NULL) receives the counters. */
+ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
+                       const ic_shape* shape, int32_t* idx_cache, void* ws, size_t ws_bytes,
+                       ic_stats* stats, void* stream);
+
+/* One decode step through the stack.  shape.Lq must be 1 and shape.Lk is
+ * the cache capacity.  seq_len [B] int32 (device) counts each sequence's
+ * tokens including the new one, whose k_I (F layers) and kv rows the caller
+ * has already written at row seq_len[b]-1; the new query sits at that
+ * position and sees keys 0..seq_len[b]-1 (1 <= seq_len[b] <= Lk).
+ * idx_cache [B, 1, k].  Same pattern and cache rules as ic_run_stack. */
+ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* layers,
+                         const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
+                         void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
+
+/* Counters of the last stack call on this thread. */
+ic_status ic_get_stats(ic_stats* out);
+
+/* Description of the last failure on this thread ("" if none). */
+const char* ic_last_error(void);
+
+/* Library version: major*10000 + minor*100 + patch. */
+int32_t ic_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INDEXCACHE_H */

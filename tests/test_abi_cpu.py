@@ -1,0 +1,103 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every declared symbol,
+and rejects bad arguments before launching anything (no GPU needed for these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dsa_lightning_indexer_scores_amd as ic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "indexcache.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ic_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ic.LIB_PATH):
+        pytest.fail(f"{ic.LIB_PATH} missing: run the build first")
+    return ic.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in indexcache.h but not exported"
+
+
+def test_version_and_empty_error(L):
+    assert ic.version() >= 100
+
+
+def _shape(**kw):
+    base = dict(B=1, Lq=512, Lk=512, k=64, H=4, d=64, H_I=4, d_I=32, idx_dtype=ic.IC_BF16)
+    base.update(kw)
+    return ic.make_shape(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: every call below fails validation first
+
+
+def _layers(pattern):
+    arr = (ic.Layer * len(pattern))()
+    for i, c in enumerate(pattern):
+        full = c in "F1"
+        arr[i] = ic.Layer(FAKE if full else None, FAKE if full else None, FAKE if full else None, FAKE, FAKE, FAKE)
+    return arr
+
+
+def _stack(pattern, n_layers=None, shape=None, ws_bytes=1 << 30):
+    s = shape or _shape()
+    n = len(pattern) if n_layers is None else n_layers
+    return ic.lib().ic_run_stack(pattern.encode(), n, _layers(pattern.ljust(n, "S")[:n] if n else pattern),
+                                 ctypes.byref(s), FAKE, ctypes.c_void_p(0x10000), ws_bytes, None, None)
+
+
+def test_pattern_errors(L):
+    assert _stack("SFSS") == ic.IC_ERR_NO_CACHED_INDICES
+    assert "No cached indices" in ic.last_error()
+    assert _stack("0100") == ic.IC_ERR_NO_CACHED_INDICES
+    assert _stack("FXSS") == ic.IC_ERR_PATTERN
+    assert _stack("FSS", n_layers=4) == ic.IC_ERR_PATTERN
+
+
+def test_shape_and_workspace_errors(L):
+    assert _stack("FSSS", shape=_shape(d=96)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", shape=_shape(d_I=48)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", shape=_shape(H_I=65)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", shape=_shape(k=0)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", shape=_shape(Lq=600)) == ic.IC_ERR_SHAPE        # pos0 + Lq > Lk
+    assert _stack("FSSS", shape=_shape(idx_dtype=7)) == ic.IC_ERR_DTYPE
+    assert _stack("FSSS", shape=_shape(chunk=100)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", ws_bytes=16) == ic.IC_ERR_WORKSPACE
+    need = ic.workspace_size(_shape(), ic.IC_OP_RUN_STACK)
+    assert need >= 512 * 512 * 4                                           # one chunk x visible keys, fp32
+    assert ic.workspace_size(_shape(d=96), ic.IC_OP_RUN_STACK) == 0
+
+
+def test_missing_pointers(L):
+    arr = _layers("FSSS")
+    arr[0].k_I = None
+    s = _shape()
+    r = L.ic_run_stack(b"FSSS", 4, arr, ctypes.byref(s), FAKE, ctypes.c_void_p(0x10000), 1 << 30, None, None)
+    assert r == ic.IC_ERR_ARG
+    dec = _shape(Lq=2)
+    r = L.ic_decode_step(b"FSSS", 4, _layers("FSSS"), ctypes.byref(dec), FAKE, FAKE, ctypes.c_void_p(0x10000),
+                         1 << 30, None, None)
+    assert r == ic.IC_ERR_SHAPE                                            # decode needs Lq == 1
+
+
+def test_workspace_sizes_scale_with_chunk(L):
+    s_full = _shape(Lq=8192, Lk=8192, chunk=0)
+    s_small = _shape(Lq=8192, Lk=8192, chunk=1024)
+    assert ic.workspace_size(s_full, ic.IC_OP_INDEXER_TOPK) == 4096 * 8192 * 4
+    assert ic.workspace_size(s_small, ic.IC_OP_INDEXER_TOPK) == 1024 * 8192 * 4
+    dec = _shape(B=32, Lq=1, Lk=65600, k=2048, H=16, d=128, H_I=64, d_I=128, idx_dtype=ic.IC_FP8_E4M3)
+    assert ic.workspace_size(dec, ic.IC_OP_DECODE_STEP) >= 32 * 65600 * 4
