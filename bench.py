@@ -1,0 +1,266 @@
+#!/usr/bin/env python3
+"""Benchmark of the IndexCache / DSA hot path on one MI355X.
+
+Workload (one timed step = one prefill pass through the whole stack):
+  stack32k  B=1, L=32768 tokens, 16 layers 'FSSS'x4 (one indexer kept per four
+            layers), lightning indexer H_I=64, d_I=128 in fp8 e4m3 with fp32
+            accumulation, top-k 2048, sparse attention H=16 heads on one KV
+            head, d=128, bf16.
+After the timed prefill steps the same run measures, outside the timed loop:
+  decode    decode64k: B=32 sequences with 65536 cached tokens, 24 layers
+            'FSSS'x6, 64 decode steps (one new token per sequence per step);
+  kernels   each kernel of the path timed alone with HIP events on the stream
+            it runs on, priced against its roofline (MFMA for the indexer, HBM
+            for top-k and gather attention);
+  all-F     the same stack with every layer running its indexer (the
+            comparison the pages' prefill speedups are quoted against);
+  oracle    the CPU oracle on a bounded sample of tokens (cpu_baseline).
+
+Prints ONE JSON line.  Inputs are seeded synthetic tensors generated on the
+GPU, resident in HBM before timing starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=2)
+    p.add_argument("--decode-steps", type=int, default=64)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-kernels", action="store_true")
+    p.add_argument("--no-allf", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-tokens", type=int, default=96)
+    return p.parse_args()
+
+
+def timed_events(fn, reps: int):
+    """Average ms of fn() over reps, bracketed by HIP events on the current stream."""
+    import torch
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(reps):
+        fn()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def kernel_rooflines(cfg, layers, ws):
+    """Time each kernel of the prefill path alone; return per-kernel roofline entries."""
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    L, k = cfg.L, cfg.k
+    f = layers[0]
+    pairs = L * (L + 1) // 2
+    out = {}
+    # a1: indexer scores over the full causal triangle (one launch, all 32768 queries)
+    scores = torch.empty((1, L, L), dtype=torch.float32, device="cuda")
+    ic.indexer_scores(f["q_I"], f["w"], f["k_I"], scores=scores, row_stride=L)
+    ms = timed_events(lambda: ic.indexer_scores(f["q_I"], f["w"], f["k_I"], scores=scores, row_stride=L), 3)
+    flops = 2.0 * cfg.H_I * cfg.d_I * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    out["indexer"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS[cfg.idx_dtype],
+                      "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS[cfg.idx_dtype], 4), "ms": round(ms, 4),
+                      "work": f"{flops:.4g} flop = 2*H_I*d_I per causal pair x {pairs} pairs"}
+    # a2: top-k over those rows (one launch, 32768 rows)
+    sc2 = scores[0]
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    ic.topk_rows(sc2, 1, k, idx=idx)
+    ms = timed_events(lambda: ic.topk_rows(sc2, 1, k, idx=idx), 3)
+    by = 4.0 * pairs + 4.0 * k * L
+    gbs = by / (ms * 1e-3) / 1e9
+    out["topk"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                   "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
+                   "work": f"{by:.4g} B = 4 B per visible score + 4k B idx per query"}
+    del scores
+    # a4: gather attention of one layer with those indices
+    idx3 = idx.view(1, L, k)
+    o = torch.empty_like(layers[1]["q"])
+    ic.sparse_attn(layers[1]["q"], layers[1]["kv"], idx3, out=o)
+    ms = timed_events(lambda: ic.sparse_attn(layers[1]["q"], layers[1]["kv"], idx3, out=o), 5)
+    rows = int((idx3 >= 0).sum().item())
+    by = 512.0 * rows + L * (cfg.H * cfg.d * 2 * 2 + 4 * k)
+    gbs = by / (ms * 1e-3) / 1e9
+    out["attention"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                        "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
+                        "work": f"{by:.4g} B = 512 B per selected [K|V] row x {rows} rows + q, out, idx"}
+    return out
+
+
+def cpu_baseline(cfg, layers, n_tokens: int, seed: int = 7):
+    """Time the oracle on n_tokens query positions drawn uniformly from the sequence,
+    each taken through every layer of the stack (F: indexer + top-k + attention; S: attention)."""
+    import numpy as np
+    import oracle as O
+    from dsa_lightning_indexer_scores_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rng = np.random.default_rng(seed)
+    pos = np.sort(rng.choice(cfg.L, size=n_tokens, replace=False))
+    pos_t = __import__("torch").from_numpy(pos).cuda()
+    ref = []
+    for c, lay in zip(cfg.pattern, layers):
+        r = {"q": O.decode_bf16(synth.bits_u16(lay["q"][0].index_select(0, pos_t))),
+             "kv": O.decode_bf16(synth.bits_u16(lay["kv"][0]))}
+        if c in "F1":
+            dq = O.decode_e4m3 if cfg.idx_dtype == "fp8" else O.decode_bf16
+            raw = synth.bits_u8 if cfg.idx_dtype == "fp8" else synth.bits_u16
+            r["q_I"] = dq(raw(lay["q_I"][0].index_select(0, pos_t)))
+            r["w"] = lay["w"][0].index_select(0, pos_t).double().cpu().numpy()
+            r["k_I"] = dq(raw(lay["k_I"][0]))
+        ref.append(r)
+    scale = 1.0 / np.sqrt(cfg.d)
+    t0 = time.perf_counter()
+    for i, p in enumerate(pos):
+        cache = None
+        for c, r in zip(cfg.pattern, ref):
+            if c in "F1":
+                cache = O.topk_row(O.to_decision_precision(O.indexer_scores_row(r["q_I"][i], r["w"][i], r["k_I"], int(p))),
+                                   cfg.k)
+            O.sparse_attn_row(r["q"][i], r["kv"], cache, scale)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_tokens / dt, 3), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_tokens} query positions drawn uniformly from the 32768-token prefill, each through "
+                      f"all {len(cfg.pattern)} layers ('FSSS'x4) of the same seeded inputs; fp64 numpy oracle, "
+                      f"{dt:.1f} s"}
+
+
+def bench_decode(n_steps: int, warm: int = 4):
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+    cfg = synth.WORKLOADS["decode64k"]
+    total = warm + n_steps
+    caches = synth.decode_caches(cfg, device="cuda", steps=total)
+    qs = [synth.decode_queries(cfg, s, device="cuda") for s in range(total)]
+    seq = [torch.full((cfg.B,), cfg.L + s + 1, dtype=torch.int32, device="cuda") for s in range(total)]
+    layers_by_step = [[dict(caches[l], **qs[s][l]) for l in range(cfg.n_layers)] for s in range(total)]
+    outs = [torch.empty_like(l["q"]) for l in layers_by_step[0]]
+    idx_cache = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device="cuda")
+    shape = ic._stack_shape(cfg.pattern, layers_by_step[0], cfg.k, 0, 0)
+    ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_DECODE_STEP), dtype=torch.uint8, device="cuda")
+    for s in range(warm):
+        ic.decode_step(cfg.pattern, layers_by_step[s], seq[s], cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(warm, total):
+        ic.decode_step(cfg.pattern, layers_by_step[s], seq[s], cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return {"tokens_per_s": round(cfg.B * n_steps / dt, 1), "ms_per_step": round(dt * 1e3 / n_steps, 4),
+            "steps": n_steps, "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, "
+                                          "fp8 indexer, H=16, d=128"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+
+    cfg = synth.WORKLOADS["stack32k"]
+    torch.cuda.set_device(0)
+    log(f"generating {cfg.name} inputs on the GPU")
+    layers = synth.prefill_stack(cfg, device="cuda")
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx_cache = torch.empty((cfg.B, cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    shape = ic._stack_shape(cfg.pattern, layers, cfg.k, 0, 0)
+    ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_RUN_STACK), dtype=torch.uint8, device="cuda")
+
+    def step():
+        return ic.run_stack(cfg.pattern, layers, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+
+    for _ in range(args.warmup):
+        _, _, stats = step()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} prefill steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        _, _, stats = step()
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms_step = dt * 1e3 / args.steps
+    value = cfg.B * cfg.L / (dt / args.steps)
+    log(f"prefill {ms_step:.2f} ms/step, {value:.0f} tokens/s, stats {stats}")
+
+    result = {
+        "metric": "stack prefill tokens/s @32K (FSSS) + decode tokens/s; indexer MFMA %",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 indexer (fp32 accumulate) + bf16 attention", "data": "synthetic (seeded, generated on GPU)",
+        "config": {"workload": "stack32k: B=1, L=32768, 16 layers 'FSSS'x4, H_I=64, d_I=128 fp8, k=2048, "
+                               "H=16, d=128 bf16", "global_batch": cfg.B, "seq_len": cfg.L,
+                   "parallelism": "single GPU"},
+        "stack_stats": stats,
+    }
+
+    if not args.no_kernels:
+        log("timing kernels alone")
+        kr = kernel_rooflines(cfg, layers, ws)
+        share = {"indexer": kr["indexer"]["ms"] * cfg.pattern.count("F"),
+                 "topk": kr["topk"]["ms"] * cfg.pattern.count("F"),
+                 "attention": kr["attention"]["ms"] * cfg.n_layers}
+        dom = max(share, key=share.get)
+        result["roofline"] = dict({k: v for k, v in kr[dom].items() if k in ("bound", "achieved", "peak", "unit",
+                                                                          "frac")}, kernel=dom, traffic=None)
+        result["kernels"] = kr
+        result["kernel_ms_in_stack"] = {k: round(v, 3) for k, v in share.items()}
+        result["indexer_mfma_frac"] = kr["indexer"]["frac"]
+
+    if not args.no_allf:
+        log("timing the all-F stack")
+        allf = [dict(layers[(l // 4) * 4], q=layers[l]["q"], kv=layers[l]["kv"]) for l in range(cfg.n_layers)]
+        pat = "F" * cfg.n_layers
+        ic.run_stack(pat, allf, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(2):
+            ic.run_stack(pat, allf, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+        torch.cuda.synchronize()
+        allf_ms = (time.perf_counter() - t0) * 1e3 / 2
+        result["all_f"] = {"ms_per_step": round(allf_ms, 3), "speedup_of_pattern": round(allf_ms / ms_step, 3)}
+
+    if not args.no_decode:
+        log("timing decode64k")
+        del outs
+        result["decode"] = bench_decode(args.decode_steps)
+        result["decode_tokens_per_s"] = result["decode"]["tokens_per_s"]
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(cfg, layers, args.cpu_tokens)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,128 @@
+"""GPU parity at the full workload sizes, in the launch configuration the benchmark
+times, on sampled rows the oracle computes one by one:
+
+  stack32k   L=32768, 16 layers 'FSSS'x4, fp8 indexer, k=2048, chunk 4096
+  long128k   L=131072, 8 layers 'FSSSSSSS', fp8 indexer, 4096-query chunks
+  decode64k  B=32, 65536 cached tokens, 24 layers 'FSSS'x6 (two steps)
+
+Inputs are the seeded tensors the benchmark uses, generated on the GPU by the
+input module and copied back for the oracle.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import dsa_lightning_indexer_scores_amd as ic
+from dsa_lightning_indexer_scores_amd import synth
+from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, sample_rows, summary
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_f_rows(lay_f, idx, rows, p_of, k, H_I, d_I):
+    """Certify sampled idx rows of one F layer against the oracle."""
+    k_I = dec(lay_f["k_I"][0])
+    q_I = dec(lay_f["q_I"][0][torch.as_tensor(rows, device=lay_f["q_I"].device)])
+    w = dec(lay_f["w"][0][torch.as_tensor(rows, device=lay_f["w"].device)])
+    cert, ovl = 0, []
+    for i, t in enumerate(rows):
+        c, o, _ = check_topk_row(idx[t], q_I[i], w[i], k_I, p_of(t), k, H_I, d_I)
+        cert += c
+        ovl.append(o)
+    return cert, float(np.mean(ovl)), float(np.min(ovl))
+
+
+def _check_attn_rows(lay, out, idx, rows, d):
+    worst = 0.0
+    qs = dec(lay["q"][0][torch.as_tensor(rows, device="cuda")])
+    got = dec(out[0][torch.as_tensor(rows, device="cuda")])
+    kv = lay["kv"][0]
+    for i, t in enumerate(rows):
+        sel = idx[t][idx[t] >= 0]
+        kv_sel = dec(kv.index_select(0, torch.as_tensor(sel, device="cuda").long()))
+        ref = O.sparse_attn_row(qs[i], kv_sel, np.arange(len(sel), dtype=np.int32), 1.0 / np.sqrt(d))
+        worst = max(worst, attn_rel_err(got[i], ref))
+    return worst
+
+
+def test_stack32k_sampled():
+    cfg = synth.WORKLOADS["stack32k"]
+    print("[full] stack32k: generating inputs", flush=True)
+    layers = synth.prefill_stack(cfg, device="cuda")
+    outs, idx_last, st = ic.run_stack(cfg.pattern, layers, cfg.k)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == 4 and st["attn_calls"] == 16 and st["score_tiles"] == 4 * 8
+    # the first group alone gives layer 0's indices and must reproduce the stack's outputs
+    outs0, idx0, st0 = ic.run_stack("FSSS", layers[:4], cfg.k)
+    torch.cuda.synchronize()
+    assert st0["indexer_calls"] == 1
+    for l in range(4):
+        assert torch.equal(outs0[l], outs[l]), f"layer {l}: stack and group runs differ"
+    rows = sample_rows(cfg.L, 128, seed=11)
+    print(f"[full] stack32k: checking {len(rows)} rows", flush=True)
+    for name, lay_f, idx, group in (("F0", layers[0], idx0, range(0, 4)), ("F12", layers[12], idx_last, range(12, 16))):
+        idx_np = idx.cpu().numpy()[0]
+        cert, mean_o, min_o = _check_f_rows(lay_f, idx_np, rows, lambda t: t, cfg.k, cfg.H_I, cfg.d_I)
+        worst = max(_check_attn_rows(layers[l], outs[l], idx_np, rows, cfg.d) for l in group)
+        summary(f"stack32k {name}", {"certified": f"{cert}/{len(rows)}", "mean_overlap": mean_o,
+                                     "min_overlap": min_o, "attn_max_rel_err": worst})
+        assert mean_o >= 0.99 and worst <= ATTN_TOL
+
+
+def test_long128k_sampled():
+    cfg = synth.WORKLOADS["long128k"]
+    print("[full] long128k: generating inputs", flush=True)
+    layers = synth.prefill_stack(cfg, device="cuda")
+    outs, idx, st = ic.run_stack(cfg.pattern, layers, cfg.k)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == 1 and st["attn_calls"] == 8 and st["score_tiles"] == cfg.L // 4096
+    rows = sample_rows(cfg.L, 24, seed=12, chunk=4096 * 8)
+    print(f"[full] long128k: checking {len(rows)} rows", flush=True)
+    idx_np = idx.cpu().numpy()[0]
+    cert, mean_o, min_o = _check_f_rows(layers[0], idx_np, rows, lambda t: t, cfg.k, cfg.H_I, cfg.d_I)
+    worst = max(_check_attn_rows(layers[l], outs[l], idx_np, rows, cfg.d) for l in (0, 3, 7))
+    summary("long128k F0", {"certified": f"{cert}/{len(rows)}", "mean_overlap": mean_o, "min_overlap": min_o,
+                            "attn_max_rel_err": worst})
+    assert mean_o >= 0.99 and worst <= ATTN_TOL
+
+
+def test_decode64k_sampled():
+    cfg = synth.WORKLOADS["decode64k"]
+    steps = (0, cfg.decode_steps - 1)
+    print("[full] decode64k: generating caches", flush=True)
+    caches = synth.decode_caches(cfg, device="cuda")
+    cap = cfg.L + cfg.decode_steps
+    for step in steps:
+        qs = synth.decode_queries(cfg, step, device="cuda")
+        layers = [dict(caches[l], **qs[l]) for l in range(cfg.n_layers)]
+        n = cfg.L + step + 1
+        sl = torch.full((cfg.B,), n, dtype=torch.int32, device="cuda")
+        outs, idx_last, st = ic.decode_step(cfg.pattern, layers, sl, cfg.k)
+        torch.cuda.synchronize()
+        assert st["indexer_calls"] == 6 and st["attn_calls"] == 24
+        for g0 in (0, 20):
+            grp = layers[g0:g0 + 4]
+            go, gidx, _ = ic.decode_step("FSSS", grp, sl, cfg.k)
+            torch.cuda.synchronize()
+            for l in range(4):
+                assert torch.equal(go[l], outs[g0 + l]), f"step {step} layer {g0 + l}"
+            idx_np = gidx.cpu().numpy()[:, 0]
+            cert, ovl, worst = 0, [], 0.0
+            for b in (0, 17, 31):
+                f = grp[0]
+                c, o, _ = check_topk_row(idx_np[b], dec(f["q_I"][b, 0]), dec(f["w"][b, 0]), dec(f["k_I"][b, :n]),
+                                         n - 1, cfg.k, cfg.H_I, cfg.d_I)
+                cert += c
+                ovl.append(o)
+                sel = idx_np[b][idx_np[b] >= 0]
+                assert sel.max() < n <= cap
+                for l in range(4):
+                    kv_sel = dec(grp[l]["kv"][b].index_select(0, torch.as_tensor(sel, device="cuda").long()))
+                    ref = O.sparse_attn_row(dec(grp[l]["q"][b, 0]), kv_sel, np.arange(len(sel), dtype=np.int32),
+                                            1.0 / np.sqrt(cfg.d))
+                    worst = max(worst, attn_rel_err(dec(go[l][b, 0]), ref))
+            summary(f"decode64k step {step} group {g0 // 4}", {"certified": f"{cert}/3", "overlap": np.mean(ovl),
+                                                                "attn_max_rel_err": worst})
+            assert np.mean(ovl) >= 0.99 and worst <= ATTN_TOL
+        del outs, layers, qs
