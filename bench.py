@@ -49,8 +49,53 @@ def parse():
     p.add_argument("--no-kernels", action="store_true")
     p.add_argument("--no-allf", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=96)
+    p.add_argument("--cpu-tokens", type=int, default=640)
+    p.add_argument("--only", choices=["indexer", "topk", "attention", "decode", "copy"], default=None,
+                   help="run just one kernel of the path a few times (for profiler counter runs)")
+    p.add_argument("--reps", type=int, default=3)
     return p.parse_args()
+
+
+def only_kernel(which: str, reps: int):
+    """Launch one kernel of the path `reps` times on the stack32k inputs (or a 1 GiB copy),
+    so that a profiler's counters cover exactly that kernel.  Prints one JSON line."""
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+    cfg = synth.WORKLOADS["stack32k"]
+    L, k = cfg.L, cfg.k
+    info = {"only": which, "reps": reps}
+    if which == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(reps):
+            dst.copy_(src)
+        info.update(bytes_read=n, bytes_written=n)
+    elif which == "decode":
+        info.update(bench_decode(4, warm=1))
+    else:
+        layers = synth.prefill_stack(cfg, device="cuda", pattern="FS")
+        f = layers[0]
+        scores = torch.empty((1, L, L), dtype=torch.float32, device="cuda")
+        ic.indexer_scores(f["q_I"], f["w"], f["k_I"], scores=scores, row_stride=L)
+        idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+        torch.cuda.synchronize()
+        if which == "indexer":
+            for _ in range(reps):
+                ic.indexer_scores(f["q_I"], f["w"], f["k_I"], scores=scores, row_stride=L)
+        ic.topk_rows(scores[0], 1, k, idx=idx)
+        if which == "topk":
+            for _ in range(reps):
+                ic.topk_rows(scores[0], 1, k, idx=idx)
+        if which == "attention":
+            del scores
+            o = torch.empty_like(layers[1]["q"])
+            for _ in range(reps):
+                ic.sparse_attn(layers[1]["q"], layers[1]["kv"], idx.view(1, L, k), out=o)
+    torch.cuda.synchronize()
+    print(json.dumps(info), flush=True)
 
 
 def timed_events(fn, reps: int):
@@ -149,31 +194,84 @@ def cpu_baseline(cfg, layers, n_tokens: int, seed: int = 7):
                       f"{dt:.1f} s"}
 
 
-def bench_decode(n_steps: int, warm: int = 4):
+def bench_decode(n_steps: int, warm: int = 2):
+    """decode64k: the 64 steps replay one captured HIP graph of ic_decode_step.
+
+    Each step's new queries (q for every layer, q_I and w for F layers) and the
+    sequence lengths live in one static input buffer; per step a single
+    device-to-device copy loads that step's seeded inputs into it, then the
+    graph replays.  Both the copy and the replay are inside the timed loop.
+    """
     import torch
     import dsa_lightning_indexer_scores_amd as ic
     from dsa_lightning_indexer_scores_amd import synth
     cfg = synth.WORKLOADS["decode64k"]
     total = warm + n_steps
     caches = synth.decode_caches(cfg, device="cuda", steps=total)
-    qs = [synth.decode_queries(cfg, s, device="cuda") for s in range(total)]
-    seq = [torch.full((cfg.B,), cfg.L + s + 1, dtype=torch.int32, device="cuda") for s in range(total)]
-    layers_by_step = [[dict(caches[l], **qs[s][l]) for l in range(cfg.n_layers)] for s in range(total)]
-    outs = [torch.empty_like(l["q"]) for l in layers_by_step[0]]
+    # static input buffer layout: per layer q (+ q_I, w), then seq_len
+    first = synth.decode_queries(cfg, 0, device="cuda")
+    parts = []
+    for lay in first:
+        for name in ("q", "q_I", "w"):
+            if name in lay:
+                parts.append((lay[name].dtype, tuple(lay[name].shape), lay[name].numel() * lay[name].element_size()))
+    parts.append((torch.int32, (cfg.B,), 4 * cfg.B))
+    nbytes = sum(-(-p[2] // 256) * 256 for p in parts)
+    static = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    pregen = torch.empty((total, nbytes), dtype=torch.uint8, device="cuda")
+
+    def views(buf):
+        out, off = [], 0
+        for dt, shape, nb in parts:
+            out.append(buf[off:off + nb].view(dt).view(shape))
+            off += -(-nb // 256) * 256
+        return out
+
+    for s_ in range(total):
+        qs = first if s_ == 0 else synth.decode_queries(cfg, s_, device="cuda")
+        flat = [lay[name] for lay in qs for name in ("q", "q_I", "w") if name in lay]
+        flat.append(torch.full((cfg.B,), cfg.L + s_ + 1, dtype=torch.int32, device="cuda"))
+        for dst, src in zip(views(pregen[s_]), flat):
+            dst.copy_(src)
+    sv = views(static)
+    layers, i = [], 0
+    for l, c in enumerate(cfg.pattern):
+        lay = dict(caches[l])
+        lay["q"] = sv[i]; i += 1
+        if c in "F1":
+            lay["q_I"] = sv[i]; lay["w"] = sv[i + 1]; i += 2
+        layers.append(lay)
+    seq_len = sv[i]
+    outs = [torch.empty_like(l["q"]) for l in layers]
     idx_cache = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device="cuda")
-    shape = ic._stack_shape(cfg.pattern, layers_by_step[0], cfg.k, 0, 0)
+    shape = ic._stack_shape(cfg.pattern, layers, cfg.k, 0, 0)
     ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_DECODE_STEP), dtype=torch.uint8, device="cuda")
-    for s in range(warm):
-        ic.decode_step(cfg.pattern, layers_by_step[s], seq[s], cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    static.copy_(pregen[0])
+    ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    for s_ in range(warm):
+        static.copy_(pregen[s_])
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(warm, total):
-        ic.decode_step(cfg.pattern, layers_by_step[s], seq[s], cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    for s_ in range(warm, total):
+        static.copy_(pregen[s_])
+        g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
+    eager_t0 = time.perf_counter()
+    for s_ in range(warm, min(total, warm + 8)):
+        static.copy_(pregen[s_])
+        ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - eager_t0) * 1e3 / min(n_steps, 8)
     return {"tokens_per_s": round(cfg.B * n_steps / dt, 1), "ms_per_step": round(dt * 1e3 / n_steps, 4),
-            "steps": n_steps, "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, "
-                                          "fp8 indexer, H=16, d=128"}
+            "eager_ms_per_step": round(eager_ms, 4), "steps": n_steps,
+            "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, fp8 indexer, H=16, "
+                        "d=128; one captured graph replayed per step"}
 
 
 def main():
@@ -183,6 +281,9 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.only:
+        only_kernel(args.only, args.reps)
+        return
     import torch
     import dsa_lightning_indexer_scores_amd as ic
     from dsa_lightning_indexer_scores_amd import synth

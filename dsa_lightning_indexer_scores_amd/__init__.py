@@ -56,7 +56,7 @@ class ICError(RuntimeError):
 
 
 class NoCachedIndices(ICError):
-    """An S layer came before any F layer (the pages' 'No cached indices available')."""
+    """An S layer came before any F layer, so there are no cached indices to reuse."""
 
 
 _lib = None

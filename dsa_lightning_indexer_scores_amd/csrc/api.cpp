@@ -79,11 +79,14 @@ size_t indexer_ws(const ic_shape& s) {
     return (size_t)round_up(rows * round_up((int64_t)s.pos0 + s.Lq, 4) * 4, 256);
 }
 
+// Key splits per decode query: enough waves to fill the GPU (~2048), at most one
+// 32-row tile per split, and a multiple of 4 (a workgroup merges 4 splits).
 int decode_splits(const ic_shape& s) {
     const int HG = (s.H + 15) / 16;
-    int want = (1024 + s.B * HG - 1) / (s.B * HG);
-    int cap = std::max(1, s.k / 128);
-    return std::max(1, std::min(want, cap));
+    const int want = (2048 + s.B * HG - 1) / (s.B * HG);
+    const int tiles = (s.k + 31) / 32;
+    const int ns = std::min(want, tiles);
+    return ns < 4 ? 1 : ns / 4 * 4;
 }
 
 size_t decode_ws(const ic_shape& s) {
@@ -181,7 +184,7 @@ ic_status check_stack(const char* pattern, int32_t n_layers, const ic_layer* lay
         if (!full && c != 'S' && c != '0')
             return fail(IC_ERR_PATTERN, "pattern[%d] = '%c' is not one of F, S, 1, 0", l, c);
         if (!full && !cached)
-            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available: layer %d is S before any F layer", l);
+            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: layer %d is S and no F layer precedes it", l);
         if (full) {
             cached = true;
             if (!layers[l].q_I || !layers[l].w || !layers[l].k_I)
@@ -302,7 +305,7 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
             cached = true;
             ++cnt.indexer_calls;
         } else if (!cached) {
-            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available");
+            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
         r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
         if (r != IC_OK) return r;
@@ -360,7 +363,7 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
             ++cnt.indexer_calls;
             ++cnt.score_tiles;
         } else if (!cached) {
-            return fail(IC_ERR_NO_CACHED_INDICES, "No cached indices available");
+            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
         r = run_attn(s, 1, L.q, L.kv, idx_cache, L.out, nsplit, part, st);
         if (r != IC_OK) return r;

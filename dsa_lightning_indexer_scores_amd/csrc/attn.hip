@@ -17,8 +17,9 @@
 //       16-byte loads into the wave's LDS tile and read back transposed with
 //       ds_read_b64_tr_b16; P^T is the S^T accumulator packed to bf16 (its
 //       k order matches the transposed read, so no shuffle is needed).
-// Decode splits a query's rows over several waves (split-K) and merges the
-// partial (max, sum, O) in a fixed order, so results are deterministic.
+// Decode splits a query's rows over several waves (split-K): the 4 waves of a
+// workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
+// the workgroups' partials in a fixed order, so results are deterministic.
 #include "common.h"
 
 using namespace ic;
@@ -190,48 +191,70 @@ __global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
             }
         }
     } else {
-        // partial: O^T unnormalised [16 heads][D], then (m, l) per head
-        const int64_t pidx = item;                           // ((qi*HG + hg)*nsplit + sp)
-        float* po = part + pidx * (16 * D + 32);
-        float4* dst = reinterpret_cast<float4*>(po + n * D + 4 * g);
+        // Split-K: the workgroup's 4 waves hold 4 consecutive splits of one (query, head
+        // group).  Merge them through LDS (the V tiles are no longer needed) and write
+        // one partial: unnormalised O^T [16 heads][D] and (max, sum) per head.
+        float* mo = reinterpret_cast<float*>(vlds_all[0]);   // [4 waves][16 heads][D]
+        float* ml = mo + ATT_NW * 16 * D;                     // [4 waves][16 heads][2]
+        __syncthreads();                                      // every wave is done with its V tile
+        float4* dst = reinterpret_cast<float4*>(mo + (wv * 16 + n) * D + 4 * g);
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) dst[4 * dt] = make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
         if (g == 0) {
-            po[16 * D + 2 * n] = m_run;
-            po[16 * D + 2 * n + 1] = l_run;
+            ml[(wv * 16 + n) * 2] = m_run;
+            ml[(wv * 16 + n) * 2 + 1] = l_run;
+        }
+        __syncthreads();
+        float* po = part + (item / ATT_NW) * (16 * D + 32);   // ((qi*HG + hg)*nsplit/4 + sp/4)
+        for (int e = threadIdx.x; e < 16 * D; e += ATT_NW * 64) {
+            const int hn = e / D;
+            float M = -INFINITY;
+#pragma unroll
+            for (int w = 0; w < ATT_NW; ++w) M = fmaxf(M, ml[(w * 16 + hn) * 2]);
+            float num = 0.f, den = 0.f;
+            if (M != -INFINITY) {
+#pragma unroll
+                for (int w = 0; w < ATT_NW; ++w) {
+                    const float c = exp2f(ml[(w * 16 + hn) * 2] - M);   // 0 for an empty split
+                    num += c * mo[(w * 16) * D + e];
+                    den += c * ml[(w * 16 + hn) * 2 + 1];
+                }
+            }
+            po[e] = num;
+            if (e % D == 0) {
+                po[16 * D + 2 * hn] = M;
+                po[16 * D + 2 * hn + 1] = den;
+            }
         }
     }
 }
 
-// Merge the nsplit partials of each (query, head group) in split order.
+// Merge the partials of each (query, head) in split order: one workgroup per
+// (query, head), one thread per channel.
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                          int nq, int H, int nsplit) {
+__global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                        int H, int nparts) {
     const int HG = (H + 15) / 16;
-    const int64_t grp = blockIdx.x;                      // qi * HG + hg
-    const int64_t qi = grp / HG;
-    const int hg = (int)(grp % HG);
-    const float* base = part + grp * nsplit * (16 * D + 32);
-    for (int e = threadIdx.x; e < 16 * D; e += 256) {
-        const int hn = e / D, dd = e % D;
-        const int head = 16 * hg + hn;
-        if (head >= H) continue;
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsplit; ++sp) M = fmaxf(M, base[sp * (16 * D + 32) + 16 * D + 2 * hn]);
-        float num = 0.f, den = 0.f;
-        for (int sp = 0; sp < nsplit; ++sp) {
-            const float* ps = base + sp * (16 * D + 32);
-            const float l = ps[16 * D + 2 * hn + 1];
-            if (l == 0.f) continue;                          // split with no selected rows
-            const float c = exp2f(ps[16 * D + 2 * hn] - M);
-            num += c * ps[hn * D + dd];
-            den += c * l;
-        }
-        const float v = num / den;
-        uint32_t u = __float_as_uint(v);
-        u += 0x7FFFu + ((u >> 16) & 1u);
-        out[(qi * H + head) * D + dd] = (uint16_t)(u >> 16);
+    const int64_t qi = blockIdx.x / H;
+    const int head = blockIdx.x % H;
+    const int hg = head / 16, hn = head % 16;
+    const float* base = part + (qi * HG + hg) * nparts * (16 * D + 32);
+    const int dd = threadIdx.x;
+    float M = -INFINITY;
+    for (int sp = 0; sp < nparts; ++sp) M = fmaxf(M, base[sp * (16 * D + 32) + 16 * D + 2 * hn]);
+    float num = 0.f, den = 0.f;
+    for (int sp = 0; sp < nparts; ++sp) {
+        const float* ps = base + sp * (16 * D + 32);
+        const float l = ps[16 * D + 2 * hn + 1];
+        if (l == 0.f) continue;                              // split with no selected rows
+        const float c = exp2f(ps[16 * D + 2 * hn] - M);
+        num += c * ps[hn * D + dd];
+        den += c * l;
     }
+    const float v = num / den;
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    out[(qi * H + head) * D + dd] = (uint16_t)(u >> 16);
 }
 
 template <int D>
@@ -245,8 +268,8 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
                        a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, a.nsplit, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nsplit == 1) return e;
-    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((int64_t)a.nq * HG)), dim3(256), 0, st,
-                       a.ws, (uint16_t*)a.out, a.nq, a.H, a.nsplit);
+    hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((int64_t)a.nq * a.H)), dim3(D), 0, st,
+                       a.ws, (uint16_t*)a.out, a.H, a.nsplit / ATT_NW);
     return hipGetLastError();
 }
 
@@ -255,11 +278,12 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
 size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit) {
     if (nsplit <= 1) return 0;
     const int64_t HG = (H + 15) / 16;
-    return (size_t)nq * HG * nsplit * (16 * d + 32) * sizeof(float);
+    return (size_t)nq * HG * (nsplit / ATT_NW) * (16 * d + 32) * sizeof(float);
 }
 
 hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st) {
     if (a.nq <= 0) return hipSuccess;
+    if (a.nsplit > 1 && a.nsplit % ATT_NW != 0) return hipErrorInvalidValue;   // splits merge 4 per workgroup
     if (a.d == 128) return attn_launch<128>(a, st);
     if (a.d == 64) return attn_launch<64>(a, st);
     return hipErrorInvalidValue;

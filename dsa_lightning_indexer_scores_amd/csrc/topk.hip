@@ -1,21 +1,28 @@
 // Per-query top-k over the indexer scores: exact radix select on gfx950.
 //
-// The indexer "selects the top-k most relevant tokens per query" ("IndexCache:
-// Accelerating Sparse Attention via Cross-Layer Index Reuse", arXiv abstract);
-// the agent skill page (Step 1) shapes the result (batch, seq_len, k).  Rule
-// implemented here: the k largest visible scores of a row; among equal scores
-// the lower key index wins; the row is written in ascending key order and
-// padded with -1 when fewer than k keys are visible.
+// In DSA the lightning indexer keeps, for every query, the k keys with the
+// highest scores ("IndexCache: Accelerating Sparse Attention via Cross-Layer
+// Index Reuse", arXiv abstract); the agent skill page (Step 1) gives the
+// result the shape (batch, seq_len, k).  Rule implemented here: the k largest
+// visible scores of a row; among equal scores the lower key index wins; the
+// row is written in ascending key order and padded with -1 when fewer than k
+// keys are visible.
 //
 // One workgroup per row.  Scores become order-preserving u32 keys (-0.0 folded
 // onto +0.0).  The bits shared by the row's smallest and largest key are
 // skipped; the rest are resolved most-significant digit first with 11-bit LDS
 // histograms until the k-th key's prefix is exact or its bin is taken whole.
 // A final pass walks the row in index order and compacts the selected
-// positions with wave ballots and a workgroup prefix sum, so the output is
-// sorted for free and ties resolve to the lowest indices.  Rows of up to
-// LDS_ROW_CAP keys are staged once in LDS; longer rows are re-read from
-// global memory (L2 / MALL) at every pass.
+// positions with wave ballots (mbcnt prefix counts) and a prefix sum over the
+// waves, so the output is sorted for free and ties resolve to the lowest
+// indices.
+//
+// The row is cut into blocks of NT*EPT keys.  In a block, wave w owns the
+// contiguous span [w*64*EPT, (w+1)*64*EPT) and lane l holds its keys
+// 256*j + 4*l + e (j < EPT/4, e < 4): loads are coalesced 16-byte vectors and
+// every pass works out of VGPRs.  Rows of one block (<= 32768 keys with 1024
+// threads) are read from HBM exactly once; longer rows stream their blocks
+// again at every pass (re-reads hit L2 / MALL).
 #include "common.h"
 
 using namespace ic;
@@ -24,29 +31,23 @@ namespace {
 
 constexpr int HIST_BITS = 11;
 constexpr int HIST_BINS = 1 << HIST_BITS;
-constexpr int LDS_ROW_CAP = 36864;   // keys staged in LDS (144 KiB)
-constexpr int EPT = 8;               // elements per thread per emit segment
 
-template <int NT>
-struct TopkShared {
-    uint32_t hist[HIST_BINS];
-    uint32_t wtot[NT / 64];
-    uint32_t wtot2[NT / 64];
-    uint32_t kmin, kmax;
-    uint32_t found_bin, found_above;
-};
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
 
-// Exclusive prefix sum of x over the workgroup (thread order). Returns it; *total gets the sum.
-template <int NT>
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wtot, uint32_t* total) {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    uint32_t v = x;
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        uint32_t y = __shfl_up(v, o);
-        if (lane >= o) v += y;
-    }
-    if (lane == 63) wtot[wv] = v;
+    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+    return x;
+}
+
+// Exclusive prefix over waves of a wave-uniform value; *total gets the sum over all waves.
+// Ends with a barrier, so `wtot` may be reused right after.
+template <int NT>
+__device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wtot, uint32_t* total) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    if (lane == 0) wtot[wv] = wave_total;
     __syncthreads();
     uint32_t before = 0, tot = 0;
 #pragma unroll
@@ -57,164 +58,214 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t x, uint32_t* wtot, 
     }
     __syncthreads();
     *total = tot;
-    return before + v - x;
+    return before;
 }
 
-template <int NT, bool IN_LDS>
+template <int NT, int EPT, bool VEC, bool STREAM>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
                                                   int first_len, const int32_t* __restrict__ seq_len, int k,
                                                   int32_t* __restrict__ idx, int max_len) {
-    extern __shared__ uint32_t keys_lds[];
-    __shared__ TopkShared<NT> sh;
+    constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
+    constexpr int BLOCK = NT * EPT;                  // keys per block
+    __shared__ uint32_t hist[HIST_BINS];
+    __shared__ uint32_t wtot[NT / 64];
+    __shared__ uint32_t kminmax[2], found[2];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    // visible length, clamped to the staged / allocated row (a bad seq_len cannot overrun)
-    const int n = max(1, min(seq_len ? seq_len[row] : first_len + row, max_len));
+    // visible length, clamped to the allocated row (a bad seq_len cannot overrun)
+    const int n = max(1, min(seq_len ? seq_len[row] : first_len + row, STREAM ? max_len : min(max_len, BLOCK)));
     int32_t* out = idx + (int64_t)row * k;
-    const float* src = scores + (int64_t)row * row_stride;
-
-    if (n <= k) {                                   // every visible key is selected
+    if (n <= k) {                                    // every visible key is selected
         for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
         return;
     }
+    const float* src = scores + (int64_t)row * row_stride;
+    const int lane_base = wv * 64 * EPT + 4 * lane;  // element of (round 0, slot 0) within a block
+    const int nblocks = STREAM ? (n + BLOCK - 1) / BLOCK : 1;
 
-    auto key_at = [&](int i) -> uint32_t {
-        if constexpr (IN_LDS) return keys_lds[i];
-        else return score_key(src[i]);
+    uint32_t key[EPT];
+    auto load_block = [&](int blk) {
+        const int b0 = blk * BLOCK + lane_base;
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {
+            const int i0 = b0 + 256 * j;
+            float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if (VEC) {
+                if (i0 < n) {                        // 16 B stay inside the row: row_stride % 4 == 0
+                    const float4 f = *reinterpret_cast<const float4*>(src + i0);
+                    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (i0 + e < n) ? src[i0 + e] : 0.f;
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) key[4 * j + e] = score_key(v[e]);
+        }
     };
+    auto valid = [&](int blk, int j, int e) { return blk * BLOCK + lane_base + 256 * j + e < n; };
 
-    // Stage (or scan) the row: smallest and largest key.
+    // Smallest and largest key of the row.
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-    for (int i = tid; i < n; i += NT) {
-        const uint32_t kk = score_key(src[i]);
-        if constexpr (IN_LDS) keys_lds[i] = kk;
-        lo = min(lo, kk);
-        hi = max(hi, kk);
+    for (int blk = 0; blk < nblocks; ++blk) {
+        load_block(blk);
+#pragma unroll
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (valid(blk, j, e)) { lo = min(lo, key[4 * j + e]); hi = max(hi, key[4 * j + e]); }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
         lo = min(lo, (uint32_t)__shfl_xor(lo, o));
         hi = max(hi, (uint32_t)__shfl_xor(hi, o));
     }
-    if (tid == 0) { sh.kmin = 0xFFFFFFFFu; sh.kmax = 0u; }
+    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; }
     __syncthreads();
-    if (lane == 0) { atomicMin(&sh.kmin, lo); atomicMax(&sh.kmax, hi); }
+    if (lane == 0) { atomicMin(&kminmax[0], lo); atomicMax(&kminmax[1], hi); }
     __syncthreads();
-    const uint32_t kmin = sh.kmin, kmax = sh.kmax;
+    const uint32_t kmin = kminmax[0], kmax = kminmax[1];
 
-    // Radix select state: candidates are keys with (key >> shift) == prefix.
+    // Radix select: candidates are the keys with (key >> shift) == prefix.
     int shift = (kmin == kmax) ? 0 : 32 - __clz(kmin ^ kmax);
     uint32_t prefix = shift >= 32 ? 0u : (kmax >> shift);
-    uint32_t k_rem = (uint32_t)k;                   // still to take among the candidates
-
+    uint32_t k_rem = (uint32_t)k;                    // still to take among the candidates
     while (shift > 0) {
         const int width = min(HIST_BITS, shift);
         const int sh_lo = shift - width;
         const uint32_t mask = (1u << width) - 1u;
         const int nb = 1 << width;
-        for (int b = tid; b < nb; b += NT) sh.hist[b] = 0u;
+        for (int b = tid; b < nb; b += NT) hist[b] = 0u;
         __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-            const uint32_t kk = key_at(i);
-            const uint32_t hi_bits = shift >= 32 ? 0u : (kk >> shift);
-            if (hi_bits == prefix) atomicAdd(&sh.hist[(kk >> sh_lo) & mask], 1u);
+        for (int blk = 0; blk < nblocks; ++blk) {
+            if (STREAM) load_block(blk);
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[4 * j + e];
+                    if (valid(blk, j, e) && (shift >= 32 || (kk >> shift) == prefix))
+                        atomicAdd(&hist[(kk >> sh_lo) & mask], 1u);
+                }
         }
         __syncthreads();
-        // Find bin b with above(b) < k_rem <= above(b) + hist[b], above = count in higher bins.
+        // Bin b with above(b) < k_rem <= above(b) + hist[b]; above = count in higher bins.
         constexpr int BPT = (HIST_BINS + NT - 1) / NT;
-        uint32_t local = 0;
-        uint32_t hv[BPT];
+        uint32_t local = 0, hv[BPT];
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
             const int b = tid * BPT + j;
-            hv[j] = b < nb ? sh.hist[b] : 0u;
+            hv[j] = b < nb ? hist[b] : 0u;
             local += hv[j];
         }
-        // suffix sum over threads: count in bins owned by higher threads
-        uint32_t suf = local;
+        uint32_t suf = local;                        // suffix sum over the lanes of this wave
 #pragma unroll
         for (int o = 1; o < 64; o <<= 1) {
-            uint32_t y = __shfl_down(suf, o);
+            const uint32_t y = __shfl_down(suf, o);
             if (lane + o < 64) suf += y;
         }
-        if (lane == 0) sh.wtot[wv] = suf;
+        if (lane == 0) wtot[wv] = suf;
         __syncthreads();
         uint32_t above = suf - local;
 #pragma unroll
-        for (int i = 0; i < NT / 64; ++i) above += (i > wv) ? sh.wtot[i] : 0u;
+        for (int i = 0; i < NT / 64; ++i) above += (i > wv) ? wtot[i] : 0u;
 #pragma unroll
         for (int j = BPT - 1; j >= 0; --j) {
             const int b = tid * BPT + j;
-            if (b < nb && above < k_rem && k_rem <= above + hv[j]) {
-                sh.found_bin = (uint32_t)b;
-                sh.found_above = above;
-            }
+            if (b < nb && above < k_rem && k_rem <= above + hv[j]) { found[0] = (uint32_t)b; found[1] = above; }
             above += hv[j];
         }
         __syncthreads();
-        const uint32_t fb = sh.found_bin;
-        const uint32_t fa = sh.found_above;
-        const uint32_t in_bin = sh.hist[fb];
+        const uint32_t fb = found[0], fa = found[1];
+        const uint32_t in_bin = hist[fb];
         prefix = (shift >= 32 ? 0u : (prefix << width)) | fb;
         k_rem -= fa;
         shift = sh_lo;
-        __syncthreads();                             // hist / found_* reused next pass
+        __syncthreads();                             // hist, wtot and found are reused
         if (in_bin == k_rem) break;                  // the whole bin is taken: no ties to cut
     }
 
-    // Emit in index order: key prefix above -> selected; equal -> the first k_rem of them.
-    uint32_t eq_run = 0, sel_run = 0;
-    for (int base = 0; base < n; base += NT * EPT) {
-        uint32_t kk[EPT];
-        bool gt[EPT], eq[EPT];
+    // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them.
+    auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
+    uint32_t eq_run = 0, pos_run = 0;                // totals of earlier blocks
+    for (int blk = 0; blk < nblocks; ++blk) {
+        if (STREAM) load_block(blk);
         uint32_t eqc = 0;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            const int i = base + tid * EPT + j;
-            gt[j] = eq[j] = false;
-            if (i < n) {
-                kk[j] = key_at(i);
-                const uint32_t dgt = shift >= 32 ? 0u : (kk[j] >> shift);
-                gt[j] = dgt > prefix;
-                eq[j] = dgt == prefix;
-                eqc += eq[j];
-            }
-        }
+        for (int j = 0; j < NR; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) eqc += valid(blk, j, e) && digit(key[4 * j + e]) == prefix;
         uint32_t eq_tot;
-        uint32_t eq_rank = eq_run + block_excl_scan<NT>(eqc, sh.wtot, &eq_tot);
-        bool sel[EPT];
+        uint32_t eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
+        uint32_t selbits[(EPT + 31) / 32];
+#pragma unroll
+        for (int w = 0; w < (EPT + 31) / 32; ++w) selbits[w] = 0u;
         uint32_t selc = 0;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            sel[j] = gt[j] || (eq[j] && eq_rank < k_rem);
-            eq_rank += eq[j];
-            selc += sel[j];
+        for (int j = 0; j < NR; ++j) {
+            bool eq[4], gt[4];
+            uint32_t before = 0, tot = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = valid(blk, j, e);
+                const uint32_t dg = digit(key[4 * j + e]);
+                eq[e] = ok && dg == prefix;
+                gt[e] = ok && dg > prefix;
+                const uint64_t b = __ballot(eq[e]);
+                before += lanes_below(b);
+                tot += (uint32_t)__popcll(b);
+            }
+            uint32_t r = eq_rank + before;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool sel = gt[e] || (eq[e] && r < k_rem);
+                r += eq[e];
+                if (sel) {
+                    selbits[(4 * j + e) >> 5] |= 1u << ((4 * j + e) & 31);
+                    ++selc;
+                }
+            }
+            eq_rank += tot;
         }
         uint32_t sel_tot;
-        uint32_t pos = sel_run + block_excl_scan<NT>(selc, sh.wtot2, &sel_tot);
+        uint32_t pos = pos_run + waves_scan<NT>(wave_sum(selc), wtot, &sel_tot);
+        const int b0 = blk * BLOCK + lane_base;
 #pragma unroll
-        for (int j = 0; j < EPT; ++j) {
-            if (sel[j] && pos < (uint32_t)k) out[pos++] = base + tid * EPT + j;
+        for (int j = 0; j < NR; ++j) {
+            bool sel[4];
+            uint32_t before = 0, tot = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                sel[e] = (selbits[(4 * j + e) >> 5] >> ((4 * j + e) & 31)) & 1u;
+                const uint64_t b = __ballot(sel[e]);
+                before += lanes_below(b);
+                tot += (uint32_t)__popcll(b);
+            }
+            uint32_t r = pos + before;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                if (sel[e]) {
+                    if (r < (uint32_t)k) out[r] = b0 + 256 * j + e;
+                    ++r;
+                }
+            }
+            pos += tot;
         }
         eq_run += eq_tot;
-        sel_run += sel_tot;
+        pos_run += sel_tot;
     }
 }
 
-template <int NT, bool IN_LDS>
+template <int NT, int EPT, bool STREAM>
 hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
-    size_t lds = IN_LDS ? (size_t)a.max_len * 4 : 0;
-    static bool attr_set = false;
-    if (IN_LDS && !attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)topk_kernel<NT, IN_LDS>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           LDS_ROW_CAP * 4);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
-    hipLaunchKernelGGL((topk_kernel<NT, IN_LDS>), dim3(a.rows), dim3(NT), lds, st, a.scores, a.row_stride,
-                       a.first_len, a.seq_len, a.k, a.idx, a.max_len);
+    const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
+    if (vec)
+        hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
+                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
+    else
+        hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
+                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
     return hipGetLastError();
 }
 
@@ -222,10 +273,9 @@ hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
 
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
-    if (a.max_len <= LDS_ROW_CAP) {
-        if (a.max_len <= 4096) return topk_launch<256, true>(a, st);
-        if (a.max_len <= 16384) return topk_launch<512, true>(a, st);
-        return topk_launch<1024, true>(a, st);
-    }
-    return topk_launch<1024, false>(a, st);
+    if (a.max_len <= 2048) return topk_launch<256, 8, false>(a, st);
+    if (a.max_len <= 4096) return topk_launch<256, 16, false>(a, st);
+    if (a.max_len <= 16384) return topk_launch<1024, 16, false>(a, st);
+    if (a.max_len <= 32768) return topk_launch<1024, 32, false>(a, st);
+    return topk_launch<1024, 16, true>(a, st);
 }

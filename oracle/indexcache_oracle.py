@@ -219,7 +219,7 @@ def run_stack(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int, pos
             cache = indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k, pos0)
             calls += 1
         elif cache is None:
-            raise NoCachedIndices("No cached indices available")
+            raise NoCachedIndices("no cached indices: an S layer came before any F layer")
         outs.append(sparse_attn(lay["q"], lay["kv"], cache))
         used.append(cache)
     return outs, used, calls

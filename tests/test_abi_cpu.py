@@ -62,7 +62,7 @@ def _stack(pattern, n_layers=None, shape=None, ws_bytes=1 << 30):
 
 def test_pattern_errors(L):
     assert _stack("SFSS") == ic.IC_ERR_NO_CACHED_INDICES
-    assert "No cached indices" in ic.last_error()
+    assert "no cached indices" in ic.last_error()
     assert _stack("0100") == ic.IC_ERR_NO_CACHED_INDICES
     assert _stack("FXSS") == ic.IC_ERR_PATTERN
     assert _stack("FSS", n_layers=4) == ic.IC_ERR_PATTERN

@@ -1,0 +1,64 @@
+"""A decode step captured in a HIP graph and replayed: every replay, with new inputs
+copied into the static buffers and eager work in between, must equal the eager call."""
+import pytest
+import torch
+
+import dsa_lightning_indexer_scores_amd as ic
+from dsa_lightning_indexer_scores_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def test_decode_graph_replays_match_eager():
+    B, cap, H_I, d_I, k, H, d = 4, 3000, 64, 128, 512, 16, 128
+    pattern = "FSSF"
+    g = torch.Generator(device="cuda").manual_seed(5)
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda")
+
+    caches = []
+    for c in pattern:
+        lay = {"kv": rnd(B, cap, 2, d).to(torch.bfloat16)}
+        if c == "F":
+            lay["k_I"] = synth.encode(rnd(B, cap, d_I), "fp8")
+        caches.append(lay)
+
+    def step_inputs(step):
+        out = []
+        for c in pattern:
+            lay = {"q": rnd(B, 1, H, d).to(torch.bfloat16)}
+            if c == "F":
+                lay["q_I"] = synth.encode(rnd(B, 1, H_I, d_I), "fp8")
+                lay["w"] = torch.rand(B, 1, H_I, generator=g, device="cuda")
+            out.append(lay)
+        seq = torch.tensor([cap - 3 + step % 3, 700 + step, 1 + step, 2048], dtype=torch.int32, device="cuda")
+        return out, seq
+
+    static_in, static_seq = step_inputs(0)
+    layers = [dict(caches[l], **static_in[l]) for l in range(len(pattern))]
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    shape = ic._stack_shape(pattern, layers, k, 0, 0)
+    ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_DECODE_STEP), dtype=torch.uint8, device="cuda")
+    ic.decode_step(pattern, layers, static_seq, k, outs=outs, idx_cache=idx, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ic.decode_step(pattern, layers, static_seq, k, outs=outs, idx_cache=idx, ws=ws)
+    for step in range(1, 5):
+        new_in, new_seq = step_inputs(step)
+        for l in range(len(pattern)):
+            for name, t in new_in[l].items():
+                layers[l][name].copy_(t)
+        static_seq.copy_(new_seq)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        got_idx = idx.clone()
+        # eager reference on separate buffers, same inputs
+        ref_outs, ref_idx, _ = ic.decode_step(pattern, layers, static_seq, k)
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, ref_idx), f"replay {step}: idx differs"
+        for l in range(len(pattern)):
+            assert torch.equal(got[l], ref_outs[l]), f"replay {step}: layer {l} differs"
