@@ -44,13 +44,14 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 template <int D>
-__global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
+__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
     int H, int k, int nsplit, float scale_log2) {
     using G = AttGeom<D>;
     __shared__ __attribute__((aligned(16))) uint8_t vlds_all[ATT_NW][KT * G::VSTR];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps addressing scalar
     const int n = lane & 15, g = lane >> 4;
     const int HG = (H + 15) / 16;
     const int64_t item = (int64_t)blockIdx.x * ATT_NW + wv;
@@ -62,6 +63,9 @@ __global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
 
     const int seq = (int)(qi / q_per_seq);
     const uint16_t* kvs = kv + (int64_t)seq * kv_seq_stride;
+    // byte view of this sequence's rows, addressed with 32-bit offsets (a sequence's
+    // KV rows span < 4 GiB), so loads use a scalar base plus one VGPR offset
+    const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kvs);
     const int32_t* irow = idx + qi * k;
     const int head = 16 * hg + n;
 
@@ -84,46 +88,54 @@ __global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    for (int j0 = j_begin; j0 < j_end; j0 += KT) {
+    // One step of KT selected rows.  Loads of step t+1 are issued before step t is
+    // computed (two register sets, A and B), and the idx entries of step t+2 are
+    // fetched one step earlier still, so gathers overlap compute.
+    struct Tile {
+        i32x4 kf[2][G::NDC];                                 // K fragments: keys 16*kt + m
+        i32x4 vst[G::VPL];                                   // V rows, staged for LDS
+        uint32_t valid;                                      // bit e: entry e of the step is a row
+    };
+    auto load_idx = [&](int j0) -> int {
         const int jl = j0 + (lane & 31);
-        int my_idx = (jl < j_end) ? irow[jl] : -1;
-        if (my_idx >= Lk) my_idx = -1;                       // never read past the KV rows
-        const unsigned long long vb = __ballot(my_idx >= 0);
-        const uint32_t valid = (uint32_t)vb;                 // bit e: entry j0+e is a real row
-        if (valid == 0u) break;                              // -1 padding runs to the row's end
+        int v = (jl < j_end) ? irow[jl] : -1;
+        return (v >= Lk) ? -1 : v;                           // never read past the KV rows
+    };
+    auto issue = [&](Tile& T, int my_idx) {
+        T.valid = (uint32_t)__ballot(my_idx >= 0);
+        if (T.valid == 0u) return;
         const int safe_idx = my_idx >= 0 ? my_idx : 0;
-
-        // Gather V rows of the tile into LDS: piece c -> row c / PPR, byte (c % PPR) * 16.
-        i32x4 vst[G::VPL];
 #pragma unroll
-        for (int i = 0; i < G::VPL; ++i) {
+        for (int i = 0; i < G::VPL; ++i) {                   // V piece c -> row c / PPR, byte (c % PPR) * 16
             const int c = lane + 64 * i;
-            const int key = c / G::PPR;
-            const int row = __shfl(safe_idx, key);
-            vst[i] = *reinterpret_cast<const i32x4*>(kvs + ((int64_t)row * 2 + 1) * D + (c % G::PPR) * 8);
+            const int row = __shfl(safe_idx, c / G::PPR);
+            const uint32_t off = (uint32_t)row * (4 * D) + 2 * D + (c % G::PPR) * 16;
+            T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
         }
-        // K fragments (A operand of S^T): lane (m, g) -> key 16*kt + m, d = 32*dc + 8g.
-        i32x4 kf[2][G::NDC];
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
+        for (int kt = 0; kt < 2; ++kt) {                     // lane (m, g): key 16*kt + m, d = 32*dc + 8g
             const int row = __shfl(safe_idx, 16 * kt + n);
-            const uint16_t* kp = kvs + (int64_t)row * 2 * D + 8 * g;
+            const uint32_t off = (uint32_t)row * (4 * D) + 16 * g;
 #pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) kf[kt][dc] = *reinterpret_cast<const i32x4*>(kp + 32 * dc);
+            for (int dc = 0; dc < G::NDC; ++dc)
+                T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
         }
+    };
+    auto compute = [&](const Tile& T) {
+        if (T.valid == 0u) return;                           // a step of -1 entries contributes nothing
+        const uint32_t valid = T.valid;
 #pragma unroll
         for (int i = 0; i < G::VPL; ++i) {
             const int c = lane + 64 * i;
-            *reinterpret_cast<i32x4*>(vlds + (c / G::PPR) * G::VSTR + (c % G::PPR) * 16) = vst[i];
+            *reinterpret_cast<i32x4*>(vlds + (c / G::PPR) * G::VSTR + (c % G::PPR) * 16) = T.vst[i];
         }
-
         // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e.
         f32x4 s[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) acc = mfma_bf16_k32(kf[kt][dc], qf[dc], acc);
+            for (int dc = 0; dc < G::NDC; ++dc) acc = mfma_bf16_k32(T.kf[kt][dc], qf[dc], acc);
             s[kt] = acc;
         }
         float x[8];
@@ -139,7 +151,7 @@ __global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
             }
         tmax = max_xor16(tmax);
         tmax = max_xor32(tmax);
-        const float m_new = fmaxf(m_run, tmax);              // finite: the tile has a valid row
+        const float m_new = fmaxf(m_run, tmax);              // finite: the step has a row
         const float alpha = exp2f(m_run - m_new);
         float psum = 0.f;
 #pragma unroll
@@ -174,6 +186,28 @@ __global__ __launch_bounds__(ATT_NW * 64) void sparse_attn_kernel(
             o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
         }
         lds_wave_sync();
+    };
+
+    const int nsteps = j_end > j_begin ? (j_end - j_begin + KT - 1) / KT : 0;
+    Tile TA, TB;
+    int idx0 = 0, idx1 = 0;
+    if (nsteps > 0) {
+        issue(TA, load_idx(j_begin));
+        idx1 = load_idx(j_begin + KT);
+    }
+    for (int t = 0; t < nsteps; t += 2) {
+        if (t + 1 < nsteps) {
+            issue(TB, idx1);
+            idx0 = load_idx(j_begin + (t + 2) * KT);
+        }
+        compute(TA);
+        if (t + 1 < nsteps) {
+            if (t + 2 < nsteps) {
+                issue(TA, idx0);
+                idx1 = load_idx(j_begin + (t + 3) * KT);
+            }
+            compute(TB);
+        }
     }
 
     l_run = sum_xor16(l_run);
