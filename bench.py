@@ -33,6 +33,39 @@ if ROOT not in sys.path:
 
 PEAK_HBM_GBS = 8000.0
 PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "csrc")
+KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "attn.hip"}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "common.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+    (scaled by the copy-kernel calibration), or None if absent or if the kernel source
+    has changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{kernel}_stack32k_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                vals[key.strip()] = val.strip()
+    if vals.get("source_sha256") != kernel_source_hash(kernel):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg: str):
@@ -332,7 +365,10 @@ def main():
                  "attention": kr["attention"]["ms"] * cfg.n_layers}
         dom = max(share, key=share.get)
         result["roofline"] = dict({k: v for k, v in kr[dom].items() if k in ("bound", "achieved", "peak", "unit",
-                                                                          "frac")}, kernel=dom, traffic=None)
+                                                                          "frac")}, kernel=dom,
+                                  traffic=measured_traffic(dom))
+        for name in kr:
+            kr[name]["traffic"] = measured_traffic(name)
         result["kernels"] = kr
         result["kernel_ms_in_stack"] = {k: round(v, 3) for k, v in share.items()}
         result["indexer_mfma_frac"] = kr["indexer"]["frac"]

@@ -89,10 +89,20 @@ int decode_splits(const ic_shape& s) {
     return ns < 4 ? 1 : ns / 4 * 4;
 }
 
-size_t decode_ws(const ic_shape& s) {
-    const size_t scores = (size_t)round_up((int64_t)s.B * s.Lk * 4, 256);
-    return scores + round_up(sparse_attn_ws_bytes(s.B, s.H, s.d, decode_splits(s)), 256);
+// Decode workspace: scores [B, round_up(Lk, 4)] fp32 | attention partials.
+struct DecodeWs {
+    int64_t score_stride;
+    size_t scores_off, part_off, total;
+};
+DecodeWs decode_layout(const ic_shape& s) {
+    DecodeWs w;
+    w.score_stride = round_up(s.Lk, 4);                   // 16-byte rows for the top-k's vector loads
+    w.scores_off = 0;
+    w.part_off = (size_t)round_up((int64_t)s.B * w.score_stride * 4, 256);
+    w.total = w.part_off + (size_t)round_up(sparse_attn_ws_bytes(s.B, s.H, s.d, decode_splits(s)), 256);
+    return w;
 }
+size_t decode_ws(const ic_shape& s) { return decode_layout(s).total; }
 
 ic_status check_ws(const void* ws, size_t have, size_t need) {
     if (need == 0) return IC_OK;
@@ -327,8 +337,9 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
     if ((r = check_ws(ws, ws_bytes, decode_ws(*shape))) != IC_OK) return r;
     const ic_shape& s = *shape;
     hipStream_t st = (hipStream_t)stream;
-    float* scores = static_cast<float*>(ws);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + round_up((int64_t)s.B * s.Lk * 4, 256));
+    const DecodeWs lay = decode_layout(s);
+    float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scores_off);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.part_off);
     const int nsplit = decode_splits(s);
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;
@@ -341,6 +352,7 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
             a.k_I = L.k_I;
             a.seq_len = seq_len;
             a.scores = scores;
+            a.score_stride = lay.score_stride;
             a.B = s.B;
             a.Lk = s.Lk;
             a.H_I = s.H_I;
@@ -350,7 +362,7 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
             if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
             ic_topk_args t;
             t.scores = scores;
-            t.row_stride = s.Lk;
+            t.row_stride = lay.score_stride;
             t.rows = s.B;
             t.first_len = 0;
             t.seq_len = seq_len;

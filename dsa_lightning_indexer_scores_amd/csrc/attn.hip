@@ -19,7 +19,9 @@
 //       k order matches the transposed read, so no shuffle is needed).
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
 // workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
-// the workgroups' partials in a fixed order, so results are deterministic.
+// the workgroups' partials in split order, so results are deterministic.  (A
+// fused last-workgroup merge needs device-scope ordering, which on this part
+// costs L2 write-back / invalidation or serialised coherent loads: slower.)
 #include "common.h"
 
 using namespace ic;
@@ -43,7 +45,7 @@ __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcn
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D>
+template <int D, bool SPLIT>
 __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 
     l_run = sum_xor16(l_run);
     l_run = sum_xor32(l_run);
-    if (nsplit == 1) {
+    if constexpr (!SPLIT) {
         if (head < H) {
             const float inv = 1.f / l_run;
             uint16_t* op = out + (qi * H + head) * D + 4 * g;
@@ -263,8 +265,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
 }
 
-// Merge the partials of each (query, head) in split order: one workgroup per
-// (query, head), one thread per channel.
+// Merge the workgroups' partials of each (query, head) in split order: one
+// workgroup per (query, head), one thread per channel.
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
                                                         int H, int nparts) {
@@ -275,15 +277,14 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     const float* base = part + (qi * HG + hg) * nparts * (16 * D + 32);
     const int dd = threadIdx.x;
     float M = -INFINITY;
-    for (int sp = 0; sp < nparts; ++sp) M = fmaxf(M, base[sp * (16 * D + 32) + 16 * D + 2 * hn]);
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, base[p * (16 * D + 32) + 16 * D + 2 * hn]);
     float num = 0.f, den = 0.f;
-    for (int sp = 0; sp < nparts; ++sp) {
-        const float* ps = base + sp * (16 * D + 32);
-        const float l = ps[16 * D + 2 * hn + 1];
-        if (l == 0.f) continue;                              // split with no selected rows
-        const float c = exp2f(ps[16 * D + 2 * hn] - M);
+    for (int p = 0; p < nparts; ++p) {
+        const float* ps = base + p * (16 * D + 32);
+        const float m = ps[16 * D + 2 * hn];
+        const float c = (m == -INFINITY) ? 0.f : exp2f(m - M);   // a split with no selected rows adds nothing
         num += c * ps[hn * D + dd];
-        den += c * l;
+        den += c * ps[16 * D + 2 * hn + 1];
     }
     const float v = num / den;
     uint32_t u = __float_as_uint(v);
@@ -297,11 +298,17 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     const int64_t items = (int64_t)a.nq * HG * a.nsplit;
     const int64_t blocks = (items + ATT_NW - 1) / ATT_NW;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
-    hipLaunchKernelGGL((sparse_attn_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+    if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
+        hipLaunchKernelGGL((sparse_attn_kernel<D, false>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.ws,
+                           a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, 1, scale_log2);
+        return hipGetLastError();
+    }
+    hipLaunchKernelGGL((sparse_attn_kernel<D, true>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.ws,
                        a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, a.nsplit, scale_log2);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || a.nsplit == 1) return e;
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((attn_combine_kernel<D>), dim3((unsigned)((int64_t)a.nq * a.H)), dim3(D), 0, st,
                        a.ws, (uint16_t*)a.out, a.H, a.nsplit / ATT_NW);
     return hipGetLastError();
@@ -317,7 +324,8 @@ size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit) {
 
 hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st) {
     if (a.nq <= 0) return hipSuccess;
-    if (a.nsplit > 1 && a.nsplit % ATT_NW != 0) return hipErrorInvalidValue;   // splits merge 4 per workgroup
+    if (a.nsplit > 1 && (a.nsplit % ATT_NW != 0 || a.ws == nullptr))
+        return hipErrorInvalidValue;                        // splits merge 4 per workgroup, then in a combine kernel
     if (a.d == 128) return attn_launch<128>(a, st);
     if (a.d == 64) return attn_launch<64>(a, st);
     return hipErrorInvalidValue;

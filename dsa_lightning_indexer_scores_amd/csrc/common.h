@@ -90,7 +90,8 @@ struct ic_indexer_decode_args {
     const float* w;       // [B, H_I]
     const void* k_I;      // [B, Lk, d_I]
     const int32_t* seq_len;  // [B] device
-    float* scores;        // [B, Lk]
+    float* scores;        // [B, score_stride]
+    int64_t score_stride; // >= Lk
     int32_t B, Lk, H_I, d_I, fp8;
 };
 hipError_t launch_indexer_decode(const ic_indexer_decode_args& a, hipStream_t st);
@@ -115,7 +116,8 @@ struct ic_attn_args {
     int64_t kv_seq_stride;   // elements between sequences in kv
     int32_t Lk;              // KV rows per sequence (idx entries >= Lk are ignored)
     int32_t nq, q_per_seq, H, d, k;
-    // split-K (decode): nsplit > 1 writes partials to ws and combines
+    // split-K (decode): nsplit > 1 (a multiple of 4) writes partials to ws and a
+    // combine kernel merges them
     int32_t nsplit;
     float* ws;
 };

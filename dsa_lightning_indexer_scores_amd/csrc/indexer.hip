@@ -239,7 +239,7 @@ constexpr int DEC_KEYS_PER_WG = DEC_NW * DEC_TILES_PER_WAVE * 16;
 template <bool FP8, int D_I, int HT>
 __global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int Lk, int H_I) {
+    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I) {
     using G = IdxGeom<FP8, D_I>;
     const int b = blockIdx.y;
     const int n = max(1, min(seq_len[b], Lk));                // visible keys (clamped to the cache)
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
         for (int ht = 0; ht < HT; ++ht) acc[ht] = tile_mma<FP8, D_I>(A[ht], Bf[i]);
         val[i] = head_reduce<HT>(acc, wr);
     }
-    float* srow = scores + (int64_t)b * Lk;
+    float* srow = scores + (int64_t)b * score_stride;
 #pragma unroll
     for (int grp = 0; grp < DEC_TILES_PER_WAVE / 4; ++grp) {
         const int s = key0 + 64 * grp + 16 * g + r;
@@ -280,10 +280,9 @@ __global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
     }
 }
 
-template <bool FP8, int D_I, int HT>
-hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
+template <bool FP8, int D_I, int HT, int NW>
+hipError_t prefill_launch(const ic_indexer_args& a, hipStream_t st) {
     constexpr int QW = FP8 ? 2 : 1;
-    constexpr int NW = 8;
     constexpr int KB = 64;
     constexpr int QB = QW * NW;
     const int nblk = (a.nq + QB - 1) / QB;
@@ -293,11 +292,21 @@ hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
     return hipGetLastError();
 }
 
+// 8-wave workgroups share each k_I block among 16 queries; when that leaves fewer than
+// two workgroups per CU (a 4096-query chunk), 4-wave workgroups keep the CUs fed.
+template <bool FP8, int D_I, int HT>
+hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
+    constexpr int QW = FP8 ? 2 : 1;
+    if ((a.nq + QW * 8 - 1) / (QW * 8) >= 512) return prefill_launch<FP8, D_I, HT, 8>(a, st);
+    return prefill_launch<FP8, D_I, HT, 4>(a, st);
+}
+
 template <bool FP8, int D_I, int HT>
 hipError_t decode_dispatch(const ic_indexer_decode_args& a, hipStream_t st) {
     dim3 grid((a.Lk + DEC_KEYS_PER_WG - 1) / DEC_KEYS_PER_WG, a.B);
     hipLaunchKernelGGL((indexer_decode_kernel<FP8, D_I, HT>), grid, dim3(DEC_NW * 64), 0, st,
-                       (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.seq_len, a.scores, a.Lk, a.H_I);
+                       (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.seq_len, a.scores, a.score_stride,
+                       a.Lk, a.H_I);
     return hipGetLastError();
 }
 

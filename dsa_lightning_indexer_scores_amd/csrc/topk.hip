@@ -11,7 +11,8 @@
 // One workgroup per row.  Scores become order-preserving u32 keys (-0.0 folded
 // onto +0.0).  The bits shared by the row's smallest and largest key are
 // skipped; the rest are resolved most-significant digit first with 11-bit LDS
-// histograms until the k-th key's prefix is exact or its bin is taken whole.
+// histograms (for long rows one copy per wave, summed at the scan) until the
+// k-th key's prefix is exact or its bin is taken whole.
 // A final pass walks the row in index order and compacts the selected
 // positions with wave ballots (mbcnt prefix counts) and a prefix sum over the
 // waves, so the output is sorted for free and ties resolve to the lowest
@@ -20,9 +21,9 @@
 // The row is cut into blocks of NT*EPT keys.  In a block, wave w owns the
 // contiguous span [w*64*EPT, (w+1)*64*EPT) and lane l holds its keys
 // 256*j + 4*l + e (j < EPT/4, e < 4): loads are coalesced 16-byte vectors and
-// every pass works out of VGPRs.  Rows of one block (<= 32768 keys with 1024
-// threads) are read from HBM exactly once; longer rows stream their blocks
-// again at every pass (re-reads hit L2 / MALL).
+// every pass works out of VGPRs.  Rows of one block (<= 67584 keys: 1024 x 32
+// or 512 x 132) are read from HBM exactly once; longer rows stream their
+// blocks again at every pass (re-reads hit L2 / MALL).
 #include "common.h"
 
 using namespace ic;
@@ -67,9 +68,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   int32_t* __restrict__ idx, int max_len) {
     constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
     constexpr int BLOCK = NT * EPT;                  // keys per block
-    __shared__ uint32_t hist[HIST_BINS];
+    // Long rows keep one histogram per wave: a concentrated score distribution puts
+    // most keys in a few bins, and per-wave copies keep the LDS atomics of different
+    // waves apart.  Short rows share one copy (a cheaper scan wins there).
+    constexpr int NH = (NT * EPT > 32768) ? NT / 64 : 1;
+    __shared__ uint32_t hist[NH][HIST_BINS];
     __shared__ uint32_t wtot[NT / 64];
-    __shared__ uint32_t kminmax[2], found[2];
+    __shared__ uint32_t kminmax[2], found[3];
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -100,21 +105,28 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = (i0 + e < n) ? src[i0 + e] : 0.f;
             }
+            // Positions past the row get key 0, which no score maps to (a real key is
+            // >= 0x007FFFFF): it sorts below every real key, only ever lands in
+            // histogram bin 0 (corrected below) and comes after every real key in
+            // index order, so it is never selected.
 #pragma unroll
-            for (int e = 0; e < 4; ++e) key[4 * j + e] = score_key(v[e]);
+            for (int e = 0; e < 4; ++e) key[4 * j + e] = (i0 + e < n) ? score_key(v[e]) : 0u;
         }
     };
-    auto valid = [&](int blk, int j, int e) { return blk * BLOCK + lane_base + 256 * j + e < n; };
+    const uint32_t n_pad = (uint32_t)(nblocks * BLOCK - n);   // key-0 slots in the whole row
 
-    // Smallest and largest key of the row.
+    // Smallest and largest real key of the row.
     uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int blk = 0; blk < nblocks; ++blk) {
         load_block(blk);
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (valid(blk, j, e)) { lo = min(lo, key[4 * j + e]); hi = max(hi, key[4 * j + e]); }
+            for (int e = 0; e < 4; ++e) {
+                const uint32_t kk = key[4 * j + e];
+                lo = min(lo, kk ? kk : 0xFFFFFFFFu);
+                hi = max(hi, kk);
+            }
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -136,7 +148,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         const int sh_lo = shift - width;
         const uint32_t mask = (1u << width) - 1u;
         const int nb = 1 << width;
-        for (int b = tid; b < nb; b += NT) hist[b] = 0u;
+        for (int b = tid; b < nb * NH; b += NT) hist[b / nb][b % nb] = 0u;
         __syncthreads();
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
@@ -145,10 +157,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t kk = key[4 * j + e];
-                    if (valid(blk, j, e) && (shift >= 32 || (kk >> shift) == prefix))
-                        atomicAdd(&hist[(kk >> sh_lo) & mask], 1u);
+                    if (shift >= 32 || (kk >> shift) == prefix)
+                        atomicAdd(&hist[NH > 1 ? wv : 0][(kk >> sh_lo) & mask], 1u);
                 }
         }
+        __syncthreads();
+        if (tid == 0 && n_pad != 0u && (shift >= 32 || prefix == 0u)) hist[0][0] -= n_pad;   // drop the key-0 slots
         __syncthreads();
         // Bin b with above(b) < k_rem <= above(b) + hist[b]; above = count in higher bins.
         constexpr int BPT = (HIST_BINS + NT - 1) / NT;
@@ -156,8 +170,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
             const int b = tid * BPT + j;
-            hv[j] = b < nb ? hist[b] : 0u;
-            local += hv[j];
+            uint32_t c = 0;
+            if (b < nb) {
+#pragma unroll
+                for (int w = 0; w < NH; ++w) c += hist[w][b];
+            }
+            hv[j] = c;
+            local += c;
         }
         uint32_t suf = local;                        // suffix sum over the lanes of this wave
 #pragma unroll
@@ -173,12 +192,16 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
         for (int j = BPT - 1; j >= 0; --j) {
             const int b = tid * BPT + j;
-            if (b < nb && above < k_rem && k_rem <= above + hv[j]) { found[0] = (uint32_t)b; found[1] = above; }
+            if (b < nb && above < k_rem && k_rem <= above + hv[j]) {
+                found[0] = (uint32_t)b;
+                found[1] = above;
+                found[2] = hv[j];
+            }
             above += hv[j];
         }
         __syncthreads();
         const uint32_t fb = found[0], fa = found[1];
-        const uint32_t in_bin = hist[fb];
+        const uint32_t in_bin = found[2];
         prefix = (shift >= 32 ? 0u : (prefix << width)) | fb;
         k_rem -= fa;
         shift = sh_lo;
@@ -195,7 +218,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) eqc += valid(blk, j, e) && digit(key[4 * j + e]) == prefix;
+            for (int e = 0; e < 4; ++e) eqc += digit(key[4 * j + e]) == prefix;
         uint32_t eq_tot;
         uint32_t eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
         uint32_t selbits[(EPT + 31) / 32];
@@ -208,10 +231,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             uint32_t before = 0, tot = 0;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool ok = valid(blk, j, e);
                 const uint32_t dg = digit(key[4 * j + e]);
-                eq[e] = ok && dg == prefix;
-                gt[e] = ok && dg > prefix;
+                eq[e] = dg == prefix;
+                gt[e] = dg > prefix;
                 const uint64_t b = __ballot(eq[e]);
                 before += lanes_below(b);
                 tot += (uint32_t)__popcll(b);
@@ -260,12 +282,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 template <int NT, int EPT, bool STREAM>
 hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
     const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
-    if (vec)
+    if constexpr (NT * EPT > 32768 && !STREAM) {     // register-heavy variant: vector loads only
+        if (!vec) return hipErrorInvalidValue;
         hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
                            a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-    else
-        hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
-                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
+    } else {
+        if (vec)
+            hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
+                               a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
+        else
+            hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
+                               a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
+    }
     return hipGetLastError();
 }
 
@@ -273,9 +301,11 @@ hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
 
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
+    const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
     if (a.max_len <= 2048) return topk_launch<256, 8, false>(a, st);
     if (a.max_len <= 4096) return topk_launch<256, 16, false>(a, st);
     if (a.max_len <= 16384) return topk_launch<1024, 16, false>(a, st);
     if (a.max_len <= 32768) return topk_launch<1024, 32, false>(a, st);
-    return topk_launch<1024, 16, true>(a, st);
+    if (vec && a.max_len <= 512 * 132) return topk_launch<512, 132, false>(a, st);   // 256 VGPRs, vector loads only
+    return topk_launch<1024, 32, true>(a, st);
 }
