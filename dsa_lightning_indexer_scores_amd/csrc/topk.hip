@@ -13,17 +13,21 @@
 // skipped; the rest are resolved most-significant digit first with 11-bit LDS
 // histograms (for long rows one copy per wave, summed at the scan) until the
 // k-th key's prefix is exact or its bin is taken whole.
-// A final pass walks the row in index order and compacts the selected
-// positions with wave ballots (mbcnt prefix counts) and a prefix sum over the
-// waves, so the output is sorted for free and ties resolve to the lowest
-// indices.
+// For long rows (streamed from L2 at every pass) a pass is expensive, so once
+// the bin holding the k-th key has at most CAND_CAP keys, one pass gathers that
+// bin's keys and positions into LDS and ranks them exactly, giving the
+// threshold pair (key, position) and a single-pass emit.  Register-resident
+// rows keep narrowing the digit instead (measured faster there).  A final pass walks the row in index
+// order and compacts the selected positions with wave ballots (mbcnt prefix
+// counts) and a prefix sum over the waves, so the output is sorted for free
+// and ties resolve to the lowest indices.
 //
 // The row is cut into blocks of NT*EPT keys.  In a block, wave w owns the
 // contiguous span [w*64*EPT, (w+1)*64*EPT) and lane l holds its keys
 // 256*j + 4*l + e (j < EPT/4, e < 4): loads are coalesced 16-byte vectors and
-// every pass works out of VGPRs.  Rows of one block (<= 67584 keys: 1024 x 32
-// or 512 x 132) are read from HBM exactly once; longer rows stream their
-// blocks again at every pass (re-reads hit L2 / MALL).
+// every pass works out of VGPRs.  Rows of one block (<= 32768 keys with 1024
+// threads) are read from HBM exactly once; longer rows stream their blocks
+// again at every pass (re-reads hit L2 / MALL).
 #include "common.h"
 
 using namespace ic;
@@ -32,6 +36,7 @@ namespace {
 
 constexpr int HIST_BITS = 11;
 constexpr int HIST_BINS = 1 << HIST_BITS;
+constexpr int CAND_CAP = 256;       // threshold-bin keys resolved by exact ranking in LDS
 
 __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
@@ -75,6 +80,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     __shared__ uint32_t hist[NH][HIST_BINS];
     __shared__ uint32_t wtot[NT / 64];
     __shared__ uint32_t kminmax[2], found[3];
+    __shared__ uint32_t cand_key[CAND_CAP];
+    __shared__ int32_t cand_idx[CAND_CAP];
+    __shared__ uint32_t ncand, thr_key;
+    __shared__ int32_t thr_idx;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
@@ -143,6 +152,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     int shift = (kmin == kmax) ? 0 : 32 - __clz(kmin ^ kmax);
     uint32_t prefix = shift >= 32 ? 0u : (kmax >> shift);
     uint32_t k_rem = (uint32_t)k;                    // still to take among the candidates
+    bool ranked = false;                             // threshold bin resolved by ranking its keys
     while (shift > 0) {
         const int width = min(HIST_BITS, shift);
         const int sh_lo = shift - width;
@@ -207,6 +217,88 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         shift = sh_lo;
         __syncthreads();                             // hist, wtot and found are reused
         if (in_bin == k_rem) break;                  // the whole bin is taken: no ties to cut
+        if (STREAM && in_bin <= (uint32_t)CAND_CAP) {   // few keys share the k-th key's bin: rank them
+            ranked = true;
+            break;
+        }
+    }
+
+    if (STREAM && ranked) {
+        // Gather the bin's keys (with their positions) into LDS and find the k_rem-th of
+        // them in (key descending, position ascending) order: the exact threshold pair.
+        if (tid == 0) ncand = 0u;
+        __syncthreads();
+        for (int blk = 0; blk < nblocks; ++blk) {
+            if (STREAM) load_block(blk);
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[4 * j + e];
+                    if (kk != 0u && (kk >> shift) == prefix) {
+                        const uint32_t at = atomicAdd(&ncand, 1u);
+                        if (at < (uint32_t)CAND_CAP) {
+                            cand_key[at] = kk;
+                            cand_idx[at] = blk * BLOCK + lane_base + 256 * j + e;
+                        }
+                    }
+                }
+        }
+        __syncthreads();
+        const int nc = (int)min(ncand, (uint32_t)CAND_CAP);
+        for (int c = tid; c < nc; c += NT) {
+            const uint32_t ck = cand_key[c];
+            const int32_t ci = cand_idx[c];
+            uint32_t rank = 0;
+            for (int o = 0; o < nc; ++o) {
+                const uint32_t ok = cand_key[o];
+                rank += (ok > ck) || (ok == ck && cand_idx[o] < ci);
+            }
+            if (rank == k_rem - 1u) { thr_key = ck; thr_idx = ci; }
+        }
+        __syncthreads();
+        const uint32_t tk = thr_key;
+        const int32_t ti = thr_idx;
+        // Emit in index order: every key above the threshold pair.
+        uint32_t pos_run = 0;
+        for (int blk = 0; blk < nblocks; ++blk) {
+            if (STREAM) load_block(blk);
+            const int b0 = blk * BLOCK + lane_base;
+            uint32_t selc = 0;
+#pragma unroll
+            for (int j = 0; j < NR; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[4 * j + e];
+                    selc += (kk > tk) || (kk == tk && b0 + 256 * j + e <= ti);
+                }
+            uint32_t sel_tot;
+            uint32_t pos = pos_run + waves_scan<NT>(wave_sum(selc), wtot, &sel_tot);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                bool sel[4];
+                uint32_t before = 0, tot = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[4 * j + e];
+                    sel[e] = (kk > tk) || (kk == tk && b0 + 256 * j + e <= ti);
+                    const uint64_t b = __ballot(sel[e]);
+                    before += lanes_below(b);
+                    tot += (uint32_t)__popcll(b);
+                }
+                uint32_t r = pos + before;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (sel[e]) {
+                        if (r < (uint32_t)k) out[r] = b0 + 256 * j + e;
+                        ++r;
+                    }
+                }
+                pos += tot;
+            }
+            pos_run += sel_tot;
+        }
+        return;
     }
 
     // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them.
@@ -282,18 +374,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 template <int NT, int EPT, bool STREAM>
 hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
     const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
-    if constexpr (NT * EPT > 32768 && !STREAM) {     // register-heavy variant: vector loads only
-        if (!vec) return hipErrorInvalidValue;
+    if (vec)
         hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
                            a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-    } else {
-        if (vec)
-            hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
-                               a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-        else
-            hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
-                               a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-    }
+    else
+        hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
+                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
     return hipGetLastError();
 }
 
@@ -306,6 +392,5 @@ hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
     if (a.max_len <= 4096) return topk_launch<256, 16, false>(a, st);
     if (a.max_len <= 16384) return topk_launch<1024, 16, false>(a, st);
     if (a.max_len <= 32768) return topk_launch<1024, 32, false>(a, st);
-    if (vec && a.max_len <= 512 * 132) return topk_launch<512, 132, false>(a, st);   // 256 VGPRs, vector loads only
     return topk_launch<1024, 32, true>(a, st);
 }
