@@ -8,6 +8,7 @@
 
 namespace ic {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -30,6 +31,12 @@ __device__ __forceinline__ f32x4 mfma_bf16_k32(const i32x4& a, const i32x4& b, f
 // fp8 e4m3 x fp8 e4m3, K = 128 (32 bytes per lane); unit block scales.
 __device__ __forceinline__ f32x4 mfma_fp8_k128(const i32x8& a, const i32x8& b, f32x4 c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// Same contraction with an E8M0 scale on A: lane l's byte scales row l%16 over K block
+// l/16 (32 elements) by 2^(byte - 127).  B is unscaled.
+__device__ __forceinline__ f32x4 mfma_fp8_k128_scale_a(const i32x8& a, int scale_a, const i32x8& b, f32x4 c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
 }
 
 // ---- cross-lane sums over the four 16-lane rows of a wave ----

@@ -9,13 +9,26 @@
 //
 // Tiling.  One 16x16 MFMA output tile holds 16 indexer heads (rows) x 16
 // keys (columns).  Lane l gets key l%16 and heads 4*(l/16)..+3, so the ReLU
-// (one v_med3) and the w-weighted head sum (one v_fmac) run in registers over
-// that lane's 16 heads, and two lane-row swaps finish the sum over 64 heads.
+// and the w-weighted head sum run in registers over that lane's 16 heads, and
+// lane-row swaps finish the sum over 64 heads, four key tiles at a time.
+//
+// fp8 prefill epilogue.  ReLU(y) = (y + |y|) / 2 splits the score into
+//     1/2 sum_j w_j |q_j . k|   +   1/2 (sum_j w_j q_j) . k.
+// The first sum is one v_fma per (head, key) with |y| as a free input
+// modifier (the plain form needs a max and an fma).  The second is linear in
+// k, so it runs on the matrix core: the head-weighted query is split into
+// e4m3 parts with an E8M0 scale per 32-channel block, one MFMA row per part,
+// and each part carries the next 4 significant bits of what the earlier parts
+// left, so 8 parts leave a residual below 2^-32 of the block's largest value.
+// That halves the vector work per MFMA, which is what bounds this kernel on
+// gfx950 (the matrix core hides about 4 VALU ops per fp8 MFMA, not 8).
 // A query's q_I slab stays in VGPRs for the whole key sweep; k_I rows stream
 // through LDS in blocks shared by all waves of the workgroup.  Key blocks past
 // the workgroup's last query are never loaded (causal skipping), and no L x L
 // matrix exists: scores go to a [queries-of-chunk, visible keys] tile, written
 // 64 contiguous keys per store instruction.
+#include <algorithm>
+
 #include "common.h"
 
 using namespace ic;
@@ -87,43 +100,138 @@ __device__ __forceinline__ f32x4 tile_mma(const Frag<FP8, D_I>& a, const Frag<FP
 // max(x, 0) in one instruction for the finite MFMA outputs.
 __device__ __forceinline__ float relu(float x) { return __builtin_amdgcn_fmed3f(x, 0.f, 3.0e38f); }
 
-// ReLU, head weights, sum over this lane's heads, then over the 4 lane rows.
+// ReLU and head weights over this lane's heads (its part of the 64-head sum).
 template <int HT>
-__device__ __forceinline__ float head_reduce(const f32x4 (&acc)[HT], const float (&wv)[HT][4]) {
+__device__ __forceinline__ float head_partial(const f32x4 (&acc)[HT], const float (&wv)[HT][4]) {
     float s = 0.f;
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int e = 0; e < 4; ++e) s = fmaf(wv[ht][e], relu(acc[ht][e]), s);
-    s = sum_xor16(s);
-    s = sum_xor32(s);
     return s;
 }
 
-// v[g] for lane row g (g < 4).
-__device__ __forceinline__ float pick4(float a, float b, float c, float d, int g) {
-    return g < 2 ? (g == 0 ? a : b) : (g == 2 ? c : d);
+// Same in the |y| form: s0 + sum_e w'_e |y_e| (w' = w/2).
+template <int HT>
+__device__ __forceinline__ float head_partial_abs(const f32x4 (&acc)[HT], const float (&wv)[HT][4], float s) {
+#pragma unroll
+    for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s = fmaf(wv[ht][e], fabsf(acc[ht][e]), s);
+    return s;
+}
+
+// Finishes the head sums of four key tiles at once: p_i is a lane's partial for tile
+// i, and lane row g returns the sum of p_g over the four lane rows, added as
+// (rows 0+1) + (rows 2+3).  Three lane-row swaps and three adds replace eight of
+// each, and lane row g ends up holding exactly the tile it stores.
+__device__ __forceinline__ float rowsum_scatter4(float p0, float p1, float p2, float p3) {
+    // swap16(x, y): x' = rows (x0, y0, x2, y2), y' = rows (x1, y1, x3, y3)
+    const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const u32x2 b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+    const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    // swap32(x, y): x' = rows (x0, x1, y0, y1), y' = rows (x2, x3, y2, y3)
+    const u32x2 c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Linear-term operand of one wave's two queries: the head-weighted query
+// qt = sum_j w_j q_I[j, :] (fp32) as LIN_NP e4m3 parts.  Part p of query q is MFMA
+// row 4*(p/2) + 2*q + p%2, so lane row g finds parts 2g, 2g+1 of query 0 in
+// accumulator elements 0, 1 and those of query 1 in elements 2, 3.
+//
+// Scale blocks.  The scaled MFMA numbers K so that bytes 0-15 of the four lane
+// rows come first and bytes 16-31 second; its 32-element block b is therefore
+// bytes 0-15 (b = 0, 1) or 16-31 (b = 2, 3) of lane rows 2(b%2) and 2(b%2)+1, and
+// lane row b supplies that block's scale.  With lane row g holding channels
+// 32g..32g+31 (as the k_I fragments do), channel c falls in block
+// (c >= 64) + 2 * (c % 32 >= 16).
+constexpr int LIN_NP = 8;
+struct LinScratch {
+    uint8_t part[16][128];   // [row][channel] e4m3 bytes
+    uint8_t scale[16][4];    // [row][scale block] E8M0
+};
+
+template <int D_I>
+__device__ void build_lin_rows(LinScratch& ls, const uint8_t* __restrict__ qI, const float* __restrict__ w,
+                               const int64_t (&qrow)[2], const bool (&valid)[2], int H_I, int lane) {
+    const int c = 2 * lane;                                   // this lane's channels c, c+1
+    const int blk = (lane >= 32) + 2 * ((lane & 15) >= 8);    // their scale block; its lanes differ in bits 0-2, 4
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        float r0 = 0.f, r1 = 0.f;
+        if (valid[q] && c < D_I) {
+            const uint8_t* base = qI + qrow[q] * D_I + c;
+            const float* wq = w + qrow[q];
+            int j = 0;
+            for (; j + 4 <= H_I; j += 4) {
+                unsigned short v[4];
+                float wj[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    v[u] = *reinterpret_cast<const unsigned short*>(base + (int64_t)(j + u) * D_I);
+                    wj[u] = wq[j + u];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(v[u], false);
+                    r0 = fmaf(wj[u], f[0], r0);
+                    r1 = fmaf(wj[u], f[1], r1);
+                }
+            }
+            for (; j < H_I; ++j) {
+                const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(
+                    *reinterpret_cast<const unsigned short*>(base + (int64_t)j * D_I), false);
+                r0 = fmaf(wq[j], f[0], r0);
+                r1 = fmaf(wq[j], f[1], r1);
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < LIN_NP; ++p) {
+            // Block scale: the block's largest |residual| maps into [128, 256), far from
+            // e4m3's 448 limit; the byte also carries the 1/2 of the |y| split.
+            float m = fmaxf(fabsf(r0), fabsf(r1));
+            m = fmaxf(m, __shfl_xor(m, 1));
+            m = fmaxf(m, __shfl_xor(m, 2));
+            m = fmaxf(m, __shfl_xor(m, 4));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            const int e = __builtin_amdgcn_frexp_expf(m) - 8;
+            const bool ok = e + 126 >= 0;                     // residuals below 2^-118 are dropped
+            const float v0 = ok ? ldexpf(r0, -e) : 0.f;
+            const float v1 = ok ? ldexpf(r1, -e) : 0.f;
+            const int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false) & 0xffff;
+            const f32x2 back = __builtin_amdgcn_cvt_pk_f32_fp8(pk, false);
+            r0 -= ldexpf(back[0], e);
+            r1 -= ldexpf(back[1], e);
+            const int row = 4 * (p >> 1) + 2 * q + (p & 1);
+            *reinterpret_cast<unsigned short*>(&ls.part[row][c]) = (unsigned short)pk;
+            if ((lane & 23) == 0) ls.scale[row][blk] = (uint8_t)(ok ? e + 126 : 0);   // lanes 0, 8, 32, 40
+        }
+    }
 }
 
 // Head weights of this lane (heads 16*ht + 4g + e) for one query row (NULL -> zeros).
 template <int HT>
-__device__ __forceinline__ void load_w(float (&wr)[HT][4], const float* wrow, int H_I, int g) {
+__device__ __forceinline__ void load_w(float (&wr)[HT][4], const float* wrow, int H_I, int g, float f = 1.f) {
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int hh = 16 * ht + 4 * g + e;
-            wr[ht][e] = (wrow != nullptr && hh < H_I) ? wrow[hh] : 0.f;
+            wr[ht][e] = (wrow != nullptr && hh < H_I) ? f * wrow[hh] : 0.f;
         }
 }
 
 // ---------------------------------------------------------------------------
 // Prefill: workgroup = QW*NW consecutive queries of a chunk, all their keys.
 // ---------------------------------------------------------------------------
+// Two waves per SIMD is the occupancy either workgroup size runs at; saying so keeps the
+// compiler from parking MFMA accumulators in AGPRs (each VALU read would then cost a copy).
 template <bool FP8, int D_I, int HT, int QW, int NW, int KB>
-__global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_prefill_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    float* __restrict__ scores, int64_t row_stride, int q_begin, int nq, int pos_begin, int H_I) {
+    float* __restrict__ scores, int64_t row_stride, int q_begin, int nq, int pos_begin, int H_I, int seg_blocks) {
     using G = IdxGeom<FP8, D_I>;
     static_assert(KB % 64 == 0, "a key block is stored 64 keys per instruction");
     constexpr int QB = QW * NW;
@@ -132,10 +240,12 @@ __global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
     constexpr int CHUNKS = KB * G::ROWB / 16;                 // 16-byte pieces per key block
     constexpr int CPT = (CHUNKS + NT - 1) / NT;               // pieces per thread
     constexpr int CPR = G::ROWB / 16;                         // pieces per key row
+    constexpr bool LIN = FP8 && QW == 2;                      // |y| epilogue + linear-term MFMA row
     __shared__ __attribute__((aligned(32))) uint8_t lds[2][KB * G::LSTR];
+    __shared__ __attribute__((aligned(32))) LinScratch lin_lds[LIN ? NW : 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wv = tid >> 6;
+    const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int nblk = (nq + QB - 1) / QB;
     const int blk = nblk - 1 - (int)blockIdx.x;               // late (long) query blocks first
@@ -143,25 +253,42 @@ __global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
     const int t_last = min(t0 + QB, nq) - 1;
     const int nkeys = pos_begin + t_last + 1;                 // keys visible to the block
     const int nkb = (nkeys + KB - 1) / KB;
+    // Work item: this query block's key blocks [kb_begin, kb_end).  Scores need no sum
+    // across keys, so splitting long rows into segments only balances the load.
+    const int kb_begin = (int)blockIdx.y * seg_blocks;
+    if (kb_begin >= nkb) return;                              // past the causal edge (whole workgroup)
+    const int kb_end = min(nkb, kb_begin + seg_blocks);
 
     // This wave's queries: A fragments (q_I slabs) and head weights, kept in VGPRs.
     Frag<FP8, D_I> A[QW][HT];
     float wr[QW][HT][4];
     int pq[QW];                                               // absolute position, -1 if no query
     float* srow[QW];
+    int64_t qrows[QW];
+    bool qvalid[QW];
 #pragma unroll
     for (int q = 0; q < QW; ++q) {
         const int t = t0 + wv * QW + q;
         const bool valid = t < nq;
+        qvalid[q] = valid;
         pq[q] = valid ? pos_begin + t : -1;
         srow[q] = scores + (int64_t)(valid ? t : 0) * row_stride + 16 * g + r;
         const int64_t qrow = (int64_t)(q_begin + (valid ? t : 0)) * H_I;
+        qrows[q] = qrow;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
             const int h = 16 * ht + r;
             load_frag<FP8, D_I>(A[q][ht], (valid && h < H_I) ? qI + (qrow + h) * G::ROWB : nullptr, g);
         }
-        load_w<HT>(wr[q], valid ? w + qrow : nullptr, H_I, g);
+        load_w<HT>(wr[q], valid ? w + qrow : nullptr, H_I, g, LIN ? 0.5f : 1.f);
+    }
+    i32x8 Alin = {0, 0, 0, 0, 0, 0, 0, 0};
+    int sAlin = 0;
+    if constexpr (LIN) {
+        build_lin_rows<D_I>(lin_lds[wv], qI, w, qrows, qvalid, H_I, lane);
+        __syncthreads();
+        Alin = *reinterpret_cast<const i32x8*>(&lin_lds[wv].part[r][32 * g]);
+        sAlin = lin_lds[wv].scale[r][g];
     }
 
     // Cooperative k_I block load: piece c -> key c / CPR, byte offset (c % CPR) * 16.
@@ -170,11 +297,11 @@ __global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
 #pragma unroll
         for (int i = 0; i < CPT; ++i) {
             const int c = tid + i * NT;
-            const int key = kb * KB + c / CPR;
-            i32x4 v = {0, 0, 0, 0};
-            if (c < CHUNKS && key < nkeys)
-                v = *reinterpret_cast<const i32x4*>(kI + (int64_t)key * G::ROWB + (c % CPR) * 16);
-            stage[i] = v;
+            // Keys past the block's last visible key re-read that key: their score
+            // columns are never stored, and the load needs no branch.
+            const int key = min(kb * KB + c / CPR, nkeys - 1);
+            if (c < CHUNKS)
+                stage[i] = *reinterpret_cast<const i32x4*>(kI + (int64_t)key * G::ROWB + (c % CPR) * 16);
         }
     };
     auto lstore = [&](int buf) {
@@ -186,17 +313,21 @@ __global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
         }
     };
 
-    gload(0);
+    gload(kb_begin);
     lstore(0);
+    // Drain every load issued so far (q_I, w, block 0) on all paths, so the loop's only
+    // outstanding load is the next k_I block, waited for just before its LDS store.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-    for (int kb = 0; kb < nkb; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkb) gload(kb + 1);
+    for (int kb = kb_begin; kb < kb_end; ++kb) {
+        const int buf = (kb - kb_begin) & 1;
+        if (kb + 1 < kb_end) gload(kb + 1);
         // Software pipeline over the block's tiles: the MFMAs of tile kt are issued before
         // the ReLU / head-sum epilogue of tile kt-1, so matrix and vector units overlap.
         float val[QW][NKT];
         f32x4 acc[2][QW][HT];
+        f32x4 lin[2];
 #pragma unroll
         for (int kt = 0; kt <= NKT; ++kt) {
             if (kt < NKT) {
@@ -206,24 +337,43 @@ __global__ __launch_bounds__(NW * 64) void indexer_prefill_kernel(
                 for (int q = 0; q < QW; ++q)
 #pragma unroll
                     for (int ht = 0; ht < HT; ++ht) acc[kt & 1][q][ht] = tile_mma<FP8, D_I>(A[q][ht], Bf);
+                if constexpr (LIN) {
+                    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+                    lin[kt & 1] = mfma_fp8_k128_scale_a(Alin, sAlin, Bf.f8, z);
+                }
             }
             if (kt > 0) {
+                if constexpr (LIN) {
+                    const f32x4& l = lin[(kt - 1) & 1];
+                    val[0][kt - 1] = head_partial_abs<HT>(acc[(kt - 1) & 1][0], wr[0], l[0] + l[1]);
+                    val[1][kt - 1] = head_partial_abs<HT>(acc[(kt - 1) & 1][1], wr[1], l[2] + l[3]);
+                } else {
 #pragma unroll
-                for (int q = 0; q < QW; ++q) val[q][kt - 1] = head_reduce<HT>(acc[(kt - 1) & 1][q], wr[q]);
+                    for (int q = 0; q < QW; ++q) val[q][kt - 1] = head_partial<HT>(acc[(kt - 1) & 1][q], wr[q]);
+                }
             }
+            // One pipeline stage per scheduling region.  The partials are consumed by an
+            // empty asm so their VALU work stays in this stage: otherwise it sinks to the
+            // stores, every tile's MFMAs issue first and the live accumulators spill.
+            if (kt > 0) {
+#pragma unroll
+                for (int q = 0; q < QW; ++q) asm volatile("" : "+v"(val[q][kt - 1]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
+        // Stage the next block first: its wait then covers only that load, not the stores.
+        if (kb + 1 < kb_end) lstore(buf ^ 1);
         // Lane row g stores tile 4*grp + g: 64 consecutive keys per query per instruction.
 #pragma unroll
         for (int grp = 0; grp < NKT / 4; ++grp) {
             const int s = kb * KB + 64 * grp + 16 * g + r;
 #pragma unroll
             for (int q = 0; q < QW; ++q) {
-                const float v = pick4(val[q][4 * grp], val[q][4 * grp + 1], val[q][4 * grp + 2],
-                                      val[q][4 * grp + 3], g);
+                const float v = rowsum_scatter4(val[q][4 * grp], val[q][4 * grp + 1], val[q][4 * grp + 2],
+                                                val[q][4 * grp + 3]);
                 if (s <= pq[q]) srow[q][kb * KB + 64 * grp] = v;
             }
         }
-        if (kb + 1 < nkb) lstore(buf ^ 1);
         __syncthreads();
     }
 }
@@ -269,36 +419,60 @@ __global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
         f32x4 acc[HT];
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) acc[ht] = tile_mma<FP8, D_I>(A[ht], Bf[i]);
-        val[i] = head_reduce<HT>(acc, wr);
+        val[i] = head_partial<HT>(acc, wr);
     }
     float* srow = scores + (int64_t)b * score_stride;
 #pragma unroll
     for (int grp = 0; grp < DEC_TILES_PER_WAVE / 4; ++grp) {
         const int s = key0 + 64 * grp + 16 * g + r;
-        const float v = pick4(val[4 * grp], val[4 * grp + 1], val[4 * grp + 2], val[4 * grp + 3], g);
+        const float v = rowsum_scatter4(val[4 * grp], val[4 * grp + 1], val[4 * grp + 2], val[4 * grp + 3]);
         if (s < n) srow[s] = v;
     }
 }
 
+constexpr int PREFILL_KB = 64;                               // keys per LDS block
+
+// Key blocks per work item: the longest query block splits into about four pieces,
+// and no piece is shorter than 16 blocks (1024 keys), which keeps the per-item set-up
+// (q_I slab, linear-term rows) small next to its key sweep.
+inline int prefill_seg_blocks(const ic_indexer_args& a) {
+    const int nkb_max = (a.pos_begin + a.nq + PREFILL_KB - 1) / PREFILL_KB;
+    return std::max(16, (nkb_max + 3) / 4);
+}
+
+// Work items (query block, key segment) that are not past the causal edge.
+inline int64_t prefill_items(const ic_indexer_args& a, int QB, int seg_blocks) {
+    int64_t items = 0;
+    for (int t0 = 0; t0 < a.nq; t0 += QB) {
+        const int nkeys = a.pos_begin + std::min(t0 + QB, a.nq);
+        const int nkb = (nkeys + PREFILL_KB - 1) / PREFILL_KB;
+        items += (nkb + seg_blocks - 1) / seg_blocks;
+    }
+    return items;
+}
+
 template <bool FP8, int D_I, int HT, int NW>
-hipError_t prefill_launch(const ic_indexer_args& a, hipStream_t st) {
+hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t st) {
     constexpr int QW = FP8 ? 2 : 1;
-    constexpr int KB = 64;
     constexpr int QB = QW * NW;
     const int nblk = (a.nq + QB - 1) / QB;
-    hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D_I, HT, QW, NW, KB>), dim3(nblk), dim3(NW * 64), 0, st,
+    const int nkb_max = (a.pos_begin + a.nq + PREFILL_KB - 1) / PREFILL_KB;
+    const dim3 grid(nblk, (nkb_max + seg_blocks - 1) / seg_blocks);
+    hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D_I, HT, QW, NW, PREFILL_KB>), grid, dim3(NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.scores, a.row_stride,
-                       a.q_begin, a.nq, a.pos_begin, a.H_I);
+                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks);
     return hipGetLastError();
 }
 
-// 8-wave workgroups share each k_I block among 16 queries; when that leaves fewer than
-// two workgroups per CU (a 4096-query chunk), 4-wave workgroups keep the CUs fed.
+// 8-wave workgroups share each k_I block among 16 queries (one workgroup per CU at two
+// waves per SIMD); when that leaves fewer than four work items per CU, 4-wave workgroups
+// (two per CU) keep the CUs fed.
 template <bool FP8, int D_I, int HT>
 hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
     constexpr int QW = FP8 ? 2 : 1;
-    if ((a.nq + QW * 8 - 1) / (QW * 8) >= 512) return prefill_launch<FP8, D_I, HT, 8>(a, st);
-    return prefill_launch<FP8, D_I, HT, 4>(a, st);
+    const int seg = prefill_seg_blocks(a);
+    if (prefill_items(a, QW * 8, seg) >= 1024) return prefill_launch<FP8, D_I, HT, 8>(a, seg, st);
+    return prefill_launch<FP8, D_I, HT, 4>(a, seg, st);
 }
 
 template <bool FP8, int D_I, int HT>
