@@ -77,13 +77,16 @@ def lib() -> ctypes.CDLL:
     L.ic_indexer_topk.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_indexer_scores.argtypes = [P(Shape), vp, vp, vp, vp, i64, vp]
     L.ic_topk_rows.argtypes = [vp, i64, i32, i32, i32, vp, vp]
+    L.ic_topk_rows_seq.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, sz, vp]
+    L.ic_topk_rows_seq_ws.argtypes = [i32, i32, i32]
+    L.ic_topk_rows_seq_ws.restype = sz
     L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
-    for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_sparse_attn", "ic_run_stack",
+    for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_sparse_attn", "ic_run_stack",
                "ic_decode_step", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -193,6 +196,30 @@ def topk_rows(scores, first_len: int, k: int, idx=None, stream=None):
     if idx is None:
         idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
     _check(lib().ic_topk_rows(_ptr(scores), stride, rows, first_len, k, _ptr(idx), _stream(stream)))
+    return idx
+
+
+def topk_rows_seq_ws(rows: int, max_len: int, k: int) -> int:
+    return int(lib().ic_topk_rows_seq_ws(rows, max_len, k))
+
+
+def topk_rows_seq(scores, seq_len, k: int, max_len: Optional[int] = None, idx=None, ws=None,
+                  segmented: bool = True, stream=None):
+    """Top-k of score rows [rows, row_stride]; row r has seq_len[r] (device int32) visible
+    entries, at most max_len (default row_stride).  segmented=False forces the
+    one-workgroup-per-row path for long rows."""
+    _need(scores, "scores", (torch.float32,), 2)
+    _need(seq_len, "seq_len", (torch.int32,), 1)
+    rows, stride = scores.shape
+    max_len = stride if max_len is None else max_len
+    if idx is None:
+        idx = torch.empty((rows, k), dtype=torch.int32, device=scores.device)
+    if segmented:
+        ws = _workspace(topk_rows_seq_ws(rows, max_len, k), scores.device, ws)
+    else:
+        ws = None
+    _check(lib().ic_topk_rows_seq(_ptr(scores), stride, rows, _ptr(seq_len), max_len, k, _ptr(idx), _ptr(ws),
+                                  0 if ws is None else ws.numel(), _stream(stream)))
     return idx
 
 

@@ -79,27 +79,36 @@ size_t indexer_ws(const ic_shape& s) {
     return (size_t)round_up(rows * round_up((int64_t)s.pos0 + s.Lq, 4) * 4, 256);
 }
 
-// Key splits per decode query: enough waves to fill the GPU (~2048), at most one
+// Key splits per decode query: about 1024 waves in all (one per SIMD; more splits
+// only add partials for the combine to merge, fewer leave CUs idle), at most one
 // 32-row tile per split, and a multiple of 4 (a workgroup merges 4 splits).
 int decode_splits(const ic_shape& s) {
     const int HG = (s.H + 15) / 16;
-    const int want = (2048 + s.B * HG - 1) / (s.B * HG);
+    const int want = (1024 + s.B * HG - 1) / (s.B * HG);
     const int tiles = (s.k + 31) / 32;
     const int ns = std::min(want, tiles);
     return ns < 4 ? 1 : ns / 4 * 4;
 }
 
-// Decode workspace: scores [B, round_up(Lk, 4)] fp32 | attention partials.
+// Decode workspace: scores [B, round_up(Lk, 4)] fp32 | attention partials | top-k
+// candidates (segmented top-k of long rows; cand_off == 0 when not used).
 struct DecodeWs {
     int64_t score_stride;
-    size_t scores_off, part_off, total;
+    size_t scores_off, part_off, cand_off, total;
 };
 DecodeWs decode_layout(const ic_shape& s) {
     DecodeWs w;
     w.score_stride = round_up(s.Lk, 4);                   // 16-byte rows for the top-k's vector loads
     w.scores_off = 0;
     w.part_off = (size_t)round_up((int64_t)s.B * w.score_stride * 4, 256);
-    w.total = w.part_off + (size_t)round_up(sparse_attn_ws_bytes(s.B, s.H, s.d, decode_splits(s)), 256);
+    const size_t cand_at = w.part_off + (size_t)round_up(sparse_attn_ws_bytes(s.B, s.H, s.d, decode_splits(s)), 256);
+    ic_topk_args t{};
+    t.rows = s.B;
+    t.k = s.k;
+    t.max_len = s.Lk;
+    const size_t cand_bytes = topk_ws_bytes(t);
+    w.cand_off = cand_bytes ? cand_at : 0;
+    w.total = cand_at + (size_t)round_up((int64_t)cand_bytes, 256);
     return w;
 }
 size_t decode_ws(const ic_shape& s) { return decode_layout(s).total; }
@@ -150,6 +159,7 @@ ic_status run_indexer_topk(const ic_shape& s, const void* q_I, const float* w, c
             t.k = s.k;
             t.idx = idx + ((size_t)b * s.Lq + c0) * s.k;
             t.max_len = s.pos0 + c0 + nq;
+            t.cand = nullptr;
             e = launch_topk(t, st);
             if (e != hipSuccess) return hip_fail(e, "top-k launch");
             if (tiles) ++*tiles;
@@ -282,6 +292,43 @@ ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, in
     t.k = k;
     t.idx = idx;
     t.max_len = first_len + rows - 1;
+    t.cand = nullptr;
+    hipError_t e = launch_topk(t, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "top-k launch");
+    return IC_OK;
+}
+
+size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k) {
+    if (rows < 1 || max_len < 1 || k < 1 || k > kMaxK) return 0;
+    ic_topk_args t{};
+    t.rows = rows;
+    t.max_len = max_len;
+    t.k = k;
+    return topk_ws_bytes(t);
+}
+
+ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32_t rows, const int32_t* seq_len,
+                           int32_t max_len, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    if (!scores || !seq_len || !idx) return fail(IC_ERR_ARG, "scores, seq_len and idx must be non-NULL");
+    if (rows < 1 || max_len < 1 || k < 1 || k > kMaxK)
+        return fail(IC_ERR_SHAPE, "need rows >= 1, max_len >= 1, 1 <= k <= %d", kMaxK);
+    if (max_len > row_stride)
+        return fail(IC_ERR_SHAPE, "max_len %d exceeds row_stride %lld", max_len, (long long)row_stride);
+    ic_topk_args t;
+    t.scores = scores;
+    t.row_stride = row_stride;
+    t.rows = rows;
+    t.first_len = 0;
+    t.seq_len = seq_len;
+    t.k = k;
+    t.idx = idx;
+    t.max_len = max_len;
+    t.cand = nullptr;
+    if (ws != nullptr) {
+        const size_t need = topk_ws_bytes(t);
+        if (ic_status r = check_ws(ws, ws_bytes, need)) return r;
+        if (need) t.cand = static_cast<int32_t*>(ws);
+    }
     hipError_t e = launch_topk(t, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "top-k launch");
     return IC_OK;
@@ -369,6 +416,7 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
             t.k = s.k;
             t.idx = idx_cache;
             t.max_len = s.Lk;
+            t.cand = lay.cand_off ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + lay.cand_off) : nullptr;
             e = launch_topk(t, st);
             if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
             cached = true;

@@ -267,6 +267,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 
 // Merge the workgroups' partials of each (query, head) in split order: one
 // workgroup per (query, head), one thread per channel.
+constexpr int COMBINE_FAST = 16;        // partials merged from registers after one round of loads
 template <int D>
 __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
                                                         int H, int nparts) {
@@ -276,15 +277,39 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
     const int hg = head / 16, hn = head % 16;
     const float* base = part + (qi * HG + hg) * nparts * (16 * D + 32);
     const int dd = threadIdx.x;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, base[p * (16 * D + 32) + 16 * D + 2 * hn]);
-    float num = 0.f, den = 0.f;
-    for (int p = 0; p < nparts; ++p) {
-        const float* ps = base + p * (16 * D + 32);
-        const float m = ps[16 * D + 2 * hn];
-        const float c = (m == -INFINITY) ? 0.f : exp2f(m - M);   // a split with no selected rows adds nothing
-        num += c * ps[hn * D + dd];
-        den += c * ps[16 * D + 2 * hn + 1];
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    if (nparts <= COMBINE_FAST) {
+        // Every load issued before any use: one memory round trip for the whole merge.
+        float mm[COMBINE_FAST], ll[COMBINE_FAST], oo[COMBINE_FAST];
+#pragma unroll
+        for (int p = 0; p < COMBINE_FAST; ++p) {
+            mm[p] = -INFINITY;
+            ll[p] = 0.f;
+            oo[p] = 0.f;
+            if (p < nparts) {
+                const float* ps = base + p * (16 * D + 32);
+                mm[p] = ps[16 * D + 2 * hn];
+                ll[p] = ps[16 * D + 2 * hn + 1];
+                oo[p] = ps[hn * D + dd];
+            }
+        }
+#pragma unroll
+        for (int p = 0; p < COMBINE_FAST; ++p) M = fmaxf(M, mm[p]);
+#pragma unroll
+        for (int p = 0; p < COMBINE_FAST; ++p) {
+            const float c = (mm[p] == -INFINITY) ? 0.f : exp2f(mm[p] - M);   // empty split adds nothing
+            num += c * oo[p];
+            den += c * ll[p];
+        }
+    } else {
+        for (int p = 0; p < nparts; ++p) M = fmaxf(M, base[p * (16 * D + 32) + 16 * D + 2 * hn]);
+        for (int p = 0; p < nparts; ++p) {
+            const float* ps = base + p * (16 * D + 32);
+            const float m = ps[16 * D + 2 * hn];
+            const float c = (m == -INFINITY) ? 0.f : exp2f(m - M);   // a split with no selected rows adds nothing
+            num += c * ps[hn * D + dd];
+            den += c * ps[16 * D + 2 * hn + 1];
+        }
     }
     const float v = num / den;
     uint32_t u = __float_as_uint(v);

@@ -112,7 +112,14 @@ struct ic_topk_args {
     int32_t k;
     int32_t* idx;         // [rows, k]
     int32_t max_len;      // upper bound of any row's visible length (host-known)
+    int32_t* cand;        // optional workspace of topk_ws_bytes(): few long rows run segmented
 };
+// Few long rows (decode) are ranked in TOPK_SEG-key segments first, then over the
+// segments' candidates; that needs topk_ws_bytes() of workspace (0 otherwise).
+constexpr int TOPK_SEG = 8192;
+constexpr int TOPK_SEG_MAX_ROWS = 1024;
+int topk_segments(const ic_topk_args& a);
+size_t topk_ws_bytes(const ic_topk_args& a);
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st);
 
 struct ic_attn_args {

@@ -22,6 +22,14 @@
 // counts) and a prefix sum over the waves, so the output is sorted for free
 // and ties resolve to the lowest indices.
 //
+// Few long rows (decode: one row per sequence) would leave most CUs idle, so
+// they run in two launches.  First every (row, segment of SEG keys) takes its
+// own top-k with the register-resident select, writing global positions; the
+// row's top-k lies inside the union of those.  Then one workgroup per row
+// selects from that candidate list, reading each candidate's score by position.
+// Candidates are in ascending position order, so the index-order compaction
+// still gives ascending output and ties still go to the lower position.
+//
 // The row is cut into blocks of NT*EPT keys.  In a block, wave w owns the
 // contiguous span [w*64*EPT, (w+1)*64*EPT) and lane l holds its keys
 // 256*j + 4*l + e (j < EPT/4, e < 4): loads are coalesced 16-byte vectors and
@@ -67,10 +75,15 @@ __device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wt
     return before;
 }
 
-template <int NT, int EPT, bool VEC, bool STREAM>
+// Row sources: a score row; a segment of one (TOPK_SEGS: launch row = row * nseg +
+// segment); or a row's candidate positions (TOPK_GATHER).
+enum { TOPK_ROWS = 0, TOPK_SEGS = 1, TOPK_GATHER = 2 };
+
+template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
                                                   int first_len, const int32_t* __restrict__ seq_len, int k,
-                                                  int32_t* __restrict__ idx, int max_len) {
+                                                  int32_t* __restrict__ idx, int max_len, int seg, int nseg,
+                                                  const int32_t* __restrict__ cand, int cand_len) {
     constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
     constexpr int BLOCK = NT * EPT;                  // keys per block
     // Long rows keep one histogram per wave: a concentrated score distribution puts
@@ -79,7 +92,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     constexpr int NH = (NT * EPT > 32768) ? NT / 64 : 1;
     __shared__ uint32_t hist[NH][HIST_BINS];
     __shared__ uint32_t wtot[NT / 64];
-    __shared__ uint32_t kminmax[2], found[3];
+    __shared__ uint32_t kminmax[3], found[3];
     __shared__ uint32_t cand_key[CAND_CAP];
     __shared__ int32_t cand_idx[CAND_CAP];
     __shared__ uint32_t ncand, thr_key;
@@ -87,14 +100,29 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = tid >> 6;
-    // visible length, clamped to the allocated row (a bad seq_len cannot overrun)
-    const int n = max(1, min(seq_len ? seq_len[row] : first_len + row, STREAM ? max_len : min(max_len, BLOCK)));
     int32_t* out = idx + (int64_t)row * k;
-    if (n <= k) {                                    // every visible key is selected
-        for (int i = tid; i < k; i += NT) out[i] = i < n ? i : -1;
+    const int srow = MODE == TOPK_SEGS ? row / nseg : row;   // score row
+    // visible length of the score row, clamped to the allocated row (a bad seq_len cannot overrun)
+    const int len = max(1, min(seq_len ? seq_len[srow] : first_len + srow,
+                               (STREAM || MODE != TOPK_ROWS) ? max_len : min(max_len, BLOCK)));
+    int n = len, off = 0;                            // keys this workgroup ranks; position offset
+    if constexpr (MODE == TOPK_SEGS) {
+        off = (row % nseg) * seg;
+        n = min(seg, len - off);
+        if (n <= 0) {                                // segment past the row's end
+            for (int i = tid; i < k; i += NT) out[i] = -1;
+            return;
+        }
+    }
+    if (MODE == TOPK_GATHER ? len <= k : n <= k) {   // every visible key is selected
+        for (int i = tid; i < k; i += NT) out[i] = i < n ? off + i : -1;
         return;
     }
-    const float* src = scores + (int64_t)row * row_stride;
+    const float* src = scores + (int64_t)srow * row_stride + off;
+    const int32_t* crow = cand + (int64_t)row * (MODE == TOPK_GATHER ? cand_len : 0);
+    if constexpr (MODE == TOPK_GATHER) n = cand_len;  // candidate slots (-1 = none)
+    // output value of the key at position p of what this workgroup ranks
+    auto out_pos = [&](int p) -> int32_t { return MODE == TOPK_GATHER ? crow[p] : off + p; };
     const int lane_base = wv * 64 * EPT + 4 * lane;  // element of (round 0, slot 0) within a block
     const int nblocks = STREAM ? (n + BLOCK - 1) / BLOCK : 1;
 
@@ -105,6 +133,24 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         for (int j = 0; j < NR; ++j) {
             const int i0 = b0 + 256 * j;
             float v[4] = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (MODE == TOPK_GATHER) {     // candidate positions, then their scores
+                int c[4] = {-1, -1, -1, -1};
+                if (VEC) {
+                    if (i0 < n) {
+                        const int4 cv = *reinterpret_cast<const int4*>(crow + i0);
+                        c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) c[e] = (i0 + e < n) ? crow[i0 + e] : -1;
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const bool ok = c[e] >= 0 && c[e] < len;
+                    key[4 * j + e] = ok ? score_key(src[c[e]]) : 0u;
+                }
+                continue;
+            }
             if (VEC) {
                 if (i0 < n) {                        // 16 B stay inside the row: row_stride % 4 == 0
                     const float4 f = *reinterpret_cast<const float4*>(src + i0);
@@ -122,10 +168,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             for (int e = 0; e < 4; ++e) key[4 * j + e] = (i0 + e < n) ? score_key(v[e]) : 0u;
         }
     };
-    const uint32_t n_pad = (uint32_t)(nblocks * BLOCK - n);   // key-0 slots in the whole row
-
-    // Smallest and largest real key of the row.
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+    // Smallest and largest real key of the row, and (candidate lists) the empty slots.
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u, zeros = 0u;
     for (int blk = 0; blk < nblocks; ++blk) {
         load_block(blk);
 #pragma unroll
@@ -135,6 +179,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                 const uint32_t kk = key[4 * j + e];
                 lo = min(lo, kk ? kk : 0xFFFFFFFFu);
                 hi = max(hi, kk);
+                if (MODE == TOPK_GATHER) zeros += kk == 0u;
             }
     }
 #pragma unroll
@@ -142,11 +187,18 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         lo = min(lo, (uint32_t)__shfl_xor(lo, o));
         hi = max(hi, (uint32_t)__shfl_xor(hi, o));
     }
-    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; }
+    if (MODE == TOPK_GATHER) zeros = wave_sum(zeros);
+    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; kminmax[2] = 0u; }
     __syncthreads();
-    if (lane == 0) { atomicMin(&kminmax[0], lo); atomicMax(&kminmax[1], hi); }
+    if (lane == 0) {
+        atomicMin(&kminmax[0], lo);
+        atomicMax(&kminmax[1], hi);
+        if (MODE == TOPK_GATHER) atomicAdd(&kminmax[2], zeros);
+    }
     __syncthreads();
     const uint32_t kmin = kminmax[0], kmax = kminmax[1];
+    // key-0 slots in the whole row: padding past the end (and empty candidate slots)
+    const uint32_t n_pad = MODE == TOPK_GATHER ? kminmax[2] : (uint32_t)(nblocks * BLOCK - n);
 
     // Radix select: candidates are the keys with (key >> shift) == prefix.
     int shift = (kmin == kmax) ? 0 : 32 - __clz(kmin ^ kmax);
@@ -290,7 +342,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (sel[e]) {
-                        if (r < (uint32_t)k) out[r] = b0 + 256 * j + e;
+                        if (r < (uint32_t)k) out[r] = out_pos(b0 + 256 * j + e);
                         ++r;
                     }
                 }
@@ -302,7 +354,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
 
     // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them.
+    // Empty candidate slots (key 0) sit anywhere in a candidate list, so they never count as
+    // equal (key 0 is never above the prefix either).
     auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
+    auto is_eq = [&](uint32_t kk) -> bool { return digit(kk) == prefix && (MODE != TOPK_GATHER || kk != 0u); };
     uint32_t eq_run = 0, pos_run = 0;                // totals of earlier blocks
     for (int blk = 0; blk < nblocks; ++blk) {
         if (STREAM) load_block(blk);
@@ -310,7 +365,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
         for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) eqc += digit(key[4 * j + e]) == prefix;
+            for (int e = 0; e < 4; ++e) eqc += is_eq(key[4 * j + e]);
         uint32_t eq_tot;
         uint32_t eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
         uint32_t selbits[(EPT + 31) / 32];
@@ -324,7 +379,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t dg = digit(key[4 * j + e]);
-                eq[e] = dg == prefix;
+                eq[e] = is_eq(key[4 * j + e]);
                 gt[e] = dg > prefix;
                 const uint64_t b = __ballot(eq[e]);
                 before += lanes_below(b);
@@ -360,7 +415,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (sel[e]) {
-                    if (r < (uint32_t)k) out[r] = b0 + 256 * j + e;
+                    if (r < (uint32_t)k) out[r] = out_pos(b0 + 256 * j + e);
                     ++r;
                 }
             }
@@ -371,26 +426,55 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     }
 }
 
-template <int NT, int EPT, bool STREAM>
-hipError_t topk_launch(const ic_topk_args& a, hipStream_t st) {
-    const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
-    if (vec)
-        hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
-                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-    else
-        hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM>), dim3(a.rows), dim3(NT), 0, st, a.scores,
-                           a.row_stride, a.first_len, a.seq_len, a.k, a.idx, a.max_len);
-    return hipGetLastError();
+// One launch of `rows` workgroups; `len` bounds what one workgroup ranks (the row, a
+// segment, or a candidate list) and picks the block shape.
+template <int MODE>
+hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int nseg, const int32_t* cand,
+                       int32_t* out, bool vec, hipStream_t st) {
+#define IC_TOPK_GO(NT, EPT, STREAM)                                                                          \
+    do {                                                                                                    \
+        if (vec)                                                                                            \
+            hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,      \
+                               a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
+                               nseg, cand, len);                                                            \
+        else                                                                                                \
+            hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,     \
+                               a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
+                               nseg, cand, len);                                                            \
+        return hipGetLastError();                                                                           \
+    } while (0)
+    if (len <= 2048) IC_TOPK_GO(256, 8, false);
+    if (len <= 4096) IC_TOPK_GO(256, 16, false);
+    if (len <= 16384) IC_TOPK_GO(1024, 16, false);
+    if (MODE != TOPK_ROWS || len <= 32768) IC_TOPK_GO(1024, 32, false);
+    IC_TOPK_GO(1024, 32, true);
+#undef IC_TOPK_GO
 }
 
 }  // namespace
 
+int topk_segments(const ic_topk_args& a) {
+    if (a.max_len <= 32768 || a.rows > TOPK_SEG_MAX_ROWS) return 0;
+    const int nseg = (a.max_len + TOPK_SEG - 1) / TOPK_SEG;
+    return (int64_t)nseg * a.k <= 32768 ? nseg : 0;          // the candidate list must stay register-resident
+}
+
+size_t topk_ws_bytes(const ic_topk_args& a) {
+    const int nseg = topk_segments(a);
+    return nseg ? (size_t)a.rows * nseg * a.k * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
     if (a.rows <= 0) return hipSuccess;
     const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
-    if (a.max_len <= 2048) return topk_launch<256, 8, false>(a, st);
-    if (a.max_len <= 4096) return topk_launch<256, 16, false>(a, st);
-    if (a.max_len <= 16384) return topk_launch<1024, 16, false>(a, st);
-    if (a.max_len <= 32768) return topk_launch<1024, 32, false>(a, st);
-    return topk_launch<1024, 32, true>(a, st);
+    const int nseg = topk_segments(a);
+    if (nseg && a.cand != nullptr) {
+        // segments of TOPK_SEG keys -> candidate positions [rows][nseg * k], then one select per row
+        hipError_t e = topk_launch<TOPK_SEGS>(a, a.rows * nseg, TOPK_SEG, TOPK_SEG, nseg, nullptr, a.cand,
+                                              vec && TOPK_SEG % 4 == 0, st);
+        if (e != hipSuccess) return e;
+        const int clen = nseg * a.k;
+        return topk_launch<TOPK_GATHER>(a, a.rows, clen, 0, 1, a.cand, a.idx, clen % 4 == 0, st);
+    }
+    return topk_launch<TOPK_ROWS>(a, a.rows, a.max_len, 0, 1, nullptr, a.idx, vec, st);
 }

@@ -148,6 +148,21 @@ ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float*
 ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len,
                        int32_t k, int32_t* idx, void* stream);
 
+/* Top-k of score rows with per-row lengths (the decode shape: one row per
+ * sequence), same rule as ic_indexer_topk: scores [rows, row_stride] fp32,
+ * row r has n_r = seq_len[r] visible entries, seq_len a DEVICE int32 [rows]
+ * whose values are clamped to 1..max_len (max_len <= row_stride, host-known
+ * bound); writes idx [rows, k] int32.  When rows are long (max_len > 32768)
+ * and few (rows <= 1024), each 8192-key segment is ranked first and then the
+ * segments' candidates, which needs ic_topk_rows_seq_ws() bytes of `ws`;
+ * with ws NULL such rows take the one-workgroup streaming path instead (same
+ * result). */
+ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32_t rows, const int32_t* seq_len,
+                           int32_t max_len, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes ic_topk_rows_seq can use for these sizes (0 if none). */
+size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k);
+
 /* Sparse attention of one layer (arXiv abstract: core attention over the k
  * selected tokens): out [B, Lq, H, d] bf16 from q, kv and idx [B, Lq, k]
  * (entries < 0 are skipped; every row must hold at least one entry >= 0 and

@@ -101,3 +101,25 @@ def test_workspace_sizes_scale_with_chunk(L):
     assert ic.workspace_size(s_small, ic.IC_OP_INDEXER_TOPK) == 1024 * 8192 * 4
     dec = _shape(B=32, Lq=1, Lk=65600, k=2048, H=16, d=128, H_I=64, d_I=128, idx_dtype=ic.IC_FP8_E4M3)
     assert ic.workspace_size(dec, ic.IC_OP_DECODE_STEP) >= 32 * 65600 * 4
+
+
+def test_topk_rows_seq_validation(L):
+    ws = ctypes.c_void_p(0x10000)
+    # NULL seq_len, bad k, max_len beyond the row stride: rejected before any launch
+    assert L.ic_topk_rows_seq(FAKE, 100, 4, None, 100, 8, FAKE, None, 0, None) == 1
+    assert L.ic_topk_rows_seq(FAKE, 100, 4, FAKE, 100, 0, FAKE, None, 0, None) == 2
+    assert L.ic_topk_rows_seq(FAKE, 100, 4, FAKE, 101, 8, FAKE, None, 0, None) == 2
+    # a workspace that is given must be large enough and 256-byte aligned
+    need = ic.topk_rows_seq_ws(32, 65600, 2048)
+    assert L.ic_topk_rows_seq(FAKE, 65600, 32, FAKE, 65600, 2048, FAKE, ws, need - 1, None) == 6
+    assert L.ic_topk_rows_seq(FAKE, 65600, 32, FAKE, 65600, 2048, FAKE, ctypes.c_void_p(0x10010), need, None) == 6
+
+
+def test_topk_rows_seq_workspace_sizes():
+    # short rows, or many rows, need none; few long rows keep k candidates per 8192-key segment
+    assert ic.topk_rows_seq_ws(32, 32768, 2048) == 0
+    assert ic.topk_rows_seq_ws(4096, 65600, 2048) == 0
+    assert ic.topk_rows_seq_ws(32, 65600, 2048) == 32 * 9 * 2048 * 4
+    assert ic.topk_rows_seq_ws(3, 40000, 100) == 3 * 5 * 100 * 4
+    # a candidate list longer than one register-resident block falls back to streaming
+    assert ic.topk_rows_seq_ws(8, 200000, 2048) == 0

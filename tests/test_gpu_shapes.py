@@ -96,9 +96,13 @@ def test_scores_match_oracle_within_bound_fp8():
     summary("fp8 scores vs exact", {"max_err_over_bound": worst})
 
 
+# Split-K decode attention: k = 256 gives 8 splits (2 partials), k = 520 gives 16
+# (17 tiles, the last one ragged), and k = 4096 gives 128 splits whose 32 partials,
+# most of them empty (every row has fewer than k keys), take the looped combine.
+@pytest.mark.parametrize("k", [256, 520, 4096])
 @pytest.mark.parametrize("dtype,dist", [("bf16", "int3"), ("fp8", "gauss")])
-def test_decode_ragged_vs_oracle_and_prefill(dtype, dist):
-    B, cap, H_I, d_I, k, H, d = 3, 1100, 64, 128, 256, 16, 128
+def test_decode_ragged_vs_oracle_and_prefill(dtype, dist, k):
+    B, cap, H_I, d_I, H, d = 3, 1100, 64, 128, 16, 128
     seq_len = [1100, 333, 1]
     pattern = "FSSF"
     caches = [_rand_layer(B, 1, cap, H_I, d_I, H, d, dtype, dist, 300 + i, full=(c == "F"))

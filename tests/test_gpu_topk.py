@@ -57,3 +57,46 @@ def test_topk_long_rows(n0):
 def test_topk_k_larger_than_rows():
     m = np.random.default_rng(1).standard_normal((8, 40)).astype(np.float32)
     _run(m, 10, 64)
+
+
+def _run_seq(mat: np.ndarray, lens, k: int):
+    """ic_topk_rows_seq, segmented and streamed, against the oracle on every row."""
+    rows, stride = mat.shape
+    sc = torch.from_numpy(mat).cuda()
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    seg = ic.topk_rows_seq(sc, sl, k).cpu().numpy()
+    one = ic.topk_rows_seq(sc, sl, k, segmented=False).cpu().numpy()
+    for r in range(rows):
+        want = O.topk_row(mat[r, :lens[r]], k)
+        assert np.array_equal(seg[r], want), f"segmented row {r} (n={lens[r]}, k={k})"
+        assert np.array_equal(one[r], want), f"streamed row {r} (n={lens[r]}, k={k})"
+
+
+@pytest.mark.parametrize("kind", ["ties", "zeros_signed", "random", "threshold_tie"])
+def test_topk_rows_seq_long(kind):
+    """Decode-shaped rows longer than one register block: the segmented path (segment
+    top-k, then a select over the candidates) must equal the oracle, with ragged last
+    segments, rows shorter than the longest (empty segments), and rows with n <= k."""
+    rng = np.random.default_rng({"ties": 1, "zeros_signed": 2, "random": 3, "threshold_tie": 4}[kind])
+    stride, k = 70001, 2048
+    lens = [70001, 65600, 40000, 32769, 8193, 2048, 100, 1]
+    rows = len(lens)
+    if kind == "ties":
+        m = rng.integers(-3, 4, size=(rows, stride)).astype(np.float32)
+    elif kind == "zeros_signed":
+        m = np.where(rng.random((rows, stride)) < 0.5, -0.0, 0.0).astype(np.float32)
+        m[:, ::37] = 1.0
+    elif kind == "random":
+        m = (rng.standard_normal((rows, stride)) * 50).astype(np.float32)
+    else:
+        m = np.abs(rng.standard_normal((rows, stride)).astype(np.float32)) * 30
+        m[:, 3::11] = np.float32(40.0)                    # ties straddling the k-th key
+    _run_seq(m, lens, k)
+
+
+@pytest.mark.parametrize("k", [1, 100, 4096])
+def test_topk_rows_seq_k(k):
+    rng = np.random.default_rng(k)
+    lens = [50000, 33000, 4096, 4097]
+    m = rng.integers(-20, 20, size=(len(lens), 50000)).astype(np.float32)
+    _run_seq(m, lens, k)
