@@ -22,7 +22,7 @@ ARCH = "gfx950"
 # Packed fp32 VALU ops are disabled for all device code (see the build notes).
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
+          "-fvisibility=hidden", "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -24,11 +24,12 @@
 //
 // Few long rows (decode: one row per sequence) would leave most CUs idle, so
 // they run in two launches.  First every (row, segment of SEG keys) takes its
-// own top-k with the register-resident select, writing global positions; the
-// row's top-k lies inside the union of those.  Then one workgroup per row
-// selects from that candidate list, reading each candidate's score by position.
-// Candidates are in ascending position order, so the index-order compaction
-// still gives ascending output and ties still go to the lower position.
+// own top-k with the register-resident select, writing each pick's global
+// position and key; the row's top-k lies inside the union of those.  Then one
+// workgroup per row selects from that candidate list (coalesced key loads, no
+// score gather).  Candidates are in ascending position order, so the
+// index-order compaction still gives ascending output and ties still go to the
+// lower position.
 //
 // The row is cut into blocks of NT*EPT keys.  In a block, wave w owns the
 // contiguous span [w*64*EPT, (w+1)*64*EPT) and lane l holds its keys
@@ -50,9 +51,33 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-__device__ __forceinline__ uint32_t wave_sum(uint32_t x) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+// Wave-wide sum / min / max, result in every lane: DPP pairs inside each 16-lane row
+// (quad swaps, half-row and row mirrors), then the two lane-row swaps.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t x, Op op) {
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    x = op(x, (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x140, 0xF, 0xF, false));  // row_mirror
+    const u32x2 a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = op(a[0], a[1]);
+    const u32x2 b = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return op(b[0], b[1]);
+}
+struct OpAdd { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return a + b; } };
+struct OpMin { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return min(a, b); } };
+struct OpMax { __device__ uint32_t operator()(uint32_t a, uint32_t b) const { return max(a, b); } };
+__device__ __forceinline__ uint32_t wave_sum(uint32_t x) { return wave_reduce(x, OpAdd()); }
+
+// Inclusive prefix sum over the 64 lanes in lane order: shifts within each 16-lane row,
+// then the row broadcasts of lane 15 (into rows 1, 3) and lane 31 (into rows 2, 3).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t x) {
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xF, 0xF, true);   // row_shr:1
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xF, 0xF, true);   // row_shr:2
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xF, 0xF, true);   // row_shr:4
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xF, 0xF, true);   // row_shr:8
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
 }
 
@@ -76,21 +101,26 @@ __device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wt
 }
 
 // Row sources: a score row; a segment of one (TOPK_SEGS: launch row = row * nseg +
-// segment); or a row's candidate positions (TOPK_GATHER).
+// segment; also writes the picks' keys to ckeys); or a row's candidates (TOPK_GATHER:
+// keys from ckeys, positions from cand).
 enum { TOPK_ROWS = 0, TOPK_SEGS = 1, TOPK_GATHER = 2 };
 
 template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
 __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
                                                   int first_len, const int32_t* __restrict__ seq_len, int k,
                                                   int32_t* __restrict__ idx, int max_len, int seg, int nseg,
-                                                  const int32_t* __restrict__ cand, int cand_len) {
+                                                  const int32_t* __restrict__ cand, int cand_len,
+                                                  uint32_t* __restrict__ ckeys) {
     constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
     constexpr int BLOCK = NT * EPT;                  // keys per block
     // Long rows keep one histogram per wave: a concentrated score distribution puts
     // most keys in a few bins, and per-wave copies keep the LDS atomics of different
     // waves apart.  Short rows share one copy (a cheaper scan wins there).
     constexpr int NH = (NT * EPT > 32768) ? NT / 64 : 1;
-    __shared__ uint32_t hist[NH][HIST_BINS];
+    // One-copy histograms alternate between two buffers: a pass zeroes the next pass's
+    // buffer while scanning its own, so zeroing costs no barrier.
+    constexpr int NHB = NH == 1 ? 2 : 1;
+    __shared__ uint32_t hist[NHB * NH][HIST_BINS];
     __shared__ uint32_t wtot[NT / 64];
     __shared__ uint32_t kminmax[3], found[3];
     __shared__ uint32_t cand_key[CAND_CAP];
@@ -106,21 +136,26 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     const int len = max(1, min(seq_len ? seq_len[srow] : first_len + srow,
                                (STREAM || MODE != TOPK_ROWS) ? max_len : min(max_len, BLOCK)));
     int n = len, off = 0;                            // keys this workgroup ranks; position offset
+    uint32_t* okey = ckeys + (int64_t)row * k;       // TOPK_SEGS: keys of the picks
     if constexpr (MODE == TOPK_SEGS) {
         off = (row % nseg) * seg;
         n = min(seg, len - off);
         if (n <= 0) {                                // segment past the row's end
-            for (int i = tid; i < k; i += NT) out[i] = -1;
+            for (int i = tid; i < k; i += NT) { out[i] = -1; okey[i] = 0u; }
             return;
         }
     }
+    const float* src = scores + (int64_t)srow * row_stride + off;
     if (MODE == TOPK_GATHER ? len <= k : n <= k) {   // every visible key is selected
-        for (int i = tid; i < k; i += NT) out[i] = i < n ? off + i : -1;
+        for (int i = tid; i < k; i += NT) {
+            out[i] = i < n ? off + i : -1;
+            if (MODE == TOPK_SEGS) okey[i] = i < n ? score_key(src[i]) : 0u;
+        }
         return;
     }
-    const float* src = scores + (int64_t)srow * row_stride + off;
     const int32_t* crow = cand + (int64_t)row * (MODE == TOPK_GATHER ? cand_len : 0);
-    if constexpr (MODE == TOPK_GATHER) n = cand_len;  // candidate slots (-1 = none)
+    const uint32_t* ckrow = ckeys + (int64_t)row * (MODE == TOPK_GATHER ? cand_len : 0);
+    if constexpr (MODE == TOPK_GATHER) n = cand_len;  // candidate slots (key 0 = none)
     // output value of the key at position p of what this workgroup ranks
     auto out_pos = [&](int p) -> int32_t { return MODE == TOPK_GATHER ? crow[p] : off + p; };
     const int lane_base = wv * 64 * EPT + 4 * lane;  // element of (round 0, slot 0) within a block
@@ -129,28 +164,25 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     uint32_t key[EPT];
     auto load_block = [&](int blk) {
         const int b0 = blk * BLOCK + lane_base;
+        if constexpr (MODE == TOPK_GATHER) {         // the candidates' keys, as the segments wrote them
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                const int i0 = b0 + 256 * j;
+                if (VEC) {
+                    uint4 kv = make_uint4(0u, 0u, 0u, 0u);
+                    if (i0 < n) kv = *reinterpret_cast<const uint4*>(ckrow + i0);
+                    key[4 * j] = kv.x; key[4 * j + 1] = kv.y; key[4 * j + 2] = kv.z; key[4 * j + 3] = kv.w;
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) key[4 * j + e] = (i0 + e < n) ? ckrow[i0 + e] : 0u;
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             const int i0 = b0 + 256 * j;
             float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (MODE == TOPK_GATHER) {     // candidate positions, then their scores
-                int c[4] = {-1, -1, -1, -1};
-                if (VEC) {
-                    if (i0 < n) {
-                        const int4 cv = *reinterpret_cast<const int4*>(crow + i0);
-                        c[0] = cv.x; c[1] = cv.y; c[2] = cv.z; c[3] = cv.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) c[e] = (i0 + e < n) ? crow[i0 + e] : -1;
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const bool ok = c[e] >= 0 && c[e] < len;
-                    key[4 * j + e] = ok ? score_key(src[c[e]]) : 0u;
-                }
-                continue;
-            }
             if (VEC) {
                 if (i0 < n) {                        // 16 B stay inside the row: row_stride % 4 == 0
                     const float4 f = *reinterpret_cast<const float4*>(src + i0);
@@ -182,13 +214,12 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                 if (MODE == TOPK_GATHER) zeros += kk == 0u;
             }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        lo = min(lo, (uint32_t)__shfl_xor(lo, o));
-        hi = max(hi, (uint32_t)__shfl_xor(hi, o));
-    }
+    lo = wave_reduce(lo, OpMin());
+    hi = wave_reduce(hi, OpMax());
     if (MODE == TOPK_GATHER) zeros = wave_sum(zeros);
     if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; kminmax[2] = 0u; }
+    // the first pass's histogram starts zeroed (both buffers when they alternate)
+    for (int b = tid; b < NHB * NH * HIST_BINS; b += NT) (&hist[0][0])[b] = 0u;
     __syncthreads();
     if (lane == 0) {
         atomicMin(&kminmax[0], lo);
@@ -205,13 +236,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     uint32_t prefix = shift >= 32 ? 0u : (kmax >> shift);
     uint32_t k_rem = (uint32_t)k;                    // still to take among the candidates
     bool ranked = false;                             // threshold bin resolved by ranking its keys
+    int hb = 0;                                      // histogram buffer of this pass
     while (shift > 0) {
         const int width = min(HIST_BITS, shift);
         const int sh_lo = shift - width;
         const uint32_t mask = (1u << width) - 1u;
         const int nb = 1 << width;
-        for (int b = tid; b < nb * NH; b += NT) hist[b / nb][b % nb] = 0u;
-        __syncthreads();
+        uint32_t (*H)[HIST_BINS] = &hist[hb * NH];
+        if (NHB == 1) {                              // one buffer: zero it now
+            for (int b = tid; b < nb * NH; b += NT) H[b / nb][b % nb] = 0u;
+            __syncthreads();
+        }
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
 #pragma unroll
@@ -220,41 +255,41 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t kk = key[4 * j + e];
                     if (shift >= 32 || (kk >> shift) == prefix)
-                        atomicAdd(&hist[NH > 1 ? wv : 0][(kk >> sh_lo) & mask], 1u);
+                        atomicAdd(&H[NH > 1 ? wv : 0][(kk >> sh_lo) & mask], 1u);
                 }
         }
         __syncthreads();
-        if (tid == 0 && n_pad != 0u && (shift >= 32 || prefix == 0u)) hist[0][0] -= n_pad;   // drop the key-0 slots
-        __syncthreads();
-        // Bin b with above(b) < k_rem <= above(b) + hist[b]; above = count in higher bins.
+        if (NHB == 2) {                              // the next pass's buffer (last read two passes ago)
+            uint32_t* nxt = &hist[(hb ^ 1) * NH][0];
+            for (int b = tid; b < HIST_BINS; b += NT) nxt[b] = 0u;
+        }
+        // Bin b with above(b) < k_rem <= above(b) + count(b), above = count in higher bins.
+        // Thread t holds bins 2047 - (BPT*t + j) (descending), so above is a prefix sum.
         constexpr int BPT = (HIST_BINS + NT - 1) / NT;
+        const bool drop_pad = n_pad != 0u && (shift >= 32 || prefix == 0u);   // key-0 slots sit in bin 0
         uint32_t local = 0, hv[BPT];
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
-            const int b = tid * BPT + j;
+            const int b = HIST_BINS - 1 - (tid * BPT + j);
             uint32_t c = 0;
-            if (b < nb) {
+            if (b >= 0 && b < nb) {
 #pragma unroll
-                for (int w = 0; w < NH; ++w) c += hist[w][b];
+                for (int w = 0; w < NH; ++w) c += H[w][b];
+                if (b == 0 && drop_pad) c -= n_pad;
             }
             hv[j] = c;
             local += c;
         }
-        uint32_t suf = local;                        // suffix sum over the lanes of this wave
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = __shfl_down(suf, o);
-            if (lane + o < 64) suf += y;
-        }
-        if (lane == 0) wtot[wv] = suf;
+        const uint32_t incl = wave_incl_scan(local);
+        if (lane == 63) wtot[wv] = incl;
         __syncthreads();
-        uint32_t above = suf - local;
+        uint32_t above = incl - local;
 #pragma unroll
-        for (int i = 0; i < NT / 64; ++i) above += (i > wv) ? wtot[i] : 0u;
+        for (int i = 0; i < NT / 64; ++i) above += (i < wv) ? wtot[i] : 0u;
 #pragma unroll
-        for (int j = BPT - 1; j >= 0; --j) {
-            const int b = tid * BPT + j;
-            if (b < nb && above < k_rem && k_rem <= above + hv[j]) {
+        for (int j = 0; j < BPT; ++j) {
+            const int b = HIST_BINS - 1 - (tid * BPT + j);
+            if (b >= 0 && b < nb && above < k_rem && k_rem <= above + hv[j]) {
                 found[0] = (uint32_t)b;
                 found[1] = above;
                 found[2] = hv[j];
@@ -262,12 +297,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             above += hv[j];
         }
         __syncthreads();
+        // found, wtot and this buffer are next written only after the next pass's first barrier
         const uint32_t fb = found[0], fa = found[1];
         const uint32_t in_bin = found[2];
         prefix = (shift >= 32 ? 0u : (prefix << width)) | fb;
         k_rem -= fa;
         shift = sh_lo;
-        __syncthreads();                             // hist, wtot and found are reused
+        hb ^= NHB - 1;
         if (in_bin == k_rem) break;                  // the whole bin is taken: no ties to cut
         if (STREAM && in_bin <= (uint32_t)CAND_CAP) {   // few keys share the k-th key's bin: rank them
             ranked = true;
@@ -342,7 +378,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (sel[e]) {
-                        if (r < (uint32_t)k) out[r] = out_pos(b0 + 256 * j + e);
+                        if (r < (uint32_t)k) {
+                            out[r] = out_pos(b0 + 256 * j + e);
+                            if (MODE == TOPK_SEGS) okey[r] = key[4 * j + e];
+                        }
                         ++r;
                     }
                 }
@@ -415,7 +454,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 if (sel[e]) {
-                    if (r < (uint32_t)k) out[r] = out_pos(b0 + 256 * j + e);
+                    if (r < (uint32_t)k) {
+                        out[r] = out_pos(b0 + 256 * j + e);
+                        if (MODE == TOPK_SEGS) okey[r] = key[4 * j + e];
+                    }
                     ++r;
                 }
             }
@@ -430,17 +472,17 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
 // segment, or a candidate list) and picks the block shape.
 template <int MODE>
 hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int nseg, const int32_t* cand,
-                       int32_t* out, bool vec, hipStream_t st) {
+                       uint32_t* ckeys, int32_t* out, bool vec, hipStream_t st) {
 #define IC_TOPK_GO(NT, EPT, STREAM)                                                                          \
     do {                                                                                                    \
         if (vec)                                                                                            \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,      \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len);                                                            \
+                               nseg, cand, len, ckeys);                                                     \
         else                                                                                                \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,     \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len);                                                            \
+                               nseg, cand, len, ckeys);                                                     \
         return hipGetLastError();                                                                           \
     } while (0)
     if (len <= 2048) IC_TOPK_GO(256, 8, false);
@@ -461,7 +503,7 @@ int topk_segments(const ic_topk_args& a) {
 
 size_t topk_ws_bytes(const ic_topk_args& a) {
     const int nseg = topk_segments(a);
-    return nseg ? (size_t)a.rows * nseg * a.k * sizeof(int32_t) : 0;
+    return nseg ? 2 * (size_t)a.rows * nseg * a.k * sizeof(int32_t) : 0;   // positions, then keys
 }
 
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
@@ -469,12 +511,13 @@ hipError_t launch_topk(const ic_topk_args& a, hipStream_t st) {
     const bool vec = (a.row_stride % 4 == 0) && (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0);
     const int nseg = topk_segments(a);
     if (nseg && a.cand != nullptr) {
-        // segments of TOPK_SEG keys -> candidate positions [rows][nseg * k], then one select per row
-        hipError_t e = topk_launch<TOPK_SEGS>(a, a.rows * nseg, TOPK_SEG, TOPK_SEG, nseg, nullptr, a.cand,
+        // segments of TOPK_SEG keys -> candidates [rows][nseg * k] (positions, keys), then one select per row
+        const int clen = nseg * a.k;
+        uint32_t* ckeys = reinterpret_cast<uint32_t*>(a.cand + (size_t)a.rows * clen);
+        hipError_t e = topk_launch<TOPK_SEGS>(a, a.rows * nseg, TOPK_SEG, TOPK_SEG, nseg, nullptr, ckeys, a.cand,
                                               vec && TOPK_SEG % 4 == 0, st);
         if (e != hipSuccess) return e;
-        const int clen = nseg * a.k;
-        return topk_launch<TOPK_GATHER>(a, a.rows, clen, 0, 1, a.cand, a.idx, clen % 4 == 0, st);
+        return topk_launch<TOPK_GATHER>(a, a.rows, clen, 0, 1, a.cand, ckeys, a.idx, clen % 4 == 0, st);
     }
-    return topk_launch<TOPK_ROWS>(a, a.rows, a.max_len, 0, 1, nullptr, a.idx, vec, st);
+    return topk_launch<TOPK_ROWS>(a, a.rows, a.max_len, 0, 1, nullptr, nullptr, a.idx, vec, st);
 }

@@ -51,6 +51,14 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Only the calls below are exported from the library (it is built with hidden
+ * default visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define IC_API __attribute__((visibility("default")))
+#else
+#define IC_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -123,7 +131,7 @@ enum {
 
 /* Bytes of workspace the operation needs for this shape (0 if none).
  * Returns 0 and sets ic_last_error() for an invalid shape or op. */
-size_t ic_workspace_size(const ic_shape* shape, int op);
+IC_API size_t ic_workspace_size(const ic_shape* shape, int op);
 
 /* Lightning indexer + top-k of one F layer (arXiv abstract; agent skill page,
  * Step 1 gives the (batch, seq_len, k) shape of the result).
@@ -132,20 +140,20 @@ size_t ic_workspace_size(const ic_shape* shape, int op);
  * positions of each query in ascending order, -1 padded.  The scores are
  * produced in query chunks of shape.chunk rows inside `ws`; no L x L buffer
  * is ever formed. */
-ic_status ic_indexer_topk(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+IC_API ic_status ic_indexer_topk(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
                           int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* The raw fp32 indexer scores of one F layer, for verification and
  * measurement: scores [B, Lq, row_stride], row t holding keys 0..pos0+t
  * (entries beyond are not written).  row_stride >= pos0 + Lq.  No workspace. */
-ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+IC_API ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
                             float* scores, int64_t row_stride, void* stream);
 
 /* Top-k of caller-supplied score rows with the same rule as ic_indexer_topk:
  * scores [rows, row_stride] fp32, row r has n_r = first_len + r visible
  * entries (first_len >= 1, n_r <= row_stride); writes idx [rows, k] int32.
  * Used to test the selection on chosen inputs (ties, -0.0, k >= n). */
-ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len,
+IC_API ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len,
                        int32_t k, int32_t* idx, void* stream);
 
 /* Top-k of score rows with per-row lengths (the decode shape: one row per
@@ -157,17 +165,17 @@ ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, in
  * segments' candidates, which needs ic_topk_rows_seq_ws() bytes of `ws`;
  * with ws NULL such rows take the one-workgroup streaming path instead (same
  * result). */
-ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32_t rows, const int32_t* seq_len,
+IC_API ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32_t rows, const int32_t* seq_len,
                            int32_t max_len, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace bytes ic_topk_rows_seq can use for these sizes (0 if none). */
-size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k);
+IC_API size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k);
 
 /* Sparse attention of one layer (arXiv abstract: core attention over the k
  * selected tokens): out [B, Lq, H, d] bf16 from q, kv and idx [B, Lq, k]
  * (entries < 0 are skipped; every row must hold at least one entry >= 0 and
  * every entry must be < Lk).  Softmax scale 1/sqrt(d), fp32 accumulation. */
-ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx,
+IC_API ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx,
                          void* out, void* ws, size_t ws_bytes, void* stream);
 
 /* Prefill through an F/S layer stack (agent skill page, Step 3; blog, "The
@@ -179,7 +187,7 @@ ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, c
  * S fails with IC_ERR_NO_CACHED_INDICES before any launch.
  * idx_cache: [B, Lq, k] int32, caller-owned, holds the last F layer's
  * indices on return.  stats (may be NULL) receives the counters. */
-ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
+IC_API ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
                        const ic_shape* shape, int32_t* idx_cache, void* ws, size_t ws_bytes,
                        ic_stats* stats, void* stream);
 
@@ -189,18 +197,18 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
  * has already written at row seq_len[b]-1; the new query sits at that
  * position and sees keys 0..seq_len[b]-1 (1 <= seq_len[b] <= Lk).
  * idx_cache [B, 1, k].  Same pattern and cache rules as ic_run_stack. */
-ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* layers,
+IC_API ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* layers,
                          const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
                          void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
 
 /* Counters of the last stack call on this thread. */
-ic_status ic_get_stats(ic_stats* out);
+IC_API ic_status ic_get_stats(ic_stats* out);
 
 /* Description of the last failure on this thread ("" if none). */
-const char* ic_last_error(void);
+IC_API const char* ic_last_error(void);
 
 /* Library version: major*10000 + minor*100 + patch. */
-int32_t ic_version(void);
+IC_API int32_t ic_version(void);
 
 #ifdef __cplusplus
 }
