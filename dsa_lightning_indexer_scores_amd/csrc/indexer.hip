@@ -380,31 +380,39 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 // ---------------------------------------------------------------------------
 // Decode: one query per sequence; workgroup = (key range, sequence).  Keys
-// stream straight from HBM into B fragments (no reuse to stage in LDS).
+// stream straight from HBM into B fragments (no reuse to stage in LDS).  A wave
+// sweeps DEC_CHUNKS chunks of DEC_TILES 16-key tiles and loads the next chunk
+// while it scores the current one, so its q_I slab is loaded once per 256 keys.
 // ---------------------------------------------------------------------------
-constexpr int DEC_TILES_PER_WAVE = 8;                        // 128 keys per wave
+constexpr int DEC_TILES = 4;                                 // 16-key tiles per chunk
+constexpr int DEC_CHUNKS = 4;                                // chunks per wave
 constexpr int DEC_NW = 4;
-constexpr int DEC_KEYS_PER_WG = DEC_NW * DEC_TILES_PER_WAVE * 16;
+constexpr int DEC_KEYS_PER_WAVE = DEC_CHUNKS * DEC_TILES * 16;
+constexpr int DEC_KEYS_PER_WG = DEC_NW * DEC_KEYS_PER_WAVE;
 
 template <bool FP8, int D_I, int HT>
-__global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
+__global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8 ? 3 : 2, FP8 ? 3 : 2))) void indexer_decode_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
     const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I) {
     using G = IdxGeom<FP8, D_I>;
     const int b = blockIdx.y;
     const int n = max(1, min(seq_len[b], Lk));                // visible keys (clamped to the cache)
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int key0 = blockIdx.x * DEC_KEYS_PER_WG + wv * DEC_TILES_PER_WAVE * 16;
+    const int key0 = blockIdx.x * DEC_KEYS_PER_WG + wv * DEC_KEYS_PER_WAVE;
     if (key0 >= n) return;
 
     const uint8_t* kbase = kI + (int64_t)b * Lk * G::ROWB;
-    Frag<FP8, D_I> Bf[DEC_TILES_PER_WAVE];
+    Frag<FP8, D_I> Bf[2][DEC_TILES];
+    auto load_chunk = [&](Frag<FP8, D_I> (&B)[DEC_TILES], int c) {
 #pragma unroll
-    for (int i = 0; i < DEC_TILES_PER_WAVE; ++i) {
-        const int s = key0 + 16 * i + r;
-        load_frag<FP8, D_I>(Bf[i], s < n ? kbase + (int64_t)s * G::ROWB : nullptr, g);
-    }
+        for (int i = 0; i < DEC_TILES; ++i) {
+            // keys past the last visible one re-read it: their scores are never stored
+            const int s = min(key0 + (c * DEC_TILES + i) * 16 + r, n - 1);
+            load_frag_lds<FP8, D_I>(B[i], kbase + (int64_t)s * G::ROWB, g);
+        }
+    };
+    load_chunk(Bf[0], 0);
     Frag<FP8, D_I> A[HT];
     float wr[HT][4];
 #pragma unroll
@@ -413,20 +421,26 @@ __global__ __launch_bounds__(DEC_NW * 64) void indexer_decode_kernel(
         load_frag<FP8, D_I>(A[ht], h < H_I ? qI + ((int64_t)b * H_I + h) * G::ROWB : nullptr, g);
     }
     load_w<HT>(wr, w + (int64_t)b * H_I, H_I, g);
-    float val[DEC_TILES_PER_WAVE];
-#pragma unroll
-    for (int i = 0; i < DEC_TILES_PER_WAVE; ++i) {
-        f32x4 acc[HT];
-#pragma unroll
-        for (int ht = 0; ht < HT; ++ht) acc[ht] = tile_mma<FP8, D_I>(A[ht], Bf[i]);
-        val[i] = head_partial<HT>(acc, wr);
-    }
     float* srow = scores + (int64_t)b * score_stride;
 #pragma unroll
-    for (int grp = 0; grp < DEC_TILES_PER_WAVE / 4; ++grp) {
-        const int s = key0 + 64 * grp + 16 * g + r;
-        const float v = rowsum_scatter4(val[4 * grp], val[4 * grp + 1], val[4 * grp + 2], val[4 * grp + 3]);
-        if (s < n) srow[s] = v;
+    for (int c = 0; c < DEC_CHUNKS; ++c) {
+        const int kc = key0 + c * DEC_TILES * 16;
+        if (kc >= n) break;
+        if (c + 1 < DEC_CHUNKS) load_chunk(Bf[(c + 1) & 1], c + 1);
+        float val[DEC_TILES];
+#pragma unroll
+        for (int i = 0; i < DEC_TILES; ++i) {
+            f32x4 acc[HT];
+#pragma unroll
+            for (int ht = 0; ht < HT; ++ht) acc[ht] = tile_mma<FP8, D_I>(A[ht], Bf[c & 1][i]);
+            val[i] = head_partial<HT>(acc, wr);
+        }
+#pragma unroll
+        for (int grp = 0; grp < DEC_TILES / 4; ++grp) {
+            const int s = kc + 64 * grp + 16 * g + r;
+            const float v = rowsum_scatter4(val[4 * grp], val[4 * grp + 1], val[4 * grp + 2], val[4 * grp + 3]);
+            if (s < n) srow[s] = v;
+        }
     }
 }
 
