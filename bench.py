@@ -11,7 +11,8 @@ After the timed prefill steps the same run measures, outside the timed loop:
             'FSSS'x6, 64 decode steps (one new token per sequence per step);
   kernels   each kernel of the path timed alone with HIP events on the stream
             it runs on, priced against its roofline (MFMA for the indexer, HBM
-            for top-k and gather attention);
+            for top-k and gather attention), plus the fp8 MFMA rate this GPU
+            sustains on constant and on random operands (libicprobe.so);
   all-F     the same stack with every layer running its indexer (the
             comparison the pages' prefill speedups are quoted against);
   oracle    the CPU oracle on a bounded sample of tokens (cpu_baseline).
@@ -161,6 +162,21 @@ def kernel_rooflines(cfg, layers, ws):
     out["indexer"] = {"bound": "mfma", "achieved": round(tf, 1), "peak": PEAK_TFLOPS[cfg.idx_dtype],
                       "unit": "TFLOP/s", "frac": round(tf / PEAK_TFLOPS[cfg.idx_dtype], 4), "ms": round(ms, 4),
                       "work": f"{flops:.4g} flop = 2*H_I*d_I per causal pair x {pairs} pairs"}
+    # the same layer in the 4096-query tiles the stack launches (8 launches)
+    ch = cfg.chunk
+    tile = torch.empty(ch * L, dtype=torch.float32, device="cuda")
+
+    def chunked():
+        for c0 in range(0, L, ch):
+            n = min(ch, L - c0)
+            rs = (c0 + n + 3) // 4 * 4
+            ic.indexer_scores(f["q_I"][:, c0:c0 + n], f["w"][:, c0:c0 + n], f["k_I"], pos0=c0,
+                              scores=tile[:n * rs].view(1, n, rs), row_stride=rs)
+    chunked()
+    ms_c = timed_events(chunked, 3)
+    out["indexer"]["chunked_ms"] = round(ms_c, 4)
+    out["indexer"]["chunked_frac"] = round(flops / (ms_c * 1e-3) / 1e12 / PEAK_TFLOPS[cfg.idx_dtype], 4)
+    del tile
     # a2: top-k over those rows (one launch, 32768 rows)
     sc2 = scores[0]
     idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
@@ -184,6 +200,33 @@ def kernel_rooflines(cfg, layers, ws):
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
                         "work": f"{by:.4g} B = 512 B per selected [K|V] row x {rows} rows + q, out, idx"}
     return out
+
+
+def mfma_ceiling():
+    """Sustained fp8 MFMA rate of this GPU, as fractions of the 5.0 PFLOP/s peak: a
+    stream of independent 16x16x128 fp8 MFMAs (libicprobe.so) over constant operands,
+    and over random operands that change every iteration as the indexer's keys do."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "libicprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.icp_mfma_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    blocks, iters = 8192, 2048
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    res = {}
+    for name, rnd in (("constant_operands", 0), ("random_operands", 1)):
+        def launch():
+            r = lib.icp_mfma_stream(rnd, blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+            if r != 0:
+                raise RuntimeError(f"icp_mfma_stream failed: hipError {r}")
+        launch()
+        ms = timed_events(launch, 3)
+        flops = 8.0 * 65536 * iters * blocks * 4
+        res[name] = round(flops / (ms * 1e-3) / 1e12 / PEAK_TFLOPS["fp8"], 4)
+    return res
 
 
 def cpu_baseline(cfg, layers, n_tokens: int, seed: int = 7):
@@ -372,6 +415,10 @@ def main():
         result["kernels"] = kr
         result["kernel_ms_in_stack"] = {k: round(v, 3) for k, v in share.items()}
         result["indexer_mfma_frac"] = kr["indexer"]["frac"]
+        ceil = mfma_ceiling()
+        if ceil:
+            result["mfma_sustained_frac"] = ceil
+            result["indexer_frac_of_sustained"] = round(kr["indexer"]["frac"] / ceil["random_operands"], 4)
 
     if not args.no_allf:
         log("timing the all-F stack")

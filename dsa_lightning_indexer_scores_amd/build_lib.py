@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libindexcache.so")
 SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "api.cpp"]
+# Measurement support for the benchmark (sustained MFMA rate); not linked into LIB.
+PROBE_LIB = os.path.join(PKG, "libicprobe.so")
+PROBE_SOURCES = ["mfma_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -40,19 +43,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    if not os.path.exists(HIPCC):
-        raise RuntimeError(f"hipcc not found at {HIPCC}")
-    os.makedirs(OUT_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str):
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
            "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    if not os.path.exists(HIPCC):
+        raise RuntimeError(f"hipcc not found at {HIPCC}")
+    os.makedirs(OUT_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(lambda s: _compile(s, verbose), srcs)))
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 

@@ -124,3 +124,12 @@ def test_topk_rows_seq_workspace_sizes():
     assert ic.topk_rows_seq_ws(3, 40000, 100) == 2 * 3 * 5 * 100 * 4
     # a candidate list longer than one register-resident block falls back to streaming
     assert ic.topk_rows_seq_ws(8, 200000, 2048) == 0
+
+
+def test_mfma_probe_library_exports_its_entry():
+    path = os.path.join(os.path.dirname(ic.LIB_PATH), "libicprobe.so")
+    assert os.path.exists(path), "libicprobe.so missing: run the build first"
+    P = ctypes.CDLL(path)
+    assert hasattr(P, "icp_mfma_stream")
+    P.icp_mfma_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert P.icp_mfma_stream(1, 0, 1, None, None) != 0   # rejected before any launch
