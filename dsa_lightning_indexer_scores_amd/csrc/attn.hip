@@ -8,13 +8,20 @@
 //
 // One wave owns one (query, group of 16 heads[, key split]).  Per step of 32
 // selected rows:
-//   S^T (32 keys x 16 heads) = K Q^T : K fragments are gathered straight
-//       from HBM (16 contiguous bytes per lane, 64 bytes per row per load);
+//   prefill: the rows' [K | V] are gathered with fully coalesced 16-byte loads
+//       (a row is 512 contiguous bytes, so one load instruction covers two whole
+//       rows and every 4-lane quad reads one 64-byte run) into the wave's LDS
+//       tile, and K fragments are read back from there.  Gathering K straight
+//       into fragments (lanes 0-15 on 16 different rows) makes each quad touch
+//       four rows; with every CU busy, the vector-memory address unit then bounds
+//       the kernel (measured 95% busy);
+//   split-K decode, latency-bound with one or two steps per wave, gathers K
+//       straight into fragments and stages only V (one LDS round trip fewer);
+//   S^T (32 keys x 16 heads) = K Q^T;
 //   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
 //       lane % 16) is also the layout of O^T below, so the running max and
 //       rescale never leave the lane;
-//   O^T (d x 16 heads) += V^T P^T : V rows are gathered with coalesced
-//       16-byte loads into the wave's LDS tile and read back transposed with
+//   O^T (d x 16 heads) += V^T P^T : V read back transposed with
 //       ds_read_b64_tr_b16; P^T is the S^T accumulator packed to bf16 (its
 //       k order matches the transposed read, so no shuffle is needed).
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
@@ -31,14 +38,24 @@ namespace {
 constexpr int ATT_NW = 4;
 constexpr int KT = 32;                  // selected rows per step
 
-template <int D>
+template <int D, bool ROWS>
 struct AttGeom {
     static constexpr int NDC = D / 32;  // K=32 chunks of the QK^T contraction
     static constexpr int NDT = D / 16;  // 16-wide d tiles of the output
-    static constexpr int VSTR = 2 * D + 16;   // LDS bytes per V row (padded)
-    static constexpr int VPIECES = KT * D * 2 / 16;  // 16-byte pieces per V tile
-    static constexpr int VPL = VPIECES / 64;          // per lane
-    static constexpr int PPR = D * 2 / 16;            // pieces per V row
+    static constexpr int RB = 4 * D;    // bytes per KV row: K[d] then V[d], bf16
+    // ROWS: whole rows staged in LDS
+    static constexpr int RSTR = RB + 16;   // LDS bytes per staged row (16-byte skew)
+    static constexpr int PPR = RB / 16;    // 16-byte pieces per row
+    static constexpr int RPI = 64 / PPR;   // rows per load instruction
+    static constexpr int NI = KT / RPI;    // load instructions per step
+    static_assert(PPR <= 64 && 64 % PPR == 0, "a load instruction covers whole rows");
+    // !ROWS: K gathered into fragments, V rows staged in LDS
+    static constexpr int VSTR = 2 * D + 16;           // LDS bytes per V row (padded)
+    static constexpr int VPPR = D * 2 / 16;           // 16-byte pieces per V row
+    static constexpr int VPL = KT * VPPR / 64;        // V pieces per lane
+    // staged row stride and where V starts in a staged row
+    static constexpr int STR = ROWS ? RSTR : VSTR;
+    static constexpr int VOFF = ROWS ? 2 * D : 0;
 };
 
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
@@ -50,8 +67,11 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
     int H, int k, int nsplit, float scale_log2) {
-    using G = AttGeom<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t vlds_all[ATT_NW][KT * G::VSTR];
+    constexpr bool ROWS = !SPLIT;
+    using G = AttGeom<D, ROWS>;
+    static_assert(!SPLIT || ATT_NW * 16 * D * 4 + ATT_NW * 16 * 8 <= ATT_NW * KT * G::STR,
+                  "the LDS merge reuses the row tiles");
+    __shared__ __attribute__((aligned(16))) uint8_t vlds_all[ATT_NW][KT * G::STR];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: keeps addressing scalar
     const int n = lane & 15, g = lane >> 4;
@@ -94,50 +114,81 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     // computed (two register sets, A and B), and the idx entries of step t+2 are
     // fetched one step earlier still, so gathers overlap compute.
     struct Tile {
-        i32x4 kf[2][G::NDC];                                 // K fragments: keys 16*kt + m
-        i32x4 vst[G::VPL];                                   // V rows, staged for LDS
+        i32x4 raw[ROWS ? G::NI : 1];                         // ROWS: whole rows, as loaded
+        i32x4 kf[ROWS ? 1 : 2][G::NDC];                      // !ROWS: K fragments, keys 16*kt + m
+        i32x4 vst[ROWS ? 1 : G::VPL];                        // !ROWS: V rows, staged for LDS
         uint32_t valid;                                      // bit e: entry e of the step is a row
     };
     auto load_idx = [&](int j0) -> int {
         const int jl = j0 + (lane & 31);
-        int v = (jl < j_end) ? irow[jl] : -1;
+        int v = (jl < j_end && lane < 32) ? irow[jl] : -1;
         return (v >= Lk) ? -1 : v;                           // never read past the KV rows
     };
     auto issue = [&](Tile& T, int my_idx) {
         T.valid = (uint32_t)__ballot(my_idx >= 0);
         if (T.valid == 0u) return;
         const int safe_idx = my_idx >= 0 ? my_idx : 0;
+        if constexpr (ROWS) {
+            const int piece = (lane % G::PPR) * 16;
 #pragma unroll
-        for (int i = 0; i < G::VPL; ++i) {                   // V piece c -> row c / PPR, byte (c % PPR) * 16
-            const int c = lane + 64 * i;
-            const int row = __shfl(safe_idx, c / G::PPR);
-            const uint32_t off = (uint32_t)row * (4 * D) + 2 * D + (c % G::PPR) * 16;
-            T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
-        }
+            for (int i = 0; i < G::NI; ++i) {                // rows RPI*i + lane / PPR
+                int row = __builtin_amdgcn_readlane(safe_idx, G::RPI * i);
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {                     // lane (m, g): key 16*kt + m, d = 32*dc + 8g
-            const int row = __shfl(safe_idx, 16 * kt + n);
-            const uint32_t off = (uint32_t)row * (4 * D) + 16 * g;
+                for (int r = 1; r < G::RPI; ++r) {
+                    const int other = __builtin_amdgcn_readlane(safe_idx, G::RPI * i + r);
+                    row = (lane / G::PPR == r) ? other : row;
+                }
+                T.raw[i] = *reinterpret_cast<const i32x4*>(kvb + (uint32_t)row * G::RB + piece);
+            }
+        } else {
 #pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc)
-                T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
+            for (int i = 0; i < G::VPL; ++i) {               // V piece c -> row c / VPPR, byte (c % VPPR) * 16
+                const int c = lane + 64 * i;
+                const int row = __shfl(safe_idx, c / G::VPPR);
+                const uint32_t off = (uint32_t)row * G::RB + 2 * D + (c % G::VPPR) * 16;
+                T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {                 // lane (m, g): key 16*kt + m, d = 32*dc + 8g
+                const int row = __shfl(safe_idx, 16 * kt + n);
+                const uint32_t off = (uint32_t)row * G::RB + 16 * g;
+#pragma unroll
+                for (int dc = 0; dc < G::NDC; ++dc)
+                    T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
+            }
         }
     };
     auto compute = [&](const Tile& T) {
         if (T.valid == 0u) return;                           // a step of -1 entries contributes nothing
         const uint32_t valid = T.valid;
+        if constexpr (ROWS) {
 #pragma unroll
-        for (int i = 0; i < G::VPL; ++i) {
-            const int c = lane + 64 * i;
-            *reinterpret_cast<i32x4*>(vlds + (c / G::PPR) * G::VSTR + (c % G::PPR) * 16) = T.vst[i];
+            for (int i = 0; i < G::NI; ++i)
+                *reinterpret_cast<i32x4*>(vlds + (G::RPI * i + lane / G::PPR) * G::RSTR + (lane % G::PPR) * 16) =
+                    T.raw[i];
+            lds_wave_sync();
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::VPL; ++i) {
+                const int c = lane + 64 * i;
+                *reinterpret_cast<i32x4*>(vlds + (c / G::VPPR) * G::VSTR + (c % G::VPPR) * 16) = T.vst[i];
+            }
         }
-        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e.
+        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e.  K fragment: key 16*kt + n,
+        // d = 32*dc + 8g .. +7.
         f32x4 s[2];
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) acc = mfma_bf16_k32(T.kf[kt][dc], qf[dc], acc);
+            for (int dc = 0; dc < G::NDC; ++dc) {
+                i32x4 kf;
+                if constexpr (ROWS)
+                    kf = *reinterpret_cast<const i32x4*>(vlds + (16 * kt + n) * G::RSTR + 64 * dc + 16 * g);
+                else
+                    kf = T.kf[kt][dc];
+                acc = mfma_bf16_k32(kf, qf[dc], acc);
+            }
             s[kt] = acc;
         }
         float x[8];
@@ -172,12 +223,12 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         pf[2] = (int)pack_bf16x2(x[4], x[5]);
         pf[3] = (int)pack_bf16x2(x[6], x[7]);
 
-        lds_wave_sync();
         // O^T += V^T P^T.  Transposed LDS reads: within each 16-lane row g, lane src
         // points at V[4g + src/4 (+16)][16dt + 4*(src%4)], and receives V[keys][d = 16dt + src].
         const int src = n;
-        const uint8_t* vr0 = vlds + (4 * g + (src >> 2)) * G::VSTR + (4 * (src & 3)) * 2;
-        const uint8_t* vr1 = vr0 + 16 * G::VSTR;
+        if constexpr (!ROWS) lds_wave_sync();
+        const uint8_t* vr0 = vlds + (4 * g + (src >> 2)) * G::STR + G::VOFF + (4 * (src & 3)) * 2;
+        const uint8_t* vr1 = vr0 + 16 * G::STR;
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) {
             const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr0 + 32 * dt));
