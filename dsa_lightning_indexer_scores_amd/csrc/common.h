@@ -116,7 +116,7 @@ struct ic_topk_args {
 };
 // Few long rows (decode) are ranked in TOPK_SEG-key segments first, then over the
 // segments' candidates; that needs topk_ws_bytes() of workspace (0 otherwise).
-constexpr int TOPK_SEG = 8192;
+constexpr int TOPK_SEG = 16384;                 // keys per segment (one register-resident block)
 constexpr int TOPK_SEG_MAX_ROWS = 1024;
 int topk_segments(const ic_topk_args& a);
 size_t topk_ws_bytes(const ic_topk_args& a);

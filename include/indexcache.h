@@ -161,7 +161,7 @@ IC_API ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t r
  * row r has n_r = seq_len[r] visible entries, seq_len a DEVICE int32 [rows]
  * whose values are clamped to 1..max_len (max_len <= row_stride, host-known
  * bound); writes idx [rows, k] int32.  When rows are long (max_len > 32768)
- * and few (rows <= 1024), each 8192-key segment is ranked first and then the
+ * and few (rows <= 1024), each 16384-key segment is ranked first and then the
  * segments' candidates, which needs ic_topk_rows_seq_ws() bytes of `ws`;
  * with ws NULL such rows take the one-workgroup streaming path instead (same
  * result). */

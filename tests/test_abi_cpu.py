@@ -117,13 +117,14 @@ def test_topk_rows_seq_validation(L):
 
 def test_topk_rows_seq_workspace_sizes():
     # short rows, or many rows, need none; few long rows keep k candidates (position and
-    # key) per 8192-key segment
+    # key) per 16384-key segment
     assert ic.topk_rows_seq_ws(32, 32768, 2048) == 0
     assert ic.topk_rows_seq_ws(4096, 65600, 2048) == 0
-    assert ic.topk_rows_seq_ws(32, 65600, 2048) == 2 * 32 * 9 * 2048 * 4
-    assert ic.topk_rows_seq_ws(3, 40000, 100) == 2 * 3 * 5 * 100 * 4
+    assert ic.topk_rows_seq_ws(32, 65600, 2048) == 2 * 32 * 5 * 2048 * 4
+    assert ic.topk_rows_seq_ws(3, 40000, 100) == 2 * 3 * 3 * 100 * 4
+    assert ic.topk_rows_seq_ws(8, 200000, 2048) == 2 * 8 * 13 * 2048 * 4
     # a candidate list longer than one register-resident block falls back to streaming
-    assert ic.topk_rows_seq_ws(8, 200000, 2048) == 0
+    assert ic.topk_rows_seq_ws(8, 300000, 2048) == 0
 
 
 def test_mfma_probe_library_exports_its_entry():
