@@ -229,6 +229,30 @@ def mfma_ceiling():
     return res
 
 
+def stream_read_gbs(nbytes: int = 1 << 30) -> float:
+    """HBM read bandwidth of a plain streaming kernel over a 1 GiB buffer (libicprobe.so)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "libicprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.icp_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    blocks = 4096
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def launch():
+        r = lib.icp_stream_read(ctypes.c_void_p(buf.data_ptr()), nbytes, blocks, ctypes.c_void_p(out.data_ptr()),
+                                ctypes.c_void_p(st.cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"icp_stream_read failed: hipError {r}")
+    launch()
+    ms = timed_events(launch, 5)
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def cpu_baseline(cfg, layers, n_tokens: int, seed: int = 7):
     """Time the oracle on n_tokens query positions drawn uniformly from the sequence,
     each taken through every layer of the stack (F: indexer + top-k + attention; S: attention)."""
@@ -344,10 +368,43 @@ def bench_decode(n_steps: int, warm: int = 2):
         ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - eager_t0) * 1e3 / min(n_steps, 8)
-    return {"tokens_per_s": round(cfg.B * n_steps / dt, 1), "ms_per_step": round(dt * 1e3 / n_steps, 4),
-            "eager_ms_per_step": round(eager_ms, 4), "steps": n_steps,
-            "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, fp8 indexer, H=16, "
-                        "d=128; one captured graph replayed per step"}
+    res = {"tokens_per_s": round(cfg.B * n_steps / dt, 1), "ms_per_step": round(dt * 1e3 / n_steps, 4),
+           "eager_ms_per_step": round(eager_ms, 4), "steps": n_steps,
+           "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, fp8 indexer, H=16, "
+                       "d=128; one captured graph replayed per step"}
+    res["kernels"] = decode_kernel_rooflines(cfg, layers, seq_len, idx_cache, ws, int(seq_len[0].item()))
+    return res
+
+
+def decode_kernel_rooflines(cfg, layers, seq_len, idx_cache, ws, n: int):
+    """Decode is the honest HBM test (its caches do not fit on chip).  The kernels have no
+    separate entry points, so they are timed by difference of single ABI calls on the same
+    caches (HIP events): one F layer ('F': indexer + top-k + attention), one F layer and
+    three S layers ('FSSS': + 3 attentions), and the top-k alone on scores of that shape."""
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    B, k = cfg.B, cfg.k
+    outs = [torch.empty_like(l["q"]) for l in layers[:4]]
+    one = lambda pat, lay: ic.decode_step(pat, lay, seq_len, k, outs=outs[:len(lay)], idx_cache=idx_cache, ws=ws)
+    t_f = timed_events(lambda: one("F", layers[:1]), 10)
+    t_fsss = timed_events(lambda: one("FSSS", layers[:4]), 10)
+    sc = torch.randn((B, cfg.L + cfg.decode_steps), device="cuda") * 20 + 145
+    sl = seq_len.clone()
+    ws_t = torch.empty(max(ic.topk_rows_seq_ws(B, sc.shape[1], k), 256), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    t_topk = timed_events(lambda: ic.topk_rows_seq(sc, sl, k, idx=idx, ws=ws_t), 10)
+    t_attn = (t_fsss - t_f) / 3
+    t_idx = t_f - t_attn - t_topk
+    by_idx = B * n * cfg.d_I * 1.0 + B * n * 4.0               # k_I rows read + scores written
+    by_topk = B * n * 4.0 + B * k * 4.0                       # scores read + idx written
+    by_attn = B * k * 512.0 + B * (cfg.H * cfg.d * 2 * 2 + 4 * k)   # selected rows + q, out, idx
+    mk = lambda ms, by, what: {"bound": "hbm", "ms": round(ms, 5), "achieved": round(by / (ms * 1e-3) / 1e9, 1),
+                               "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                               "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "work": what}
+    return {"indexer": mk(t_idx, by_idx, f"{by_idx:.4g} B = 128 B k_I + 4 B score per (sequence, visible key)"),
+            "topk": mk(t_topk, by_topk, f"{by_topk:.4g} B = 4 B per visible score + 4k B idx per sequence"),
+            "attention": mk(t_attn, by_attn, f"{by_attn:.4g} B = 512 B per selected row + q, out, idx"),
+            "method": "by difference: F-layer step minus attention (from FSSS) minus top-k alone"}
 
 
 def main():
@@ -419,6 +476,11 @@ def main():
         if ceil:
             result["mfma_sustained_frac"] = ceil
             result["indexer_frac_of_sustained"] = round(kr["indexer"]["frac"] / ceil["random_operands"], 4)
+        sgbs = stream_read_gbs()
+        if sgbs:
+            result["hbm_stream_read_gbs"] = sgbs
+            for name in ("topk", "attention"):
+                kr[name]["frac_of_stream"] = round(kr[name]["achieved"] / sgbs, 4)
 
     if not args.no_allf:
         log("timing the all-F stack")
@@ -438,6 +500,11 @@ def main():
         del outs
         result["decode"] = bench_decode(args.decode_steps)
         result["decode_tokens_per_s"] = result["decode"]["tokens_per_s"]
+        sgbs = result.get("hbm_stream_read_gbs")
+        if sgbs:
+            for v in result["decode"]["kernels"].values():
+                if isinstance(v, dict):
+                    v["frac_of_stream"] = round(v["achieved"] / sgbs, 4)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

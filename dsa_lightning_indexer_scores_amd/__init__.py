@@ -80,13 +80,15 @@ def lib() -> ctypes.CDLL:
     L.ic_topk_rows_seq.argtypes = [vp, i64, i32, vp, i32, i32, vp, vp, sz, vp]
     L.ic_topk_rows_seq_ws.argtypes = [i32, i32, i32]
     L.ic_topk_rows_seq_ws.restype = sz
+    L.ic_index_overlap.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp, vp]
     L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
-    for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_sparse_attn", "ic_run_stack",
+    for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
+               "ic_sparse_attn", "ic_run_stack",
                "ic_decode_step", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -221,6 +223,28 @@ def topk_rows_seq(scores, seq_len, k: int, max_len: Optional[int] = None, idx=No
     _check(lib().ic_topk_rows_seq(_ptr(scores), stride, rows, _ptr(seq_len), max_len, k, _ptr(idx), _ptr(ws),
                                   0 if ws is None else ws.numel(), _stream(stream)))
     return idx
+
+
+def index_overlap(idx_a, idx_b, stream=None):
+    """Per-row overlap of two index caches [..., k] int32 (rows ascending, -1 padded).
+    Returns (inter int32 [...], jaccard fp32 [...], recall fp32 [...], means fp32 [2] =
+    (mean Jaccard, mean recall)), all on the GPU."""
+    for t, name in ((idx_a, "idx_a"), (idx_b, "idx_b")):
+        if not isinstance(t, torch.Tensor) or t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+            raise TypeError(f"{name} must be a contiguous int32 GPU tensor")
+    if idx_a.shape != idx_b.shape:
+        raise ValueError(f"idx_a {tuple(idx_a.shape)} and idx_b {tuple(idx_b.shape)} differ")
+    k = idx_a.shape[-1]
+    lead = idx_a.shape[:-1]
+    rows = idx_a.numel() // k
+    dev = idx_a.device
+    inter = torch.empty(lead, dtype=torch.int32, device=dev)
+    jac = torch.empty(lead, dtype=torch.float32, device=dev)
+    rec = torch.empty(lead, dtype=torch.float32, device=dev)
+    means = torch.empty(2, dtype=torch.float32, device=dev)
+    _check(lib().ic_index_overlap(_ptr(idx_a), _ptr(idx_b), rows, k, _ptr(inter), _ptr(jac), _ptr(rec), _ptr(means),
+                                  _stream(stream)))
+    return inter, jac, rec, means
 
 
 def _attn_shape(q, kv, k, pos0=0) -> Shape:

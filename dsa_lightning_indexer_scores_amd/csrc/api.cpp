@@ -13,6 +13,7 @@
 #include <algorithm>
 #include <cstdarg>
 #include <cstdio>
+#include <climits>
 #include <cstring>
 #include <string>
 
@@ -432,6 +433,17 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
     }
     g_stats = cnt;
     if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows, int32_t k, int32_t* inter,
+                           float* jaccard, float* recall, float* means, void* stream) {
+    if (!idx_a || !idx_b) return fail(IC_ERR_ARG, "idx_a and idx_b must be non-NULL");
+    if (rows < 0 || rows > INT32_MAX || k < 1 || k > kMaxK)
+        return fail(IC_ERR_SHAPE, "need 0 <= rows <= 2^31-1 and 1 <= k <= %d", kMaxK);
+    if (means && (!jaccard || !recall)) return fail(IC_ERR_ARG, "means needs jaccard and recall");
+    hipError_t e = launch_overlap(idx_a, idx_b, rows, k, inter, jaccard, recall, means, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "overlap launch");
     return IC_OK;
 }
 

@@ -136,4 +136,8 @@ struct ic_attn_args {
     float* ws;
 };
 hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st);
+
+// Per-row overlap of two index caches [rows, k] (rows ascending, -1 padded); means may be NULL.
+hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int64_t rows, int k, int32_t* inter, float* jac,
+                          float* rec, float* means, hipStream_t st);
 size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit);

@@ -1,5 +1,6 @@
-// Sustained fp8 MFMA throughput of this GPU, measured so that the indexer's MFMA
-// fraction can be read against what the matrix cores actually sustain.
+// Sustained rates of this GPU, measured so that the kernels' roofline fractions can
+// be read against what the hardware actually sustains: fp8 MFMA throughput, and the
+// HBM read bandwidth of a plain streaming kernel.
 //
 // Each wave runs a stream of independent v_mfma_f32_16x16x128_f8f6f4 over 8 A
 // slabs and 2 B slabs (the shape of an indexer tile loop).  With random=0 the
@@ -62,7 +63,32 @@ __global__ __launch_bounds__(256) void mfma_stream_kernel(float* __restrict__ ou
     out[t] = s;                                      // keeps the stream live
 }
 
+// Grid-stride 16-byte reads of n16 vectors; one word per thread keeps the loads live.
+__global__ __launch_bounds__(256) void stream_read_kernel(const int4* __restrict__ p, size_t n16, int* __restrict__ out) {
+    size_t i = (size_t)blockIdx.x * 1024 + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * 1024;
+    int acc = 0;
+    for (; i < n16; i += stride) {
+        int4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = (i + 256 * u < n16) ? p[i + 256 * u] : make_int4(0, 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
 }  // namespace
+
+// Reads `bytes` (a multiple of 16) from `src` with `blocks` workgroups of 256 threads;
+// out needs blocks * 256 ints.  Returns a hipError_t.
+extern "C" __attribute__((visibility("default"))) int icp_stream_read(const void* src, size_t bytes, int blocks,
+                                                                     int* out, void* stream) {
+    if (src == nullptr || out == nullptr || blocks < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_read_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       static_cast<const int4*>(src), bytes / 16, out);
+    return (int)hipGetLastError();
+}
 
 // Launches `blocks` workgroups of 4 waves, each wave issuing 8 * iters fp8 MFMAs of
 // 16x16x128 (65536 flop each); out needs blocks * 256 floats.  Returns a hipError_t.

@@ -236,6 +236,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     uint32_t prefix = shift >= 32 ? 0u : (kmax >> shift);
     uint32_t k_rem = (uint32_t)k;                    // still to take among the candidates
     bool ranked = false;                             // threshold bin resolved by ranking its keys
+    bool whole = false;                              // the k-th key's bin is taken whole
     int hb = 0;                                      // histogram buffer of this pass
     while (shift > 0) {
         const int width = min(HIST_BITS, shift);
@@ -304,7 +305,10 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         k_rem -= fa;
         shift = sh_lo;
         hb ^= NHB - 1;
-        if (in_bin == k_rem) break;                  // the whole bin is taken: no ties to cut
+        if (in_bin == k_rem) {                       // the whole bin is taken: no ties to cut
+            whole = true;
+            break;
+        }
         if (STREAM && in_bin <= (uint32_t)CAND_CAP) {   // few keys share the k-th key's bin: rank them
             ranked = true;
             break;
@@ -392,7 +396,8 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         return;
     }
 
-    // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them.
+    // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them
+    // (all of them when the bin is taken whole, which skips the equal-key count scan).
     // Empty candidate slots (key 0) sit anywhere in a candidate list, so they never count as
     // equal (key 0 is never above the prefix either).
     auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
@@ -400,13 +405,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     uint32_t eq_run = 0, pos_run = 0;                // totals of earlier blocks
     for (int blk = 0; blk < nblocks; ++blk) {
         if (STREAM) load_block(blk);
-        uint32_t eqc = 0;
+        uint32_t eq_tot = 0, eq_rank = eq_run;
+        if (!whole) {
+            uint32_t eqc = 0;
 #pragma unroll
-        for (int j = 0; j < NR; ++j)
+            for (int j = 0; j < NR; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) eqc += is_eq(key[4 * j + e]);
-        uint32_t eq_tot;
-        uint32_t eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
+                for (int e = 0; e < 4; ++e) eqc += is_eq(key[4 * j + e]);
+            eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
+        }
         uint32_t selbits[(EPT + 31) / 32];
 #pragma unroll
         for (int w = 0; w < (EPT + 31) / 32; ++w) selbits[w] = 0u;
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             uint32_t r = eq_rank + before;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const bool sel = gt[e] || (eq[e] && r < k_rem);
+                const bool sel = gt[e] || (eq[e] && (whole || r < k_rem));
                 r += eq[e];
                 if (sel) {
                     selbits[(4 * j + e) >> 5] |= 1u << ((4 * j + e) & 31);

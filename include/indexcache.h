@@ -201,6 +201,17 @@ IC_API ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_
                          const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
                          void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
 
+/* Cross-layer overlap of two index caches, the diagnostic the agent skill page
+ * (Step 1) uses to choose which layers may share indices: per row r of idx_a,
+ * idx_b [rows, k] int32 (each row ascending and then -1 padded, as the top-k
+ * writes it; k <= 4096), inter[r] = |A & B|, jaccard[r] = inter / (|A | B| +
+ * 1e-8) and recall[r] = inter / |B| (0 when B is empty).  Any of inter,
+ * jaccard, recall may be NULL; means (NULL, or 2 floats) receives the means of
+ * jaccard and recall over the rows, summed in a fixed order, and then needs
+ * jaccard and recall.  All pointers are device pointers. */
+IC_API ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows, int32_t k,
+                                  int32_t* inter, float* jaccard, float* recall, float* means, void* stream);
+
 /* Counters of the last stack call on this thread. */
 IC_API ic_status ic_get_stats(ic_stats* out);
 

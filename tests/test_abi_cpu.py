@@ -134,3 +134,11 @@ def test_mfma_probe_library_exports_its_entry():
     assert hasattr(P, "icp_mfma_stream")
     P.icp_mfma_stream.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     assert P.icp_mfma_stream(1, 0, 1, None, None) != 0   # rejected before any launch
+
+
+def test_index_overlap_validation(L):
+    # NULL inputs, k out of range, means without the per-row outputs: rejected before any launch
+    assert L.ic_index_overlap(None, FAKE, 4, 8, None, None, None, None, None) == 1
+    assert L.ic_index_overlap(FAKE, FAKE, 4, 0, None, None, None, None, None) == 2
+    assert L.ic_index_overlap(FAKE, FAKE, 4, 5000, None, None, None, None, None) == 2
+    assert L.ic_index_overlap(FAKE, FAKE, 4, 8, None, None, None, FAKE, None) == 1
