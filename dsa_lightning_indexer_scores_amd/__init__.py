@@ -30,6 +30,7 @@ IC_OK, IC_ERR_ARG, IC_ERR_SHAPE, IC_ERR_DTYPE, IC_ERR_PATTERN = 0, 1, 2, 3, 4
 IC_ERR_NO_CACHED_INDICES, IC_ERR_WORKSPACE, IC_ERR_HIP = 5, 6, 7
 IC_BF16, IC_FP8_E4M3 = 0, 1
 IC_OP_INDEXER_TOPK, IC_OP_SPARSE_ATTN, IC_OP_RUN_STACK, IC_OP_DECODE_STEP, IC_OP_INDEXER_SCORES = 0, 1, 2, 3, 4
+IC_OP_RUN_STACK_VARLEN = 5
 
 
 class Shape(ctypes.Structure):
@@ -81,6 +82,8 @@ def lib() -> ctypes.CDLL:
     L.ic_topk_rows_seq_ws.argtypes = [i32, i32, i32]
     L.ic_topk_rows_seq_ws.restype = sz
     L.ic_index_overlap.argtypes = [vp, vp, i64, i32, vp, vp, vp, vp, vp]
+    L.ic_run_stack_varlen.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), P(ctypes.c_int32), P(ctypes.c_int32),
+                                      vp, vp, sz, P(Stats), vp]
     L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
@@ -88,7 +91,7 @@ def lib() -> ctypes.CDLL:
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
     for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
-               "ic_sparse_attn", "ic_run_stack",
+               "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen",
                "ic_decode_step", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -307,6 +310,49 @@ def run_stack(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, c
     st = Stats()
     _check(lib().ic_run_stack(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(idx_cache), _ptr(ws),
                               0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
+    return outs, idx_cache, st.as_dict()
+
+
+def run_stack_varlen(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, q_len: Sequence[int],
+                     pos0: Sequence[int], chunk: int = 0, outs: Optional[List[torch.Tensor]] = None, idx_cache=None,
+                     ws=None, stream=None):
+    """Ragged batched prefill: sequence b brings q_len[b] queries at positions pos0[b].. of its own
+    cache.  layers[l]: packed q [T, H, d] (+ q_I [T, H_I, d_I], w [T, H_I] on F layers) with
+    T = sum(q_len), and per-sequence caches kv [B, Lk, 2, d] (+ k_I [B, Lk, d_I])."""
+    B, T = len(q_len), int(sum(q_len))
+    if len(pos0) != B:
+        raise ValueError("q_len and pos0 must have one entry per sequence")
+    q0, kv0 = layers[0]["q"], layers[0]["kv"]
+    _need(q0, "q", (torch.bfloat16,), 3)
+    _need(kv0, "kv", (torch.bfloat16,), 4)
+    if q0.shape[0] != T or kv0.shape[0] != B or kv0.shape[2] != 2 or kv0.shape[3] != q0.shape[2]:
+        raise ValueError(f"q {tuple(q0.shape)} / kv {tuple(kv0.shape)} do not match q_len (B={B}, T={T})")
+    s = make_shape(B, T, kv0.shape[1], k, q0.shape[1], q0.shape[2], chunk=chunk)
+    first_f = next((l for c, l in zip(pattern, layers) if c in "F1" and "q_I" in l), None)
+    if first_f is not None:
+        _need(first_f["q_I"], "q_I", _IDX_DTYPES, 3)
+        _need(first_f["w"], "w", (torch.float32,), 2)
+        _need(first_f["k_I"], "k_I", _IDX_DTYPES, 3)
+        s.H_I, s.d_I = first_f["q_I"].shape[1], first_f["q_I"].shape[2]
+        s.idx_dtype = _idx_dtype(first_f["q_I"])
+        if (first_f["q_I"].shape[0] != T or tuple(first_f["w"].shape) != (T, s.H_I)
+                or tuple(first_f["k_I"].shape) != (B, s.Lk, s.d_I)):
+            raise ValueError("q_I [T,H_I,d_I], w [T,H_I] and k_I [B,Lk,d_I] do not match q / kv")
+    for lay in layers:
+        if tuple(lay["q"].shape) != tuple(q0.shape) or tuple(lay["kv"].shape) != tuple(kv0.shape):
+            raise ValueError("every layer must have the same q and kv shapes")
+    dev = q0.device
+    if outs is None:
+        outs = [torch.empty_like(l["q"]) for l in layers]
+    if idx_cache is None:
+        idx_cache = torch.empty((T, k), dtype=torch.int32, device=dev)
+    ws = _workspace(workspace_size(s, IC_OP_RUN_STACK_VARLEN), dev, ws)
+    arr = _layers_struct(pattern, layers, outs)
+    st = Stats()
+    ql = (ctypes.c_int32 * B)(*[int(x) for x in q_len])
+    p0 = (ctypes.c_int32 * B)(*[int(x) for x in pos0])
+    _check(lib().ic_run_stack_varlen(pattern.encode(), len(layers), arr, ctypes.byref(s), ql, p0, _ptr(idx_cache),
+                                     _ptr(ws), 0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
     return outs, idx_cache, st.as_dict()
 
 

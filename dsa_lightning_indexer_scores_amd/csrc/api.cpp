@@ -45,13 +45,16 @@ ic_status hip_fail(hipError_t e, const char* what) {
 
 int chunk_of(const ic_shape& s) { return s.chunk == 0 ? kDefaultChunk : s.chunk; }
 
-// Sizes the kernels support; `decode` relaxes the prefill position checks.
-ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode) {
+// Sizes the kernels support; `decode` relaxes the prefill position checks, and `varlen`
+// leaves them to the per-sequence check (Lq is then the packed query count).
+ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode, bool varlen = false) {
     if (!sp) return fail(IC_ERR_ARG, "shape is NULL");
     const ic_shape& s = *sp;
     if (s.B < 1 || s.Lq < 1 || s.Lk < 1) return fail(IC_ERR_SHAPE, "B, Lq, Lk must be >= 1 (got %d, %d, %d)", s.B, s.Lq, s.Lk);
     if (decode) {
         if (s.Lq != 1) return fail(IC_ERR_SHAPE, "decode needs Lq == 1 (got %d)", s.Lq);
+    } else if (varlen) {
+        if (s.pos0 != 0) return fail(IC_ERR_SHAPE, "ragged prefill takes per-sequence pos0; shape.pos0 must be 0");
     } else {
         if (s.pos0 < 0) return fail(IC_ERR_SHAPE, "pos0 must be >= 0 (got %d)", s.pos0);
         if ((int64_t)s.pos0 + s.Lq > s.Lk)
@@ -78,6 +81,12 @@ int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 size_t indexer_ws(const ic_shape& s) {
     const int64_t rows = std::min<int64_t>(chunk_of(s), s.Lq);
     return (size_t)round_up(rows * round_up((int64_t)s.pos0 + s.Lq, 4) * 4, 256);
+}
+
+// Ragged prefill: a tile for any one sequence (<= chunk rows x <= Lk columns).
+size_t indexer_ws_varlen(const ic_shape& s) {
+    const int64_t rows = std::min<int64_t>(chunk_of(s), s.Lq);
+    return (size_t)round_up(rows * round_up((int64_t)s.Lk, 4) * 4, 256);
 }
 
 // Key splits per decode query: about 1024 waves in all (one per SIMD; more splits
@@ -124,47 +133,56 @@ ic_status check_ws(const void* ws, size_t have, size_t need) {
 
 size_t elem_bytes(int dtype) { return dtype == IC_FP8_E4M3 ? 1 : 2; }
 
-// a1 + a2 for every sequence of the call: score tiles of <= chunk queries, then top-k into idx.
+// a1 + a2 for one sequence: its Lq queries at positions pos0.. against its keys, in score
+// tiles of <= chunk queries, then top-k into idx [Lq, k].
+ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_t* qb, const float* wb,
+                               const uint8_t* kb, int32_t* idx, void* ws, hipStream_t st, int64_t* tiles) {
+    const int chunk = chunk_of(s);
+    float* tile = static_cast<float*>(ws);
+    for (int c0 = 0; c0 < Lq; c0 += chunk) {
+        const int nq = std::min(chunk, Lq - c0);
+        const int64_t stride = round_up((int64_t)pos0 + c0 + nq, 4);
+        ic_indexer_args a;
+        a.q_I = qb;
+        a.w = wb;
+        a.k_I = kb;
+        a.scores = tile;
+        a.row_stride = stride;
+        a.q_begin = c0;
+        a.nq = nq;
+        a.pos_begin = pos0 + c0;
+        a.H_I = s.H_I;
+        a.d_I = s.d_I;
+        a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+        hipError_t e = launch_indexer_prefill(a, st);
+        if (e != hipSuccess) return hip_fail(e, "indexer launch");
+        ic_topk_args t;
+        t.scores = tile;
+        t.row_stride = stride;
+        t.rows = nq;
+        t.first_len = pos0 + c0 + 1;
+        t.seq_len = nullptr;
+        t.k = s.k;
+        t.idx = idx + (size_t)c0 * s.k;
+        t.max_len = pos0 + c0 + nq;
+        t.cand = nullptr;
+        e = launch_topk(t, st);
+        if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        if (tiles) ++*tiles;
+    }
+    return IC_OK;
+}
+
+// a1 + a2 for every sequence of the call (all with Lq queries at pos0).
 ic_status run_indexer_topk(const ic_shape& s, const void* q_I, const float* w, const void* k_I, int32_t* idx,
                            void* ws, hipStream_t st, int64_t* tiles) {
-    const int chunk = chunk_of(s);
     const size_t eb = elem_bytes(s.idx_dtype);
-    float* tile = static_cast<float*>(ws);
     for (int b = 0; b < s.B; ++b) {
         const uint8_t* qb = static_cast<const uint8_t*>(q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
         const float* wb = w + (size_t)b * s.Lq * s.H_I;
         const uint8_t* kb = static_cast<const uint8_t*>(k_I) + (size_t)b * s.Lk * s.d_I * eb;
-        for (int c0 = 0; c0 < s.Lq; c0 += chunk) {
-            const int nq = std::min(chunk, s.Lq - c0);
-            const int64_t stride = round_up((int64_t)s.pos0 + c0 + nq, 4);
-            ic_indexer_args a;
-            a.q_I = qb;
-            a.w = wb;
-            a.k_I = kb;
-            a.scores = tile;
-            a.row_stride = stride;
-            a.q_begin = c0;
-            a.nq = nq;
-            a.pos_begin = s.pos0 + c0;
-            a.H_I = s.H_I;
-            a.d_I = s.d_I;
-            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
-            hipError_t e = launch_indexer_prefill(a, st);
-            if (e != hipSuccess) return hip_fail(e, "indexer launch");
-            ic_topk_args t;
-            t.scores = tile;
-            t.row_stride = stride;
-            t.rows = nq;
-            t.first_len = s.pos0 + c0 + 1;
-            t.seq_len = nullptr;
-            t.k = s.k;
-            t.idx = idx + ((size_t)b * s.Lq + c0) * s.k;
-            t.max_len = s.pos0 + c0 + nq;
-            t.cand = nullptr;
-            e = launch_topk(t, st);
-            if (e != hipSuccess) return hip_fail(e, "top-k launch");
-            if (tiles) ++*tiles;
-        }
+        ic_status r = run_indexer_topk_one(s, s.Lq, s.pos0, qb, wb, kb, idx + (size_t)b * s.Lq * s.k, ws, st, tiles);
+        if (r != IC_OK) return r;
     }
     return IC_OK;
 }
@@ -231,6 +249,9 @@ size_t ic_workspace_size(const ic_shape* shape, int op) {
         case IC_OP_INDEXER_SCORES:
             if (check_shape(shape, op == IC_OP_INDEXER_SCORES, false) != IC_OK) return 0;
             return 0;
+        case IC_OP_RUN_STACK_VARLEN:
+            if (check_shape(shape, true, false, true) != IC_OK) return 0;
+            return indexer_ws_varlen(*shape);
         case IC_OP_DECODE_STEP:
             if (check_shape(shape, true, true) != IC_OK) return 0;
             return decode_ws(*shape);
@@ -367,6 +388,77 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
         }
         r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
         if (r != IC_OK) return r;
+        ++cnt.attn_calls;
+        ++cnt.layers;
+    }
+    g_stats = cnt;
+    if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape* shape,
+                              const int32_t* q_len, const int32_t* pos0, int32_t* idx_cache, void* ws, size_t ws_bytes,
+                              ic_stats* stats, void* stream) {
+    ic_status r = check_shape(shape, true, false, true);
+    if (r != IC_OK) return r;
+    if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
+    if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if (!q_len || !pos0) return fail(IC_ERR_ARG, "q_len and pos0 must be non-NULL host arrays");
+    const ic_shape& s = *shape;
+    int64_t total = 0;
+    for (int b = 0; b < s.B; ++b) {
+        if (q_len[b] < 0 || pos0[b] < 0)
+            return fail(IC_ERR_SHAPE, "sequence %d: q_len %d and pos0 %d must be >= 0", b, q_len[b], pos0[b]);
+        if ((int64_t)pos0[b] + q_len[b] > s.Lk)
+            return fail(IC_ERR_SHAPE, "sequence %d: pos0 + q_len (%lld) exceeds Lk (%d)", b,
+                        (long long)pos0[b] + q_len[b], s.Lk);
+        total += q_len[b];
+    }
+    if (total != s.Lq) return fail(IC_ERR_SHAPE, "q_len sums to %lld, shape.Lq is %d", (long long)total, s.Lq);
+    if ((r = check_ws(ws, ws_bytes, indexer_ws_varlen(s))) != IC_OK) return r;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t eb = elem_bytes(s.idx_dtype);
+    ic_stats cnt = {0, 0, 0, 0};
+    bool cached = false;                       // the index cache starts empty on every call
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        const bool full = pattern[l] == 'F' || pattern[l] == '1';
+        if (!full && !cached) return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
+        int64_t q0 = 0;                        // first packed row of sequence b
+        for (int b = 0; b < s.B; ++b) {
+            const int n = q_len[b];
+            if (n > 0) {
+                int32_t* idxb = idx_cache + q0 * s.k;
+                if (full) {
+                    r = run_indexer_topk_one(
+                        s, n, pos0[b], static_cast<const uint8_t*>(L.q_I) + q0 * s.H_I * s.d_I * eb, L.w + q0 * s.H_I,
+                        static_cast<const uint8_t*>(L.k_I) + (size_t)b * s.Lk * s.d_I * eb, idxb, ws, st,
+                        &cnt.score_tiles);
+                    if (r != IC_OK) return r;
+                }
+                ic_attn_args a;
+                a.q = static_cast<const uint16_t*>(L.q) + q0 * s.H * s.d;
+                a.kv = static_cast<const uint16_t*>(L.kv) + (size_t)b * s.Lk * 2 * s.d;
+                a.idx = idxb;
+                a.out = static_cast<uint16_t*>(L.out) + q0 * s.H * s.d;
+                a.kv_seq_stride = (int64_t)s.Lk * 2 * s.d;
+                a.Lk = s.Lk;
+                a.nq = n;
+                a.q_per_seq = n;
+                a.H = s.H;
+                a.d = s.d;
+                a.k = s.k;
+                a.nsplit = 1;
+                a.ws = nullptr;
+                hipError_t e = launch_sparse_attn(a, st);
+                if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+            }
+            q0 += n;
+        }
+        if (full) {
+            cached = true;
+            ++cnt.indexer_calls;
+        }
         ++cnt.attn_calls;
         ++cnt.layers;
     }

@@ -126,7 +126,8 @@ enum {
     IC_OP_SPARSE_ATTN = 1,
     IC_OP_RUN_STACK = 2,
     IC_OP_DECODE_STEP = 3,
-    IC_OP_INDEXER_SCORES = 4
+    IC_OP_INDEXER_SCORES = 4,
+    IC_OP_RUN_STACK_VARLEN = 5
 };
 
 /* Bytes of workspace the operation needs for this shape (0 if none).
@@ -190,6 +191,22 @@ IC_API ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void
 IC_API ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
                        const ic_shape* shape, int32_t* idx_cache, void* ws, size_t ws_bytes,
                        ic_stats* stats, void* stream);
+
+/* Ragged batched prefill through the stack: B sequences of different lengths,
+ * each continuing its own cached prefix (so a chunked prefill can resume and then
+ * hand over to ic_decode_step).  Sequence b brings q_len[b] >= 0 new queries at
+ * positions pos0[b] .. pos0[b]+q_len[b]-1 and sees its own keys 0..position;
+ * q_len and pos0 are HOST int32 arrays [B] with pos0[b] + q_len[b] <= Lk.  The
+ * queries are packed in sequence order, so shape.Lq = sum of q_len is the
+ * packed row count and shape.pos0 must be 0:
+ *   q_I [Lq, H_I, d_I], w [Lq, H_I], q [Lq, H, d], out [Lq, H, d] (packed rows)
+ *   k_I [B, Lk, d_I], kv [B, Lk, 2, d]                        (per-sequence caches)
+ *   idx_cache [Lq, k] int32.
+ * Pattern and cache rules as ic_run_stack; the workspace is
+ * ic_workspace_size(shape, IC_OP_RUN_STACK_VARLEN). */
+IC_API ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, const ic_layer* layers,
+                                     const ic_shape* shape, const int32_t* q_len, const int32_t* pos0,
+                                     int32_t* idx_cache, void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
 
 /* One decode step through the stack.  shape.Lq must be 1 and shape.Lk is
  * the cache capacity.  seq_len [B] int32 (device) counts each sequence's

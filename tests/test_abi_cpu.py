@@ -142,3 +142,19 @@ def test_index_overlap_validation(L):
     assert L.ic_index_overlap(FAKE, FAKE, 4, 0, None, None, None, None, None) == 2
     assert L.ic_index_overlap(FAKE, FAKE, 4, 5000, None, None, None, None, None) == 2
     assert L.ic_index_overlap(FAKE, FAKE, 4, 8, None, None, None, FAKE, None) == 1
+
+
+def test_run_stack_varlen_validation(L):
+    s = _shape(B=2, Lq=30, Lk=100)
+    ql = (ctypes.c_int32 * 2)(10, 20)
+    p0 = (ctypes.c_int32 * 2)(0, 50)
+    run = lambda pat, shape, q, p: L.ic_run_stack_varlen(pat.encode(), len(pat), _layers(pat), ctypes.byref(shape),
+                                                         q, p, FAKE, ctypes.c_void_p(0x10000), 1 << 30, None, None)
+    assert run("FS", s, None, p0) == 1                                    # host arrays are required
+    assert run("SF", s, ql, p0) == 5                                      # S first
+    bad = (ctypes.c_int32 * 2)(10, 21)
+    assert run("FS", s, bad, p0) == 2                                     # q_len does not sum to Lq
+    far = (ctypes.c_int32 * 2)(0, 90)
+    assert run("FS", s, ql, far) == 2                                     # pos0 + q_len beyond Lk
+    s2 = _shape(B=2, Lq=30, Lk=100, pos0=5)
+    assert run("FS", s2, ql, p0) == 2                                     # per-sequence pos0 only
