@@ -20,10 +20,16 @@
 //   S^T (32 keys x 16 heads) = K Q^T;
 //   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
 //       lane % 16) is also the layout of O^T below, so the running max and
-//       rescale never leave the lane;
+//       rescale never leave the lane.  The reference max moves only when a
+//       step's max passes it by more than 2^8, so most steps skip the O rescale;
 //   O^T (d x 16 heads) += V^T P^T : V read back transposed with
 //       ds_read_b64_tr_b16; P^T is the S^T accumulator packed to bf16 (its
-//       k order matches the transposed read, so no shuffle is needed).
+//       k order matches the transposed read, so no shuffle is needed);
+//   l += ones^T P^T, one more MFMA, so the denominator sums the same bf16 P
+//       as the numerator and costs no VALU.
+// Row offsets of a step are staged through a few wave-private LDS words so each
+// lane reads its load addresses as one vector (no per-row lane reads).  Steps past
+// a query's last real idx entry are not run.
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
 // workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
 // the workgroups' partials in split order, so results are deterministic.  (A
@@ -37,6 +43,11 @@ namespace {
 
 constexpr int ATT_NW = 4;
 constexpr int KT = 32;                  // selected rows per step
+// The running max of a head is moved (and O, l rescaled) only when a step's max
+// exceeds it by more than this many powers of two, so most steps skip the rescale;
+// the probabilities stay <= 2^RESCALE_LOG2, far inside fp32 and bf16 range.  Any
+// reference value gives the same softmax once O is divided by l.
+constexpr float RESCALE_LOG2 = 8.f;
 
 template <int D, bool ROWS>
 struct AttGeom {
@@ -82,6 +93,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int64_t qi = item / ((int64_t)nsplit * HG);
     if (qi >= nq) return;
     uint8_t* vlds = vlds_all[wv];
+    __shared__ __attribute__((aligned(16))) uint32_t idx_lds_all[ATT_NW][KT];   // ROWS: a step's row offsets
+    uint32_t* idx_lds = idx_lds_all[wv];
 
     const int seq = (int)(qi / q_per_seq);
     const uint16_t* kvs = kv + (int64_t)seq * kv_seq_stride;
@@ -104,54 +117,89 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int per = ((k + nsplit - 1) / nsplit + KT - 1) / KT * KT;
     const int j_begin = sp * per;
     const int j_end = min(k, j_begin + per);
+    // Only the steps up to the last entry that names a row are run (an idx row padded
+    // with -1 because fewer than k keys are visible costs only its real steps).
+    int j_last = -1;
+    for (int jb = j_begin; jb < j_end; jb += 64 * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + 64 * u + lane;
+            v[u] = j < j_end ? irow[j] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if ((uint32_t)v[u] < (uint32_t)Lk) j_last = max(j_last, jb + 64 * u + lane);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
+    const int nsteps = j_last < 0 ? 0 : (j_last - j_begin) / KT + 1;
+    // Ends with a wait for every load so far: the step loop below starts from a clean count.
+    __builtin_amdgcn_s_waitcnt(0);
 
     f32x4 o[G::NDT];
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY, l_run = 0.f;
+    // Reference max of the head (log2 units).  Finite from the start, so a step whose
+    // entries are all -1 gives exp2(-inf) = 0 rather than exp2(-inf + inf).
+    float m_run = -1e30f;
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};                   // softmax denominator (every slot)
+    const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};   // bf16 1.0 pairs
 
     // One step of KT selected rows.  Loads of step t+1 are issued before step t is
-    // computed (two register sets, A and B), and the idx entries of step t+2 are
-    // fetched one step earlier still, so gathers overlap compute.
+    // computed (two register sets, A and B), and the idx entries of a step are fetched
+    // one step before its loads.  Every step issues its loads and is computed (entries
+    // of -1 read a real row and are masked), so no branch separates a load from its
+    // use and the compiler's in-order load counting stays exact.
     struct Tile {
         i32x4 raw[ROWS ? G::NI : 1];                         // ROWS: whole rows, as loaded
         i32x4 kf[ROWS ? 1 : 2][G::NDC];                      // !ROWS: K fragments, keys 16*kt + m
         i32x4 vst[ROWS ? 1 : G::VPL];                        // !ROWS: V rows, staged for LDS
         uint32_t valid;                                      // bit e: entry e of the step is a row
     };
+    // The raw entry only: it is first used at the next issue, so the wait for this load
+    // lands there and not right behind the row loads issued just before it (loads
+    // complete in order, so an early use would wait for those rows too).
     auto load_idx = [&](int j0) -> int {
         const int jl = j0 + (lane & 31);
-        int v = (jl < j_end && lane < 32) ? irow[jl] : -1;
-        return (v >= Lk) ? -1 : v;                           // never read past the KV rows
+        return (jl < j_end && lane < 32) ? irow[jl] : -1;
     };
-    auto issue = [&](Tile& T, int my_idx) {
-        T.valid = (uint32_t)__ballot(my_idx >= 0);
-        if (T.valid == 0u) return;
-        const int safe_idx = my_idx >= 0 ? my_idx : 0;
+    auto issue = [&](Tile& T, int raw_idx) {
+        // Nothing of an issue may be scheduled into the previous compute: its first use of
+        // raw_idx waits for every load before it, including the tile that compute overlaps.
+        __builtin_amdgcn_sched_barrier(0);
+        const bool ok = (uint32_t)raw_idx < (uint32_t)Lk;   // -1 or past the KV rows: no row
+        T.valid = (uint32_t)__ballot(ok);
+        const uint32_t row = ok ? (uint32_t)raw_idx : 0u;    // a real row, masked later
         if constexpr (ROWS) {
-            const int piece = (lane % G::PPR) * 16;
+            // Row offsets go through the wave's LDS slots, de-interleaved so that the
+            // lanes of row r of every load instruction read theirs as one vector:
+            // entry RPI*i + r -> slot r*NI + i.
+            if (lane < KT) idx_lds[(lane % G::RPI) * G::NI + lane / G::RPI] = row * (uint32_t)G::RB;
+            lds_wave_sync();
+            uint32_t roff[G::NI];
 #pragma unroll
-            for (int i = 0; i < G::NI; ++i) {                // rows RPI*i + lane / PPR
-                int row = __builtin_amdgcn_readlane(safe_idx, G::RPI * i);
-#pragma unroll
-                for (int r = 1; r < G::RPI; ++r) {
-                    const int other = __builtin_amdgcn_readlane(safe_idx, G::RPI * i + r);
-                    row = (lane / G::PPR == r) ? other : row;
-                }
-                T.raw[i] = *reinterpret_cast<const i32x4*>(kvb + (uint32_t)row * G::RB + piece);
+            for (int i = 0; i < G::NI; i += 4) {
+                const u32x4 v = *reinterpret_cast<const u32x4*>(idx_lds + (lane / G::PPR) * G::NI + i);
+                roff[i] = v[0]; roff[i + 1] = v[1]; roff[i + 2] = v[2]; roff[i + 3] = v[3];
             }
+            const uint32_t piece = (lane % G::PPR) * 16;
+#pragma unroll
+            for (int i = 0; i < G::NI; ++i)
+                T.raw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));   // scalar base + 32-bit offset
         } else {
+            const int safe_idx = (int)row;
 #pragma unroll
             for (int i = 0; i < G::VPL; ++i) {               // V piece c -> row c / VPPR, byte (c % VPPR) * 16
                 const int c = lane + 64 * i;
-                const int row = __shfl(safe_idx, c / G::VPPR);
-                const uint32_t off = (uint32_t)row * G::RB + 2 * D + (c % G::VPPR) * 16;
+                const int r = __shfl(safe_idx, c / G::VPPR);
+                const uint32_t off = (uint32_t)r * G::RB + 2 * D + (c % G::VPPR) * 16;
                 T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
             }
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {                 // lane (m, g): key 16*kt + m, d = 32*dc + 8g
-                const int row = __shfl(safe_idx, 16 * kt + n);
-                const uint32_t off = (uint32_t)row * G::RB + 16 * g;
+                const int r = __shfl(safe_idx, 16 * kt + n);
+                const uint32_t off = (uint32_t)r * G::RB + 16 * g;
 #pragma unroll
                 for (int dc = 0; dc < G::NDC; ++dc)
                     T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
@@ -159,7 +207,6 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         }
     };
     auto compute = [&](const Tile& T) {
-        if (T.valid == 0u) return;                           // a step of -1 entries contributes nothing
         const uint32_t valid = T.valid;
         if constexpr (ROWS) {
 #pragma unroll
@@ -191,31 +238,32 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
             }
             s[kt] = acc;
         }
-        float x[8];
-        float tmax = -INFINITY;
+        float x[8];                                          // raw scores; -inf for -1 entries
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * kt + 4 * g + e;
-                const float v = ((valid >> j) & 1u) ? s[kt][e] * scale_log2 : -INFINITY;
-                x[4 * kt + e] = v;
-                tmax = fmaxf(tmax, v);
-            }
-        tmax = max_xor16(tmax);
-        tmax = max_xor32(tmax);
-        const float m_new = fmaxf(m_run, tmax);              // finite: the step has a row
-        const float alpha = exp2f(m_run - m_new);
-        float psum = 0.f;
+            for (int e = 0; e < 4; ++e) x[4 * kt + e] = s[kt][e];
+        if (valid != 0xFFFFFFFFu) {                          // wave-uniform: only ragged steps mask
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            x[e] = exp2f(x[e] - m_new);
-            psum += x[e];
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!((valid >> (16 * kt + 4 * g + e)) & 1u)) x[4 * kt + e] = -INFINITY;
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        float tmax = x[0];
 #pragma unroll
-        for (int dt = 0; dt < G::NDT; ++dt) o[dt] *= alpha;
+        for (int e = 1; e < 8; ++e) tmax = fmax_nan(tmax, x[e]);
+        tmax = max_xor32(max_xor16(tmax)) * scale_log2;      // finite: the step has a row
+        if (__ballot(tmax > m_run + RESCALE_LOG2)) {         // some head's max grew a lot (always at the first step)
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int dt = 0; dt < G::NDT; ++dt) o[dt] *= alpha;
+            lsum *= alpha;
+            m_run = m_new;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
         // P^T fragment: slots 0..3 = keys 4g+e, slots 4..7 = keys 16+4g+e.
         i32x4 pf;
         pf[0] = (int)pack_bf16x2(x[0], x[1]);
@@ -238,33 +286,36 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
             const i32x4 vf = {(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1]};
             o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
         }
+        // l += sum over the step's keys of P (as rounded to bf16, like the numerator):
+        // every d row of ones^T P^T is that sum, so each lane gets its head's l.
+        lsum = mfma_bf16_k32(ones, pf, lsum);
         lds_wave_sync();
     };
 
-    const int nsteps = j_end > j_begin ? (j_end - j_begin + KT - 1) / KT : 0;
     Tile TA, TB;
-    int idx0 = 0, idx1 = 0;
     if (nsteps > 0) {
         issue(TA, load_idx(j_begin));
-        idx1 = load_idx(j_begin + KT);
-    }
-    for (int t = 0; t < nsteps; t += 2) {
-        if (t + 1 < nsteps) {
-            issue(TB, idx1);
-            idx0 = load_idx(j_begin + (t + 2) * KT);
-        }
-        compute(TA);
-        if (t + 1 < nsteps) {
-            if (t + 2 < nsteps) {
-                issue(TA, idx0);
-                idx1 = load_idx(j_begin + (t + 3) * KT);
-            }
+        int idxA, idxB = load_idx(j_begin + KT);
+        int t = 0;
+        for (; t + 2 < nsteps; t += 2) {                     // both issues unconditional
+            issue(TB, idxB);
+            idxA = load_idx(j_begin + (t + 2) * KT);
+            compute(TA);
+            issue(TA, idxA);
+            idxB = load_idx(j_begin + (t + 3) * KT);
             compute(TB);
+        }
+        if (t + 1 < nsteps) {                                // last two steps
+            issue(TB, idxB);
+            compute(TA);
+            compute(TB);
+        } else {                                             // last step
+            compute(TA);
         }
     }
 
-    l_run = sum_xor16(l_run);
-    l_run = sum_xor32(l_run);
+    const float l_run = lsum[0];
+    if (l_run == 0.f) m_run = -INFINITY;                 // no selected row: an empty partial
     if constexpr (!SPLIT) {
         if (head < H) {
             const float inv = 1.f / l_run;
