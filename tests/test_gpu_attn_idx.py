@@ -1,0 +1,58 @@
+"""GPU parity of the sparse attention on idx rows that no top-k would write:
+-1 entries anywhere in a row (single holes, whole 32-entry steps, everything but
+the first or the last entry), unsorted entries and repeated entries.  The
+attention contract only asks for at least one entry >= 0 per row and every
+entry < Lk; a -1 is skipped wherever it sits and a repeated row counts twice.
+Checked against the fp64 oracle fed the same idx, to the attention tolerance."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import dsa_lightning_indexer_scores_amd as ic
+from parity_helpers import ATTN_TOL, attn_rel_err, dec, summary
+
+pytestmark = pytest.mark.gpu
+
+
+def idx_patterns(Lq: int, Lk: int, k: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng(seed)
+    idx = np.full((Lq, k), -1, dtype=np.int32)
+    for t in range(Lq):
+        kind = t % 8
+        row = rng.permutation(Lk)[:k].astype(np.int32)           # distinct, unsorted
+        if kind == 0:                                            # only the last entry
+            idx[t, k - 1] = row[0]
+        elif kind == 1:                                          # only the first entry
+            idx[t, 0] = row[0]
+        elif kind == 2:                                          # scattered holes
+            keep = rng.random(k) < 0.6
+            idx[t] = np.where(keep, row, -1)
+            idx[t, rng.integers(k)] = row[0]
+        elif kind == 3:                                          # whole steps of -1 in the middle
+            idx[t] = row
+            idx[t, 32:64] = -1
+            idx[t, 96:128] = -1
+        elif kind == 4:                                          # repeated entries
+            idx[t] = rng.integers(0, 5, size=k)
+        elif kind == 5:                                          # sorted, trailing -1 (top-k shape)
+            n = 1 + t % k
+            idx[t, :n] = np.sort(row[:n])
+        else:                                                    # every entry a row, unsorted
+            idx[t] = row
+    return idx
+
+
+@pytest.mark.parametrize("d,H,k", [(128, 16, 200), (128, 20, 256), (64, 4, 200), (64, 16, 160)])
+def test_attention_any_idx_layout(d, H, k):
+    torch.manual_seed(d * 1000 + H + k)
+    Lq, Lk = 64, 700
+    q = (torch.randn(1, Lq, H, d) * 0.5).to(torch.bfloat16).cuda()
+    kv = (torch.randn(1, Lk, 2, d) * 0.5).to(torch.bfloat16).cuda()
+    idx = idx_patterns(Lq, Lk, k, seed=d + H + k)
+    out = ic.sparse_attn(q, kv, torch.from_numpy(idx)[None].cuda())
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(dec(q)[0], dec(kv)[0], idx)
+    err = attn_rel_err(dec(out)[0], ref)
+    summary(f"attention idx layouts d={d} H={H} k={k}", {"max_rel_err": err})
+    assert err <= ATTN_TOL
