@@ -68,8 +68,9 @@ __device__ __forceinline__ float max_xor32(float x) {
 // -0.0 is folded onto +0.0 first so that the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float f) {
     f = f + 0.0f;
-    uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(f);
+    // negative: all bits flipped; otherwise the sign bit set (three VALU ops)
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
 }
 
 

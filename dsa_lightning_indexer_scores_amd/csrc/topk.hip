@@ -13,14 +13,16 @@
 // skipped; the rest are resolved most-significant digit first with 11-bit LDS
 // histograms (for long rows one copy per wave, summed at the scan) until the
 // k-th key's prefix is exact or its bin is taken whole.
-// For long rows (streamed from L2 at every pass) a pass is expensive, so once
-// the bin holding the k-th key has at most CAND_CAP keys, one pass gathers that
-// bin's keys and positions into LDS and ranks them exactly, giving the
-// threshold pair (key, position) and a single-pass emit.  Register-resident
-// rows keep narrowing the digit instead (measured faster there).  A final pass walks the row in index
-// order and compacts the selected positions with wave ballots (mbcnt prefix
-// counts) and a prefix sum over the waves, so the output is sorted for free
-// and ties resolve to the lowest indices.
+// Once the bin holding the k-th key has at most CAND_CAP keys (after the first
+// pass, for smooth score distributions), one pass gathers that bin's keys and
+// positions into LDS and ranks them exactly, giving the threshold pair (key,
+// position); when no other key shares the threshold value a plain key test
+// selects.  A final pass walks the row in index order and ranks the selected
+// positions with wave ballots (mbcnt prefix counts) and a prefix sum over the
+// waves, so the output is sorted for free and ties resolve to the lowest
+// indices; the ranked positions are staged in LDS (the histograms' space) and
+// written out with coalesced stores.  Rounds of a wave that lie past the row's
+// end are skipped in every pass.
 //
 // Few long rows (decode: one row per sequence) would leave most CUs idle, so
 // they run in two launches.  First every (row, segment of SEG keys) takes its
@@ -120,12 +122,13 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     // One-copy histograms alternate between two buffers: a pass zeroes the next pass's
     // buffer while scanning its own, so zeroing costs no barrier.
     constexpr int NHB = NH == 1 ? 2 : 1;
+    static_assert(NHB * NH * HIST_BINS >= 4096, "the output staging reuses the histograms (k <= 4096)");
     __shared__ uint32_t hist[NHB * NH][HIST_BINS];
     __shared__ uint32_t wtot[NT / 64];
-    __shared__ uint32_t kminmax[3], found[3];
-    __shared__ uint32_t cand_key[CAND_CAP];
-    __shared__ int32_t cand_idx[CAND_CAP];
-    __shared__ uint32_t ncand, thr_key;
+    __shared__ uint32_t kminmax[2], found[3];
+    __shared__ __attribute__((aligned(16))) uint32_t cand_key[CAND_CAP];
+    __shared__ __attribute__((aligned(16))) int32_t cand_idx[CAND_CAP];
+    __shared__ uint32_t ncand, thr_key, thr_ties;
     __shared__ int32_t thr_idx;
     const int row = blockIdx.x;
     const int tid = threadIdx.x;
@@ -162,6 +165,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     const int nblocks = STREAM ? (n + BLOCK - 1) / BLOCK : 1;
 
     uint32_t key[EPT];
+    // Round j of a wave covers positions [w0 + 256 j, w0 + 256 (j + 1)) of its block; when
+    // that lies inside the row (wave-uniform test) its keys need no bounds checks.
+    auto round_full = [&](int blk, int j) -> bool {
+        return blk * BLOCK + wv * 64 * EPT + 256 * (j + 1) <= n;
+    };
+    // ... and when it starts past the row end it holds only key-0 padding: skipped.
+    auto round_live = [&](int blk, int j) -> bool {
+        return MODE == TOPK_GATHER || blk * BLOCK + wv * 64 * EPT + 256 * j < n;
+    };
     auto load_block = [&](int blk) {
         const int b0 = blk * BLOCK + lane_base;
         if constexpr (MODE == TOPK_GATHER) {         // the candidates' keys, as the segments wrote them
@@ -179,64 +191,81 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             }
             return;
         }
+        float v[EPT];
+#pragma unroll
+        for (int j = 0; j < NR; ++j) {               // every load first (one wait for all of them)
+            const int i0 = b0 + 256 * j;
+            if (VEC) {
+                // a lane past the row reads the row's first 16 B instead (its keys are zeroed
+                // below); 16 B from i0 < n stay inside the row since row_stride % 4 == 0
+                const float4 f = *reinterpret_cast<const float4*>(src + (i0 < n ? i0 : 0));
+                v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[4 * j + e] = (i0 + e < n) ? src[i0 + e] : 0.f;
+            }
+        }
+        // Positions past the row get key 0, which no score maps to (a real key is
+        // >= 0x007FFFFF): it sorts below every real key, lands in histogram bin 0 of the
+        // first pass (subtracted there) and comes after every real key in index order,
+        // so it is never selected.
 #pragma unroll
         for (int j = 0; j < NR; ++j) {
             const int i0 = b0 + 256 * j;
-            float v[4] = {0.f, 0.f, 0.f, 0.f};
-            if (VEC) {
-                if (i0 < n) {                        // 16 B stay inside the row: row_stride % 4 == 0
-                    const float4 f = *reinterpret_cast<const float4*>(src + i0);
-                    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-                }
+            if (round_full(blk, j)) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) key[4 * j + e] = score_key(v[4 * j + e]);
             } else {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) v[e] = (i0 + e < n) ? src[i0 + e] : 0.f;
+                for (int e = 0; e < 4; ++e) key[4 * j + e] = (i0 + e < n) ? score_key(v[4 * j + e]) : 0u;
             }
-            // Positions past the row get key 0, which no score maps to (a real key is
-            // >= 0x007FFFFF): it sorts below every real key, only ever lands in
-            // histogram bin 0 (corrected below) and comes after every real key in
-            // index order, so it is never selected.
-#pragma unroll
-            for (int e = 0; e < 4; ++e) key[4 * j + e] = (i0 + e < n) ? score_key(v[e]) : 0u;
         }
     };
-    // Smallest and largest real key of the row, and (candidate lists) the empty slots.
-    uint32_t lo = 0xFFFFFFFFu, hi = 0u, zeros = 0u;
+    // Smallest and largest real key of the row.
+    uint32_t lo = 0xFFFFFFFFu, hi = 0u;
     for (int blk = 0; blk < nblocks; ++blk) {
         load_block(blk);
 #pragma unroll
-        for (int j = 0; j < NR; ++j)
+        for (int j = 0; j < NR; ++j) {
+            if (!round_live(blk, j)) continue;
+            if (MODE != TOPK_GATHER && round_full(blk, j)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t kk = key[4 * j + e];
-                lo = min(lo, kk ? kk : 0xFFFFFFFFu);
-                hi = max(hi, kk);
-                if (MODE == TOPK_GATHER) zeros += kk == 0u;
+                for (int e = 0; e < 4; ++e) {
+                    lo = min(lo, key[4 * j + e]);
+                    hi = max(hi, key[4 * j + e]);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t kk = key[4 * j + e];
+                    lo = min(lo, kk ? kk : 0xFFFFFFFFu);
+                    hi = max(hi, kk);
+                }
             }
+        }
     }
     lo = wave_reduce(lo, OpMin());
     hi = wave_reduce(hi, OpMax());
-    if (MODE == TOPK_GATHER) zeros = wave_sum(zeros);
-    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; kminmax[2] = 0u; }
+    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; }
     // the first pass's histogram starts zeroed (both buffers when they alternate)
     for (int b = tid; b < NHB * NH * HIST_BINS; b += NT) (&hist[0][0])[b] = 0u;
     __syncthreads();
     if (lane == 0) {
         atomicMin(&kminmax[0], lo);
         atomicMax(&kminmax[1], hi);
-        if (MODE == TOPK_GATHER) atomicAdd(&kminmax[2], zeros);
     }
     __syncthreads();
     const uint32_t kmin = kminmax[0], kmax = kminmax[1];
-    // key-0 slots in the whole row: padding past the end (and empty candidate slots)
-    const uint32_t n_pad = MODE == TOPK_GATHER ? kminmax[2] : (uint32_t)(nblocks * BLOCK - n);
 
-    // Radix select: candidates are the keys with (key >> shift) == prefix.
+    // Radix select: candidates are the keys with (key >> shift) == prefix.  Every real key
+    // shares the first pass's prefix (the bits common to kmin and kmax), so that pass
+    // histograms the rounds inside the row without a test.
     int shift = (kmin == kmax) ? 0 : 32 - __clz(kmin ^ kmax);
     uint32_t prefix = shift >= 32 ? 0u : (kmax >> shift);
     uint32_t k_rem = (uint32_t)k;                    // still to take among the candidates
     bool ranked = false;                             // threshold bin resolved by ranking its keys
     bool whole = false;                              // the k-th key's bin is taken whole
+    bool first = true;
     int hb = 0;                                      // histogram buffer of this pass
     while (shift > 0) {
         const int width = min(HIST_BITS, shift);
@@ -244,20 +273,28 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         const uint32_t mask = (1u << width) - 1u;
         const int nb = 1 << width;
         uint32_t (*H)[HIST_BINS] = &hist[hb * NH];
-        if (NHB == 1) {                              // one buffer: zero it now
+        if (NHB == 1 && !first) {                    // one buffer: zero it now
             for (int b = tid; b < nb * NH; b += NT) H[b / nb][b % nb] = 0u;
             __syncthreads();
         }
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
+            for (int j = 0; j < NR; ++j) {
+                if (!round_live(blk, j)) continue;
+                uint32_t* Hw = &H[NH > 1 ? wv : 0][0];
+                if (first && MODE != TOPK_GATHER && round_full(blk, j)) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t kk = key[4 * j + e];
-                    if (shift >= 32 || (kk >> shift) == prefix)
-                        atomicAdd(&H[NH > 1 ? wv : 0][(kk >> sh_lo) & mask], 1u);
+                    for (int e = 0; e < 4; ++e) atomicAdd(&Hw[(key[4 * j + e] >> sh_lo) & mask], 1u);
+                } else {
+                    // key-0 slots are never counted (they would all hit one bin)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t kk = key[4 * j + e];
+                        if (kk != 0u && (first || (kk >> shift) == prefix)) atomicAdd(&Hw[(kk >> sh_lo) & mask], 1u);
+                    }
                 }
+            }
         }
         __syncthreads();
         if (NHB == 2) {                              // the next pass's buffer (last read two passes ago)
@@ -267,7 +304,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         // Bin b with above(b) < k_rem <= above(b) + count(b), above = count in higher bins.
         // Thread t holds bins 2047 - (BPT*t + j) (descending), so above is a prefix sum.
         constexpr int BPT = (HIST_BINS + NT - 1) / NT;
-        const bool drop_pad = n_pad != 0u && (shift >= 32 || prefix == 0u);   // key-0 slots sit in bin 0
+
         uint32_t local = 0, hv[BPT];
 #pragma unroll
         for (int j = 0; j < BPT; ++j) {
@@ -276,7 +313,6 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
             if (b >= 0 && b < nb) {
 #pragma unroll
                 for (int w = 0; w < NH; ++w) c += H[w][b];
-                if (b == 0 && drop_pad) c -= n_pad;
             }
             hv[j] = c;
             local += c;
@@ -305,25 +341,77 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
         k_rem -= fa;
         shift = sh_lo;
         hb ^= NHB - 1;
+        first = false;
         if (in_bin == k_rem) {                       // the whole bin is taken: no ties to cut
             whole = true;
             break;
         }
-        if (STREAM && in_bin <= (uint32_t)CAND_CAP) {   // few keys share the k-th key's bin: rank them
+        if (in_bin <= (uint32_t)CAND_CAP) {          // few keys share the k-th key's bin: rank them
             ranked = true;
             break;
         }
     }
 
-    if (STREAM && ranked) {
+    // The selected positions are ranked into LDS (the histograms are no longer needed)
+    // and written out with coalesced stores at the end.
+    int32_t* ostage = reinterpret_cast<int32_t*>(&hist[0][0]);
+    uint32_t pos_run = 0;
+    // Emit in index order the keys that sel(key, position) picks: per block, wave counts
+    // from ballots, a prefix over the waves, then ranks within the wave from ballots.
+    auto emit = [&](auto&& sel_fn) {
+        for (int blk = 0; blk < nblocks; ++blk) {
+            if (STREAM) load_block(blk);
+            const int b0 = blk * BLOCK + lane_base;
+            uint32_t wcount = 0;
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                if (!round_live(blk, j)) continue;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    wcount += (uint32_t)__popcll(__ballot(sel_fn(key[4 * j + e], b0 + 256 * j + e)));
+            }
+            uint32_t sel_tot;
+            uint32_t pos = pos_run + waves_scan<NT>(wcount, wtot, &sel_tot);
+#pragma unroll
+            for (int j = 0; j < NR; ++j) {
+                if (!round_live(blk, j)) continue;
+                bool sel[4];
+                uint32_t before = 0, tot = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    sel[e] = sel_fn(key[4 * j + e], b0 + 256 * j + e);
+                    const uint64_t b = __ballot(sel[e]);
+                    before += lanes_below(b);
+                    tot += (uint32_t)__popcll(b);
+                }
+                uint32_t r = pos + before;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    if (sel[e]) {
+                        if (r < (uint32_t)k) {
+                            ostage[r] = out_pos(b0 + 256 * j + e);
+                            if (MODE == TOPK_SEGS) okey[r] = key[4 * j + e];
+                        }
+                        ++r;
+                    }
+                }
+                pos += tot;
+            }
+            pos_run += sel_tot;
+        }
+    };
+
+    if (ranked) {
         // Gather the bin's keys (with their positions) into LDS and find the k_rem-th of
-        // them in (key descending, position ascending) order: the exact threshold pair.
+        // them in (key descending, position ascending) order: the exact threshold pair,
+        // and how many keys share its value.
         if (tid == 0) ncand = 0u;
         __syncthreads();
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
+            for (int j = 0; j < NR; ++j) {
+                if (!round_live(blk, j)) continue;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t kk = key[4 * j + e];
@@ -335,144 +423,104 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                         }
                     }
                 }
+            }
         }
         __syncthreads();
         const int nc = (int)min(ncand, (uint32_t)CAND_CAP);
+        // Pad the list to a multiple of 16 with key 0 (below and unequal to every real key),
+        // so the ranking reads 16 candidates per step with vector LDS loads.
+        const int ncp = (nc + 15) & ~15;
+        for (int c = nc + tid; c < ncp; c += NT) { cand_key[c] = 0u; cand_idx[c] = INT32_MAX; }
+        __syncthreads();
         for (int c = tid; c < nc; c += NT) {
             const uint32_t ck = cand_key[c];
             const int32_t ci = cand_idx[c];
-            uint32_t rank = 0;
-            for (int o = 0; o < nc; ++o) {
-                const uint32_t ok = cand_key[o];
-                rank += (ok > ck) || (ok == ck && cand_idx[o] < ci);
+            uint32_t rank = 0, same = 0;
+            for (int o = 0; o < ncp; o += 16) {
+                uint4 ok[4];
+                int4 oi[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    ok[u] = *reinterpret_cast<const uint4*>(&cand_key[o + 4 * u]);
+                    oi[u] = *reinterpret_cast<const int4*>(&cand_idx[o + 4 * u]);
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t kq[4] = {ok[u].x, ok[u].y, ok[u].z, ok[u].w};
+                    const int32_t iq[4] = {oi[u].x, oi[u].y, oi[u].z, oi[u].w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        rank += (kq[e] > ck) || (kq[e] == ck && iq[e] < ci);
+                        same += kq[e] == ck;
+                    }
+                }
             }
-            if (rank == k_rem - 1u) { thr_key = ck; thr_idx = ci; }
+            if (rank == k_rem - 1u) { thr_key = ck; thr_idx = ci; thr_ties = same; }
         }
         __syncthreads();
         const uint32_t tk = thr_key;
         const int32_t ti = thr_idx;
-        // Emit in index order: every key above the threshold pair.
-        uint32_t pos_run = 0;
-        for (int blk = 0; blk < nblocks; ++blk) {
-            if (STREAM) load_block(blk);
-            const int b0 = blk * BLOCK + lane_base;
-            uint32_t selc = 0;
+        if (thr_ties == 1u)                          // the threshold value is unique: a key test suffices
+            emit([&](uint32_t kk, int) { return kk >= tk; });
+        else
+            emit([&](uint32_t kk, int p) { return (kk > tk) || (kk == tk && p <= ti); });
+    } else {
+        // Digit above the prefix -> selected; equal -> the first k_rem of them in index
+        // order (all of them when the bin is taken whole).  Empty candidate slots (key 0)
+        // sit anywhere in a candidate list, so they never count as equal (key 0 is never
+        // above the prefix either).
+        auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
+        auto is_eq = [&](uint32_t kk) -> bool { return digit(kk) == prefix && (MODE != TOPK_GATHER || kk != 0u); };
+        if (whole) {
+            emit([&](uint32_t kk, int) { return digit(kk) > prefix || is_eq(kk); });
+        } else {
+            // the k_rem-th equal key in index order is the last one taken: find its position
+            // (per block: wave counts of equal keys, a prefix over the waves, ballot ranks)
+            if (tid == 0) thr_idx = INT32_MAX;
+            uint32_t eq_run = 0;
+            for (int blk = 0; blk < nblocks; ++blk) {
+                if (STREAM) load_block(blk);
+                const int b0 = blk * BLOCK + lane_base;
+                uint32_t wcount = 0;
 #pragma unroll
-            for (int j = 0; j < NR; ++j)
+                for (int j = 0; j < NR; ++j) {
+                    if (!round_live(blk, j)) continue;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t kk = key[4 * j + e];
-                    selc += (kk > tk) || (kk == tk && b0 + 256 * j + e <= ti);
+                    for (int e = 0; e < 4; ++e) wcount += (uint32_t)__popcll(__ballot(is_eq(key[4 * j + e])));
                 }
-            uint32_t sel_tot;
-            uint32_t pos = pos_run + waves_scan<NT>(wave_sum(selc), wtot, &sel_tot);
+                uint32_t eq_tot;
+                uint32_t r = eq_run + waves_scan<NT>(wcount, wtot, &eq_tot);
 #pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                bool sel[4];
-                uint32_t before = 0, tot = 0;
+                for (int j = 0; j < NR; ++j) {
+                    if (!round_live(blk, j)) continue;
+                    bool eq[4];
+                    uint32_t before = 0, tot = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const uint32_t kk = key[4 * j + e];
-                    sel[e] = (kk > tk) || (kk == tk && b0 + 256 * j + e <= ti);
-                    const uint64_t b = __ballot(sel[e]);
-                    before += lanes_below(b);
-                    tot += (uint32_t)__popcll(b);
-                }
-                uint32_t r = pos + before;
+                    for (int e = 0; e < 4; ++e) {
+                        eq[e] = is_eq(key[4 * j + e]);
+                        const uint64_t b = __ballot(eq[e]);
+                        before += lanes_below(b);
+                        tot += (uint32_t)__popcll(b);
+                    }
+                    uint32_t q = r + before;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (sel[e]) {
-                        if (r < (uint32_t)k) {
-                            out[r] = out_pos(b0 + 256 * j + e);
-                            if (MODE == TOPK_SEGS) okey[r] = key[4 * j + e];
+                    for (int e = 0; e < 4; ++e) {
+                        if (eq[e]) {
+                            if (q == k_rem - 1u) thr_idx = b0 + 256 * j + e;
+                            ++q;
                         }
-                        ++r;
                     }
+                    r += tot;
                 }
-                pos += tot;
+                eq_run += eq_tot;
             }
-            pos_run += sel_tot;
+            __syncthreads();
+            const int32_t ti = thr_idx;
+            emit([&](uint32_t kk, int p) { return digit(kk) > prefix || (is_eq(kk) && p <= ti); });
         }
-        return;
     }
-
-    // Emit in index order: digit above the prefix -> selected; equal -> the first k_rem of them
-    // (all of them when the bin is taken whole, which skips the equal-key count scan).
-    // Empty candidate slots (key 0) sit anywhere in a candidate list, so they never count as
-    // equal (key 0 is never above the prefix either).
-    auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
-    auto is_eq = [&](uint32_t kk) -> bool { return digit(kk) == prefix && (MODE != TOPK_GATHER || kk != 0u); };
-    uint32_t eq_run = 0, pos_run = 0;                // totals of earlier blocks
-    for (int blk = 0; blk < nblocks; ++blk) {
-        if (STREAM) load_block(blk);
-        uint32_t eq_tot = 0, eq_rank = eq_run;
-        if (!whole) {
-            uint32_t eqc = 0;
-#pragma unroll
-            for (int j = 0; j < NR; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) eqc += is_eq(key[4 * j + e]);
-            eq_rank = eq_run + waves_scan<NT>(wave_sum(eqc), wtot, &eq_tot);
-        }
-        uint32_t selbits[(EPT + 31) / 32];
-#pragma unroll
-        for (int w = 0; w < (EPT + 31) / 32; ++w) selbits[w] = 0u;
-        uint32_t selc = 0;
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            bool eq[4], gt[4];
-            uint32_t before = 0, tot = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t dg = digit(key[4 * j + e]);
-                eq[e] = is_eq(key[4 * j + e]);
-                gt[e] = dg > prefix;
-                const uint64_t b = __ballot(eq[e]);
-                before += lanes_below(b);
-                tot += (uint32_t)__popcll(b);
-            }
-            uint32_t r = eq_rank + before;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const bool sel = gt[e] || (eq[e] && (whole || r < k_rem));
-                r += eq[e];
-                if (sel) {
-                    selbits[(4 * j + e) >> 5] |= 1u << ((4 * j + e) & 31);
-                    ++selc;
-                }
-            }
-            eq_rank += tot;
-        }
-        uint32_t sel_tot;
-        uint32_t pos = pos_run + waves_scan<NT>(wave_sum(selc), wtot, &sel_tot);
-        const int b0 = blk * BLOCK + lane_base;
-#pragma unroll
-        for (int j = 0; j < NR; ++j) {
-            bool sel[4];
-            uint32_t before = 0, tot = 0;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                sel[e] = (selbits[(4 * j + e) >> 5] >> ((4 * j + e) & 31)) & 1u;
-                const uint64_t b = __ballot(sel[e]);
-                before += lanes_below(b);
-                tot += (uint32_t)__popcll(b);
-            }
-            uint32_t r = pos + before;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                if (sel[e]) {
-                    if (r < (uint32_t)k) {
-                        out[r] = out_pos(b0 + 256 * j + e);
-                        if (MODE == TOPK_SEGS) okey[r] = key[4 * j + e];
-                    }
-                    ++r;
-                }
-            }
-            pos += tot;
-        }
-        eq_run += eq_tot;
-        pos_run += sel_tot;
-    }
+    __syncthreads();
+    for (int i = tid; i < k; i += NT) out[i] = ostage[i];
 }
 
 // One launch of `rows` workgroups; `len` bounds what one workgroup ranks (the row, a
