@@ -117,6 +117,14 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int per = ((k + nsplit - 1) / nsplit + KT - 1) / KT * KT;
     const int j_begin = sp * per;
     const int j_end = min(k, j_begin + per);
+    // A step's idx entries, raw: they are first used at that step's issue.  Loads
+    // complete in order, so each step's entries are fetched before the row loads of the
+    // step issued just ahead of it; its issue then never waits for those rows.
+    auto load_idx = [&](int j0) -> int {
+        const int jl = j0 + (lane & 31);
+        return (jl < j_end && lane < 32) ? irow[jl] : -1;
+    };
+    int idxA = load_idx(j_begin), idxB = load_idx(j_begin + KT);   // in flight with the scan below
     // Only the steps up to the last entry that names a row are run (an idx row padded
     // with -1 because fewer than k keys are visible costs only its real steps).
     int j_last = -1;
@@ -147,8 +155,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};   // bf16 1.0 pairs
 
     // One step of KT selected rows.  Loads of step t+1 are issued before step t is
-    // computed (two register sets, A and B), and the idx entries of a step are fetched
-    // one step before its loads.  Every step issues its loads and is computed (entries
+    // computed (two register sets, A and B, both possibly in flight), and the idx
+    // entries of a step are fetched two steps ahead.  Every step issues its loads and is computed (entries
     // of -1 read a real row and are masked), so no branch separates a load from its
     // use and the compiler's in-order load counting stays exact.
     struct Tile {
@@ -156,13 +164,6 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         i32x4 kf[ROWS ? 1 : 2][G::NDC];                      // !ROWS: K fragments, keys 16*kt + m
         i32x4 vst[ROWS ? 1 : G::VPL];                        // !ROWS: V rows, staged for LDS
         uint32_t valid;                                      // bit e: entry e of the step is a row
-    };
-    // The raw entry only: it is first used at the next issue, so the wait for this load
-    // lands there and not right behind the row loads issued just before it (loads
-    // complete in order, so an early use would wait for those rows too).
-    auto load_idx = [&](int j0) -> int {
-        const int jl = j0 + (lane & 31);
-        return (jl < j_end && lane < 32) ? irow[jl] : -1;
     };
     auto issue = [&](Tile& T, int raw_idx) {
         // Nothing of an issue may be scheduled into the previous compute: its first use of
@@ -294,15 +295,14 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 
     Tile TA, TB;
     if (nsteps > 0) {
-        issue(TA, load_idx(j_begin));
-        int idxA, idxB = load_idx(j_begin + KT);
+        issue(TA, idxA);
         int t = 0;
         for (; t + 2 < nsteps; t += 2) {                     // both issues unconditional
-            issue(TB, idxB);
             idxA = load_idx(j_begin + (t + 2) * KT);
+            issue(TB, idxB);                                 // TA's rows may still be in flight
             compute(TA);
-            issue(TA, idxA);
             idxB = load_idx(j_begin + (t + 3) * KT);
+            issue(TA, idxA);                                 // TB's rows may still be in flight
             compute(TB);
         }
         if (t + 1 < nsteps) {                                // last two steps
