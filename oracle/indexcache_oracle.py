@@ -45,7 +45,12 @@ design notes):
     precision the GPU kernel decides in (the pages fix none);
   * sparse attention is softmax(q . K / sqrt(d)) V over the selected rows,
     one shared KV head, K and V stored as one [K | V] row per token;
-  * decode appends the new token first, so its query sees itself.
+  * decode appends the new token first, so its query sees itself;
+  * the distillation loss of an F layer is KL(target || softmax of its
+    indexer scores) per query, in nats, taken over the query's selected
+    entries (the dense loss is the case where every visible key is
+    selected); the target averages the attention distributions of every
+    served layer (the F layer and its S layers) and head with equal weight.
 
 Parity of every function here is pinned by tests that do not reuse this code
 (hand-worked examples, closed forms, brute force, library special cases);
@@ -271,3 +276,72 @@ def jaccard_rows(idx_a: np.ndarray, idx_b: np.ndarray) -> np.ndarray:
         sb = set(int(x) for x in b[r] if x >= 0)
         out[r] = len(sa & sb) / (len(sa | sb) + 1e-8)
     return out.reshape(idx_a.shape[:-1])
+
+
+# ---------------------------------------------------------------------------
+# Multi-layer distillation loss, forward only
+#   [Abstract: each retained indexer is trained against the averaged attention
+#    distributions of all the layers it serves; Blog, "training-aware" variant;
+#    Gist, Methodologie (an F layer predicts its own and its S layers'
+#    attention, with a KL divergence to their average)]
+# ---------------------------------------------------------------------------
+
+def served_attention_row(qs_t: Sequence[np.ndarray], kvs: Sequence[np.ndarray], idx_t: np.ndarray,
+                         scale: float) -> np.ndarray:
+    """Target distribution of one query over its selected entries.
+
+    qs_t: per served layer, q_t [H, d]; kvs: per served layer, kv [Lk, 2, d];
+    idx_t [k] (-1 = unused).  For every served layer and head, the attention
+    probabilities softmax(scale * q_t[h] . K[s]) over the selected keys; the
+    target is their plain average over layers and heads.  Returns one value
+    per entry idx_t >= 0, in entry order (float64, summing to 1).
+    """
+    sel = idx_t[idx_t >= 0]
+    total = np.zeros(sel.shape[0])
+    count = 0
+    for q_t, kv in zip(qs_t, kvs):
+        logits = scale * (q_t @ kv[sel, 0, :].T)          # [H, m]
+        logits = logits - logits.max(axis=1, keepdims=True)
+        a = np.exp(logits)
+        a = a / a.sum(axis=1, keepdims=True)              # each head's distribution
+        total += a.sum(axis=0)
+        count += a.shape[0]
+    return total / count
+
+
+def distill_kl_row(I_t: np.ndarray, qs_t: Sequence[np.ndarray], kvs: Sequence[np.ndarray],
+                   idx_t: np.ndarray, scale: float) -> float:
+    """KL(target || softmax of the indexer scores) for one query, in nats.
+
+    I_t: the F layer's indexer scores of this query over its visible keys
+    (I_t[s] for key s); the indexer's distribution is the softmax of those
+    scores over the selected entries.  Entries with zero target mass add 0.
+    """
+    sel = idx_t[idx_t >= 0]
+    p = served_attention_row(qs_t, kvs, idx_t, scale)
+    z = np.asarray(I_t, dtype=np.float64)[sel]
+    log_r = z - z.max()
+    log_r = log_r - math.log(np.exp(log_r).sum())
+    nz = p > 0
+    return float(np.sum(p[nz] * (np.log(p[nz]) - log_r[nz])))
+
+
+def distill_kl(q_I: np.ndarray, w: np.ndarray, k_I: np.ndarray, idx: np.ndarray,
+               qs: Sequence[np.ndarray], kvs: Sequence[np.ndarray], pos0: int = 0, scale: float = None,
+               rows: Sequence[int] = None) -> np.ndarray:
+    """Per-query loss of one F layer and the layers it serves (itself first).
+
+    q_I [Lq, H_I, d_I], w [Lq, H_I], k_I [Lk, d_I]: the F layer's indexer
+    inputs; idx [Lq, k]: the entries the loss is taken over (the F layer's
+    top-k; the dense loss is the case of every visible key); qs[j] [Lq, H, d]
+    and kvs[j] [Lk, 2, d]: the served layers.  Query t sits at position
+    pos0 + t.  Returns [len(rows)] float64 (all queries when rows is None).
+    """
+    d = qs[0].shape[-1]
+    scale = 1.0 / math.sqrt(d) if scale is None else scale
+    rows = range(q_I.shape[0]) if rows is None else rows
+    out = []
+    for t in rows:
+        I_t = indexer_scores_row(q_I[t], w[t], k_I, pos0 + t)
+        out.append(distill_kl_row(I_t, [q[t] for q in qs], kvs, idx[t], scale))
+    return np.array(out)

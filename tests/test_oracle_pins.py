@@ -337,3 +337,101 @@ def test_attention_extreme_logits_stay_finite():
     out = O.sparse_attn_row(q, kv, np.array([0, 1], dtype=np.int32), 1.0)
     e = math.e
     np.testing.assert_allclose(out, [[e / (1 + e), 1 / (1 + e)]] * 2, rtol=1e-13)
+
+
+# ------------------------------------------------- distillation loss (fwd) --
+
+def test_distill_two_entry_closed_form():
+    """Closed form: one served layer, one head, two selected keys.  The target
+    is a logistic pair sigma(delta), the indexer distribution sigma(eps), and
+    KL = p0 ln(p0/r0) + p1 ln(p1/r1) (natural log), written out by hand."""
+    d = 4
+    q = np.array([[0.5, -1.0, 2.0, 0.25]])                   # [H=1, d]
+    kv = np.zeros((3, 2, d))
+    kv[0, 0] = [1.0, 0.0, 0.5, -2.0]
+    kv[2, 0] = [-0.5, 1.0, 1.0, 4.0]
+    idx = np.array([2, -1, 0], dtype=np.int32)               # entries: key 2 first, a hole, key 0
+    scale = 1.0 / math.sqrt(d)
+    I_t = np.array([3.0, 99.0, 1.25])                        # scores of keys 0..2 (key 1 unselected)
+    dot0 = float(q[0] @ kv[0, 0]); dot2 = float(q[0] @ kv[2, 0])
+    p_key2 = 1.0 / (1.0 + math.exp(-scale * (dot2 - dot0)))
+    r_key2 = 1.0 / (1.0 + math.exp(-(1.25 - 3.0)))
+    want = p_key2 * math.log(p_key2 / r_key2) + (1 - p_key2) * math.log((1 - p_key2) / (1 - r_key2))
+    got = O.distill_kl_row(I_t, [q], [kv], idx, scale)
+    assert abs(got - want) < 1e-12
+    p = O.served_attention_row([q], [kv], idx, scale)
+    assert abs(p[0] - p_key2) < 1e-12 and abs(p.sum() - 1.0) < 1e-12
+
+
+def test_distill_gibbs_and_library_kl():
+    """Gibbs' inequality (KL >= 0, = 0 iff the distributions agree) and torch's
+    kl_div (a separate implementation of the same divergence)."""
+    rng = np.random.default_rng(7)
+    H, d, Lk, k = 3, 8, 40, 12
+    qs = [rng.normal(size=(H, d)) for _ in range(3)]
+    kvs = [rng.normal(size=(Lk, 2, d)) for _ in range(3)]
+    idx = np.full(k, -1, dtype=np.int32)
+    idx[:9] = rng.permutation(Lk)[:9]
+    scale = 0.3
+    I_t = rng.normal(size=Lk) * 4
+    kl = O.distill_kl_row(I_t, qs, kvs, idx, scale)
+    assert kl > 0
+    p = O.served_attention_row(qs, kvs, idx, scale)
+    sel = idx[idx >= 0]
+    log_r = torch.log_softmax(torch.from_numpy(I_t[sel]), dim=0)
+    lib = torch.nn.functional.kl_div(log_r, torch.from_numpy(p), reduction="sum").item()
+    assert abs(kl - lib) < 1e-10
+    matched = np.full(Lk, -50.0)
+    matched[sel] = np.log(p) + 7.0                           # indexer distribution == target
+    assert abs(O.distill_kl_row(matched, qs, kvs, idx, scale)) < 1e-12
+
+
+def test_distill_invariances():
+    """Shifting every indexer score leaves the loss alone; so do permuting the
+    entries, moving the -1 holes, and serving the same layer twice; scaling the
+    logits changes it."""
+    rng = np.random.default_rng(11)
+    H, d, Lk = 2, 6, 30
+    q = rng.normal(size=(H, d)); kv = rng.normal(size=(Lk, 2, d))
+    q2 = rng.normal(size=(H, d)); kv2 = rng.normal(size=(Lk, 2, d))
+    sel = rng.permutation(Lk)[:10].astype(np.int32)
+    idx = np.concatenate([sel[:4], [-1, -1], sel[4:]]).astype(np.int32)
+    I_t = rng.normal(size=Lk) * 3
+    base = O.distill_kl_row(I_t, [q, q2], [kv, kv2], idx, 0.4)
+    assert abs(O.distill_kl_row(I_t + 123.0, [q, q2], [kv, kv2], idx, 0.4) - base) < 1e-9
+    perm = np.concatenate([sel[::-1], [-1, -1]]).astype(np.int32)
+    assert abs(O.distill_kl_row(I_t, [q, q2], [kv, kv2], perm, 0.4) - base) < 1e-12
+    one = O.served_attention_row([q], [kv], idx, 0.4)
+    twice = O.served_attention_row([q, q], [kv, kv], idx, 0.4)
+    assert np.allclose(one, twice, atol=1e-15)
+    both = O.served_attention_row([q, q2], [kv, kv2], idx, 0.4)
+    assert np.allclose(both, 0.5 * (one + O.served_attention_row([q2], [kv2], idx, 0.4)), atol=1e-15)
+    assert abs(O.distill_kl_row(2.0 * I_t, [q, q2], [kv, kv2], idx, 0.4) - base) > 1e-3
+
+
+def test_distill_dense_case_is_causal_softmax_attention_weights():
+    """Every visible key selected: the target is the head-mean of the causal
+    softmax(Q K^T / sqrt(d)) rows, computed here with torch's masked softmax."""
+    rng = np.random.default_rng(3)
+    L, H, d, H_I, d_I = 9, 2, 4, 2, 3
+    q = rng.normal(size=(L, H, d)); kv = rng.normal(size=(L, 2, d))
+    q_I = rng.normal(size=(L, H_I, d_I)); w = rng.uniform(size=(L, H_I)); k_I = rng.normal(size=(L, d_I))
+    idx = np.full((L, L), -1, dtype=np.int32)
+    for t in range(L):
+        idx[t, : t + 1] = np.arange(t + 1)
+    Q = torch.from_numpy(q).permute(1, 0, 2)                 # [H, L, d]
+    K = torch.from_numpy(kv[:, 0]).expand(H, L, d)
+    att = (Q @ K.transpose(1, 2)) / math.sqrt(d)
+    att = att.masked_fill(torch.triu(torch.ones(L, L, dtype=torch.bool), 1), float("-inf"))
+    target = torch.softmax(att, dim=-1).mean(0).numpy()       # [L, L]
+    y = np.einsum("thc,sc->ths", q_I, k_I)
+    I_full = np.einsum("th,ths->ts", w, np.maximum(y, 0.0))
+    for t in range(L):
+        p = O.served_attention_row([q[t]], [kv], idx[t], 1 / math.sqrt(d))
+        assert np.allclose(p, target[t, : t + 1], atol=1e-12)
+    kl = O.distill_kl(q_I, w, k_I, idx, [q], [kv])
+    for t in range(L):
+        r = np.exp(I_full[t, : t + 1] - I_full[t, : t + 1].max())
+        r /= r.sum()
+        want = float(np.sum(target[t, : t + 1] * np.log(target[t, : t + 1] / r)))
+        assert abs(kl[t] - want) < 1e-10
