@@ -84,7 +84,7 @@ def parse():
     p.add_argument("--no-allf", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=640)
-    p.add_argument("--only", choices=["indexer", "topk", "attention", "decode", "copy"], default=None,
+    p.add_argument("--only", choices=["indexer", "topk", "attention", "distill", "decode", "copy"], default=None,
                    help="run just one kernel of the path a few times (for profiler counter runs)")
     p.add_argument("--reps", type=int, default=3)
     return p.parse_args()
@@ -110,7 +110,7 @@ def only_kernel(which: str, reps: int):
     elif which == "decode":
         info.update(bench_decode(4, warm=1))
     else:
-        layers = synth.prefill_stack(cfg, device="cuda", pattern="FS")
+        layers = synth.prefill_stack(cfg, device="cuda", pattern="FSSS" if which == "distill" else "FS")
         f = layers[0]
         scores = torch.empty((1, L, L), dtype=torch.float32, device="cuda")
         ic.indexer_scores(f["q_I"], f["w"], f["k_I"], scores=scores, row_stride=L)
@@ -128,6 +128,11 @@ def only_kernel(which: str, reps: int):
             o = torch.empty_like(layers[1]["q"])
             for _ in range(reps):
                 ic.sparse_attn(layers[1]["q"], layers[1]["kv"], idx.view(1, L, k), out=o)
+        if which == "distill":
+            del scores
+            for _ in range(reps):
+                ic.distill_kl(f["q_I"], f["w"], f["k_I"], idx.view(1, L, k), [l["q"] for l in layers],
+                              [l["kv"] for l in layers], chunk=cfg.chunk)
     torch.cuda.synchronize()
     print(json.dumps(info), flush=True)
 
@@ -199,6 +204,26 @@ def kernel_rooflines(cfg, layers, ws):
     out["attention"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
                         "work": f"{by:.4g} B = 512 B per selected [K|V] row x {rows} rows + q, out, idx"}
+    # NEXT-3: distillation loss forward of the first F layer serving itself and its three S layers
+    # (the call recomputes the indexer scores in the stack's tiles; the loss kernel's own time is
+    # the call minus those indexer launches, timed above as chunked_ms)
+    if len(layers) >= 4:
+        served = layers[:4]
+        kl = torch.empty((1, L), dtype=torch.float32, device="cuda")
+        mean = torch.empty(1, dtype=torch.float32, device="cuda")
+        run = lambda: ic.distill_kl(f["q_I"], f["w"], f["k_I"], idx3, [l["q"] for l in served],
+                                    [l["kv"] for l in served], chunk=cfg.chunk, kl=kl, mean=mean)
+        run()
+        ms_call = timed_events(run, 3)
+        ms_k = max(ms_call - out["indexer"]["chunked_ms"], 1e-6)
+        by = 256.0 * rows * len(served) + L * (len(served) * cfg.H * cfg.d * 2 + 4 * k + 4 * k + 4)
+        gbs = by / (ms_k * 1e-3) / 1e9
+        out["distill"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                          "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms_k, 4), "call_ms": round(ms_call, 4),
+                          "served_layers": len(served), "loss_mean_nats": round(float(mean.item()), 4),
+                          "work": f"{by:.4g} B = 256 B K per (selected row, served layer) x {rows} rows x "
+                                  f"{len(served)} + q, idx, scores, kl (read twice: two sweeps)",
+                          "method": "call minus the indexer's tiled launches"}
     return out
 
 

@@ -31,6 +31,7 @@ IC_ERR_NO_CACHED_INDICES, IC_ERR_WORKSPACE, IC_ERR_HIP = 5, 6, 7
 IC_BF16, IC_FP8_E4M3 = 0, 1
 IC_OP_INDEXER_TOPK, IC_OP_SPARSE_ATTN, IC_OP_RUN_STACK, IC_OP_DECODE_STEP, IC_OP_INDEXER_SCORES = 0, 1, 2, 3, 4
 IC_OP_RUN_STACK_VARLEN = 5
+IC_OP_DISTILL_KL = 6
 
 
 class Shape(ctypes.Structure):
@@ -85,13 +86,14 @@ def lib() -> ctypes.CDLL:
     L.ic_run_stack_varlen.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), P(ctypes.c_int32), P(ctypes.c_int32),
                                       vp, vp, sz, P(Stats), vp]
     L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
+    L.ic_distill_kl.argtypes = [P(Shape), vp, vp, vp, vp, i32, P(vp), P(vp), vp, vp, vp, sz, vp]
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
     for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
-               "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen",
+               "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen", "ic_distill_kl",
                "ic_decode_step", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -269,6 +271,39 @@ def sparse_attn(q, kv, idx, out=None, stream=None):
         out = torch.empty_like(q)
     _check(lib().ic_sparse_attn(ctypes.byref(s), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), None, 0, _stream(stream)))
     return out
+
+
+def distill_kl(q_I, w, k_I, idx, qs: Sequence[torch.Tensor], kvs: Sequence[torch.Tensor], pos0: int = 0,
+               chunk: int = 0, kl=None, mean=None, ws=None, stream=None):
+    """Multi-layer distillation loss (forward) of one F layer and the layers it serves.
+
+    q_I, w, k_I: the F layer's indexer inputs; idx [B, Lq, k] int32: the entries the
+    loss is taken over; qs[j] [B, Lq, H, d] and kvs[j] [B, Lk, 2, d] bf16: the served
+    layers, the F layer first.  Returns (kl [B, Lq] fp32 in nats, mean [1] fp32)."""
+    if len(qs) != len(kvs) or not 1 <= len(qs) <= 16:
+        raise ValueError("qs and kvs must list the same 1..16 served layers")
+    _need(idx, "idx", (torch.int32,), 3)
+    B, Lq = q_I.shape[:2]
+    H, d = qs[0].shape[2], qs[0].shape[3]
+    for q, kv in zip(qs, kvs):
+        _need(q, "q", (torch.bfloat16,), 4)
+        _need(kv, "kv", (torch.bfloat16,), 4)
+        if tuple(q.shape) != (B, Lq, H, d) or tuple(kv.shape) != (B, k_I.shape[1], 2, d):
+            raise ValueError(f"served layer shapes q {tuple(q.shape)}, kv {tuple(kv.shape)} do not match")
+    s = _indexer_shape(q_I, w, k_I, idx.shape[2], pos0, chunk, H=H, d=d)
+    if tuple(idx.shape[:2]) != (B, Lq):
+        raise ValueError("idx must be [B, Lq, k]")
+    dev = q_I.device
+    if kl is None:
+        kl = torch.empty((B, Lq), dtype=torch.float32, device=dev)
+    if mean is None:
+        mean = torch.empty(1, dtype=torch.float32, device=dev)
+    ws = _workspace(workspace_size(s, IC_OP_DISTILL_KL), dev, ws)
+    qa = (ctypes.c_void_p * len(qs))(*[q.data_ptr() for q in qs])
+    kva = (ctypes.c_void_p * len(kvs))(*[kv.data_ptr() for kv in kvs])
+    _check(lib().ic_distill_kl(ctypes.byref(s), _ptr(q_I), _ptr(w), _ptr(k_I), _ptr(idx), len(qs), qa, kva,
+                               _ptr(kl), _ptr(mean), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+    return kl, mean
 
 
 def _layers_struct(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], outs: List[torch.Tensor]):

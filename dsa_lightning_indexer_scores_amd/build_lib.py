@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libindexcache.so")
-SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "overlap.hip", "api.cpp"]
+SOURCES = ["indexer.hip", "topk.hip", "attn.hip", "overlap.hip", "distill.hip", "api.cpp"]
 # Measurement support for the benchmark (sustained MFMA rate); not linked into LIB.
 PROBE_LIB = os.path.join(PKG, "libicprobe.so")
 PROBE_SOURCES = ["mfma_probe.hip"]

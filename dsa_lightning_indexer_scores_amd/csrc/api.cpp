@@ -255,6 +255,9 @@ size_t ic_workspace_size(const ic_shape* shape, int op) {
         case IC_OP_DECODE_STEP:
             if (check_shape(shape, true, true) != IC_OK) return 0;
             return decode_ws(*shape);
+        case IC_OP_DISTILL_KL:
+            if (check_shape(shape, true, false) != IC_OK) return 0;
+            return indexer_ws(*shape);
         default:
             fail(IC_ERR_ARG, "unknown op %d", op);
             return 0;
@@ -536,6 +539,72 @@ ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t r
     if (means && (!jaccard || !recall)) return fail(IC_ERR_ARG, "means needs jaccard and recall");
     hipError_t e = launch_overlap(idx_a, idx_b, rows, k, inter, jaccard, recall, means, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "overlap launch");
+    return IC_OK;
+}
+
+ic_status ic_distill_kl(const ic_shape* shape, const void* q_I, const float* w, const void* k_I, const int32_t* idx,
+                        int32_t n_served, const void* const* q, const void* const* kv, float* kl, float* kl_mean,
+                        void* ws, size_t ws_bytes, void* stream) {
+    ic_status st = check_shape(shape, true, false);
+    if (st != IC_OK) return st;
+    const ic_shape& s = *shape;
+    if (!q_I || !w || !k_I || !idx || !kl) return fail(IC_ERR_ARG, "q_I, w, k_I, idx and kl must be non-NULL");
+    if (n_served < 1 || n_served > IC_DISTILL_MAX_SERVED)
+        return fail(IC_ERR_ARG, "n_served must be in 1..%d (got %d)", IC_DISTILL_MAX_SERVED, n_served);
+    if (!q || !kv) return fail(IC_ERR_ARG, "q and kv must be host arrays of n_served device pointers");
+    for (int j = 0; j < n_served; ++j)
+        if (!q[j] || !kv[j]) return fail(IC_ERR_ARG, "served layer %d has a NULL q or kv", j);
+    if ((st = check_ws(ws, ws_bytes, indexer_ws(s))) != IC_OK) return st;
+    hipStream_t hs = (hipStream_t)stream;
+    const size_t eb = elem_bytes(s.idx_dtype);
+    const int chunk = chunk_of(s);
+    float* tile = static_cast<float*>(ws);
+    for (int b = 0; b < s.B; ++b) {
+        const uint8_t* qb = static_cast<const uint8_t*>(q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
+        const float* wb = w + (size_t)b * s.Lq * s.H_I;
+        const uint8_t* kb = static_cast<const uint8_t*>(k_I) + (size_t)b * s.Lk * s.d_I * eb;
+        ic_distill_args d{};
+        d.idx = idx + (size_t)b * s.Lq * s.k;
+        for (int j = 0; j < n_served; ++j) {
+            d.q[j] = static_cast<const uint16_t*>(q[j]) + (size_t)b * s.Lq * s.H * s.d;
+            d.kv[j] = static_cast<const uint16_t*>(kv[j]) + (size_t)b * s.Lk * 2 * s.d;
+        }
+        d.kl = kl + (size_t)b * s.Lq;
+        d.pos0 = s.pos0;
+        d.Lk = s.Lk;
+        d.nserved = n_served;
+        d.H = s.H;
+        d.d = s.d;
+        d.k = s.k;
+        for (int c0 = 0; c0 < s.Lq; c0 += chunk) {
+            const int nq = std::min(chunk, s.Lq - c0);
+            const int64_t stride = round_up((int64_t)s.pos0 + c0 + nq, 4);
+            ic_indexer_args a;
+            a.q_I = qb;
+            a.w = wb;
+            a.k_I = kb;
+            a.scores = tile;
+            a.row_stride = stride;
+            a.q_begin = c0;
+            a.nq = nq;
+            a.pos_begin = s.pos0 + c0;
+            a.H_I = s.H_I;
+            a.d_I = s.d_I;
+            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+            hipError_t e = launch_indexer_prefill(a, hs);
+            if (e != hipSuccess) return hip_fail(e, "indexer launch");
+            d.scores = tile;
+            d.score_stride = stride;
+            d.q_begin = c0;
+            d.nrows = nq;
+            e = launch_distill(d, hs);
+            if (e != hipSuccess) return hip_fail(e, "distillation loss launch");
+        }
+    }
+    if (kl_mean) {
+        hipError_t e = launch_mean(kl, (int64_t)s.B * s.Lq, kl_mean, hs);
+        if (e != hipSuccess) return hip_fail(e, "mean launch");
+    }
     return IC_OK;
 }
 

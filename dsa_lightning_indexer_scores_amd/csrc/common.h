@@ -142,6 +142,22 @@ struct ic_attn_args {
 };
 hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st);
 
+// Multi-layer distillation loss (forward) of the queries of one score tile.
+constexpr int IC_DISTILL_MAX_K = 4096;
+constexpr int IC_DISTILL_MAX_SERVED = 16;
+struct ic_distill_args {
+    const float* scores;      // indexer score tile [nrows, score_stride]; row r = query q_begin + r, keys 0..pos
+    int64_t score_stride;
+    const int32_t* idx;       // [Lq, k] of this sequence: the entries the loss is taken over
+    const void* q[IC_DISTILL_MAX_SERVED];    // served layer j: [Lq, H, d] bf16 of this sequence
+    const void* kv[IC_DISTILL_MAX_SERVED];   // served layer j: [Lk, 2, d] bf16 of this sequence
+    float* kl;                // [Lq] of this sequence, nats
+    int32_t q_begin, nrows, pos0, Lk, nserved, H, d, k;
+};
+hipError_t launch_distill(const ic_distill_args& a, hipStream_t st);
+// Mean of n floats, summed in a fixed order (one workgroup).
+hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t st);
+
 // Per-row overlap of two index caches [rows, k] (rows ascending, -1 padded); means may be NULL.
 hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int64_t rows, int k, int32_t* inter, float* jac,
                           float* rec, float* means, hipStream_t st);

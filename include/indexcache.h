@@ -127,7 +127,8 @@ enum {
     IC_OP_RUN_STACK = 2,
     IC_OP_DECODE_STEP = 3,
     IC_OP_INDEXER_SCORES = 4,
-    IC_OP_RUN_STACK_VARLEN = 5
+    IC_OP_RUN_STACK_VARLEN = 5,
+    IC_OP_DISTILL_KL = 6
 };
 
 /* Bytes of workspace the operation needs for this shape (0 if none).
@@ -228,6 +229,29 @@ IC_API ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_
  * jaccard and recall.  All pointers are device pointers. */
 IC_API ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows, int32_t k,
                                   int32_t* inter, float* jaccard, float* recall, float* means, void* stream);
+
+/* Multi-layer distillation loss, forward only (arXiv abstract: training-aware
+ * IndexCache trains each retained indexer against the averaged attention
+ * distributions of all the layers it serves; gist.science summary,
+ * "Methodologie": a KL divergence to that average).  For one F layer and the
+ * n_served layers it serves (itself first, then its S layers; 1..16), per
+ * query t of sequence b, over its entries S_t = { idx[b,t,j] : 0 <= idx <=
+ * pos0 + t } (the F layer's top-k; listing every visible key gives the dense
+ * loss; other entries are ignored, and every row needs at least one):
+ *   p[s] = mean over the served layers and their H heads of
+ *          softmax over S_t of q[t,h] . K[s] / sqrt(d)
+ *   r[s] = softmax over S_t of the F layer's indexer scores I[t,s]
+ *   kl[b,t] = sum over S_t of p[s] (ln p[s] - ln r[s])      (nats, fp32)
+ * q_I [B,Lq,H_I,d_I], w [B,Lq,H_I], k_I [B,Lk,d_I]: the F layer's indexer
+ * inputs (shape.idx_dtype); idx [B,Lq,k] int32 (k <= 4096); q and kv: HOST
+ * arrays of n_served device pointers, q[j] [B,Lq,H,d] bf16 and kv[j]
+ * [B,Lk,2,d] bf16; kl [B,Lq] fp32 (device); kl_mean (device, 1 float, or
+ * NULL) receives the mean of kl over all B*Lq queries, summed in a fixed
+ * order.  The indexer scores are recomputed in tiles of shape.chunk queries
+ * into ws (ic_workspace_size(shape, IC_OP_DISTILL_KL) bytes). */
+IC_API ic_status ic_distill_kl(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+                               const int32_t* idx, int32_t n_served, const void* const* q, const void* const* kv,
+                               float* kl, float* kl_mean, void* ws, size_t ws_bytes, void* stream);
 
 /* Counters of the last stack call on this thread. */
 IC_API ic_status ic_get_stats(ic_stats* out);

@@ -158,3 +158,22 @@ def test_run_stack_varlen_validation(L):
     assert run("FS", s, ql, far) == 2                                     # pos0 + q_len beyond Lk
     s2 = _shape(B=2, Lq=30, Lk=100, pos0=5)
     assert run("FS", s2, ql, p0) == 2                                     # per-sequence pos0 only
+
+
+def test_distill_kl_validation(L):
+    s = _shape()
+    ptrs = (ctypes.c_void_p * 2)(FAKE, FAKE)
+    holes = (ctypes.c_void_p * 2)(FAKE, None)
+    ws = ctypes.c_void_p(0x10000)
+    need = ic.workspace_size(s, ic.IC_OP_DISTILL_KL)
+    assert need == ic.workspace_size(s, ic.IC_OP_INDEXER_TOPK) > 0     # one score tile
+    call = lambda shape, n, q, kv, kl=FAKE, wsb=1 << 30: L.ic_distill_kl(
+        ctypes.byref(shape), FAKE, FAKE, FAKE, FAKE, n, q, kv, kl, None, ws, wsb, None)
+    assert call(s, 0, ptrs, ptrs) == ic.IC_ERR_ARG                      # no served layer
+    assert call(s, 17, ptrs, ptrs) == ic.IC_ERR_ARG                     # more than 16
+    assert call(s, 2, None, ptrs) == ic.IC_ERR_ARG                      # host pointer arrays required
+    assert call(s, 2, ptrs, holes) == ic.IC_ERR_ARG                     # a NULL layer pointer
+    assert call(s, 2, ptrs, ptrs, kl=None) == ic.IC_ERR_ARG
+    assert call(_shape(d=96), 2, ptrs, ptrs) == ic.IC_ERR_SHAPE
+    assert call(_shape(idx_dtype=7), 2, ptrs, ptrs) == ic.IC_ERR_DTYPE
+    assert call(s, 2, ptrs, ptrs, wsb=16) == ic.IC_ERR_WORKSPACE
