@@ -50,7 +50,11 @@ design notes):
     indexer scores) per query, in nats, taken over the query's selected
     entries (the dense loss is the case where every visible key is
     selected); the target averages the attention distributions of every
-    served layer (the F layer and its S layers) and head with equal weight.
+    served layer (the F layer and its S layers) and head with equal weight;
+  * dynamic refresh: an S layer that keeps its indexer probes every
+    stride-th query (ending at the last), measures the pooled recall of its
+    own top-k within the cached rows, sum |cached & own| / sum |own|, and
+    re-indexes every query when that recall is below tau.
 
 Parity of every function here is pinned by tests that do not reuse this code
 (hand-worked examples, closed forms, brute force, library special cases);
@@ -345,3 +349,58 @@ def distill_kl(q_I: np.ndarray, w: np.ndarray, k_I: np.ndarray, idx: np.ndarray,
         I_t = indexer_scores_row(q_I[t], w[t], k_I, pos0 + t)
         out.append(distill_kl_row(I_t, [q[t] for q in qs], kvs, idx[t], scale))
     return np.array(out)
+
+
+# ---------------------------------------------------------------------------
+# Drift-triggered dynamic refresh
+#   [Blog, Conclusion: decide at runtime whether a layer's neighbour is still a
+#    good proxy and refresh only when the drift exceeds a threshold; Skill,
+#    Step 1: set overlap of the top-k selections as the similarity measure]
+# ---------------------------------------------------------------------------
+
+def probe_rows(Lq: int, stride: int) -> np.ndarray:
+    """Queries the drift probe looks at: every stride-th query, ending at the last one."""
+    return np.arange((Lq - 1) % stride, Lq, stride)
+
+
+def run_stack_dynamic(pattern: str, layers: Sequence[Dict[str, np.ndarray]], k: int, stride: int, tau: float,
+                      pos0: int = 0):
+    """Prefill through a stack whose S layers may refresh the index cache.
+
+    Layers as in run_stack.  An S layer that still holds its own indexer
+    inputs (q_I, w, k_I) first probes the cache: for the probe queries it
+    takes its own top-k and measures the pooled recall of that top-k within
+    the cached rows, sum |cached & own| / sum |own|.  When the recall is below
+    tau it runs its indexer and top-k for every query and overwrites the cache
+    (acting as an F layer); otherwise it reuses the cache.  S layers without
+    indexer inputs always reuse it.
+
+    Returns (outs, idx_per_layer, refreshed [n_layers] bool, recall [n_layers]
+    float64, nan where no probe ran).
+    """
+    if len(pattern) != len(layers):
+        raise ValueError("pattern length must equal the number of layers")
+    cache = None
+    outs, used = [], []
+    refreshed = np.zeros(len(layers), dtype=bool)
+    recall = np.full(len(layers), np.nan)
+    for l, (c, lay) in enumerate(zip(pattern, layers)):
+        if is_full(c):
+            cache = indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k, pos0)
+        elif cache is None:
+            raise NoCachedIndices("no cached indices: an S layer came before any F layer")
+        elif "q_I" in lay:
+            hit = own = 0
+            for t in probe_rows(lay["q_I"].shape[0], stride):
+                row = indexer_scores_row(lay["q_I"][t], lay["w"][t], lay["k_I"], pos0 + int(t))
+                mine = set(int(x) for x in topk_row(to_decision_precision(row), k) if x >= 0)
+                cached = set(int(x) for x in cache[t] if x >= 0)
+                hit += len(mine & cached)
+                own += len(mine)
+            recall[l] = hit / own
+            if hit < tau * own:
+                cache = indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k, pos0)
+                refreshed[l] = True
+        outs.append(sparse_attn(lay["q"], lay["kv"], cache))
+        used.append(cache)
+    return outs, used, refreshed, recall

@@ -435,3 +435,55 @@ def test_distill_dense_case_is_causal_softmax_attention_weights():
         r /= r.sum()
         want = float(np.sum(target[t, : t + 1] * np.log(target[t, : t + 1] / r)))
         assert abs(kl[t] - want) < 1e-10
+
+
+# ------------------------------------------------------ dynamic refresh --
+
+def test_probe_rows_end_at_the_last_query():
+    assert O.probe_rows(10, 4).tolist() == [1, 5, 9]
+    assert O.probe_rows(8, 1).tolist() == list(range(8))
+    assert O.probe_rows(5, 64).tolist() == [4]
+
+
+def _dyn_layers(L=12, H_I=2, d_I=3, H=1, d=4, seed=0, n=3):
+    rng = np.random.default_rng(seed)
+    return [dict(q=rng.normal(size=(L, H, d)), kv=rng.normal(size=(L, 2, d)),
+                 q_I=rng.normal(size=(L, H_I, d_I)), w=rng.uniform(size=(L, H_I)), k_I=rng.normal(size=(L, d_I)))
+            for _ in range(n)]
+
+
+def test_dynamic_refresh_limits_are_the_static_patterns():
+    """tau = 0 never refreshes (the static pattern); tau > 1 always refreshes
+    (every layer runs its own indexer, as an all-F stack)."""
+    lay = _dyn_layers()
+    k = 4
+    o_s, u_s, _ = O.run_stack("FSS", lay, k)
+    o_f, u_f, _ = O.run_stack("FFF", lay, k)
+    o0, u0, r0, rec0 = O.run_stack_dynamic("FSS", lay, k, stride=3, tau=0.0)
+    assert not r0.any() and all(np.array_equal(a, b) for a, b in zip(u0, u_s))
+    assert all(np.array_equal(a, b) for a, b in zip(o0, o_s))
+    o1, u1, r1, rec1 = O.run_stack_dynamic("FSS", lay, k, stride=3, tau=1.01)
+    assert r1.tolist() == [False, True, True] and all(np.array_equal(a, b) for a, b in zip(u1, u_f))
+    assert np.isnan(rec1[0]) and np.all((rec1[1:] >= 0) & (rec1[1:] <= 1))
+
+
+def test_dynamic_refresh_recall_by_hand():
+    """The pooled recall, counted by hand: an S layer whose indexer inputs are
+    the F layer's has recall exactly 1 and never refreshes below tau = 1; one
+    whose scores reverse the order has recall counted from explicit sets."""
+    lay = _dyn_layers(n=2)
+    k, L = 4, 12
+    same = [lay[0], dict(lay[1], q_I=lay[0]["q_I"], w=lay[0]["w"], k_I=lay[0]["k_I"])]
+    _, _, ref, rec = O.run_stack_dynamic("FS", same, k, stride=5, tau=1.0)
+    assert rec[1] == 1.0 and not ref[1]
+    _, _, ref, rec = O.run_stack_dynamic("FS", same, k, stride=5, tau=1.0 + 1e-12)
+    assert ref[1]
+    cache = O.indexer_topk(lay[0]["q_I"], lay[0]["w"], lay[0]["k_I"], k)
+    hit = own = 0
+    for t in (1, 6, 11):                                     # probe rows for L = 12, stride 5
+        sc = [float(lay[1]["w"][t] @ np.maximum(lay[1]["q_I"][t] @ lay[1]["k_I"][s], 0)) for s in range(t + 1)]
+        order = sorted(range(t + 1), key=lambda s: (-np.float32(sc[s]), s))[:k]
+        hit += len(set(order) & set(int(x) for x in cache[t] if x >= 0))
+        own += len(order)
+    _, _, _, rec = O.run_stack_dynamic("FS", lay, k, stride=5, tau=0.0)
+    assert rec[1] == hit / own
