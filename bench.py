@@ -520,6 +520,24 @@ def main():
         allf_ms = (time.perf_counter() - t0) * 1e3 / 2
         result["all_f"] = {"ms_per_step": round(allf_ms, 3), "speedup_of_pattern": round(allf_ms / ms_step, 3)}
 
+        # NEXT-4: the same stack where every S layer keeps its indexer and probes the cache on every
+        # 64th query (drift-triggered refresh); tau = 0 never refreshes (the probes' cost alone),
+        # tau > 1 always refreshes (every layer re-indexed, plus the probes)
+        log("timing dynamic refresh")
+        n_s = cfg.pattern.count("S")
+        dyn = {"probe_stride": 64, "s_layers": n_s}
+        for name, tau in (("never", 0.0), ("always", 1.01)):
+            r = ic.run_stack_dynamic(cfg.pattern, allf, cfg.k, 64, tau, outs=outs, idx_cache=idx_cache)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(2):
+                r = ic.run_stack_dynamic(cfg.pattern, allf, cfg.k, 64, tau, outs=outs, idx_cache=idx_cache)
+            torch.cuda.synchronize()
+            dyn[name + "_ms_per_step"] = round((time.perf_counter() - t0) * 1e3 / 2, 3)
+            dyn[name + "_refreshed_layers"] = int((r[3] == 1).sum().item())
+        dyn["probe_ms_per_s_layer"] = round((dyn["never_ms_per_step"] - ms_step) / max(n_s, 1), 4)
+        result["dynamic_refresh"] = dyn
+
     if not args.no_decode:
         log("timing decode64k")
         del outs

@@ -11,9 +11,15 @@ Functions mirror the C entry points (without the ``ic_`` prefix):
   indexer_topk(q_I, w, k_I, k)          -> idx [B, Lq, k] int32
   indexer_scores(q_I, w, k_I)           -> scores [B, Lq, row_stride] fp32
   topk_rows(scores, first_len, k)       -> idx [rows, k] int32
+  topk_rows_seq(scores, seq_len, k)     -> idx [rows, k] int32 (few long rows: segmented)
   sparse_attn(q, kv, idx)               -> out [B, Lq, H, d] bf16
   run_stack(pattern, layers, k)         -> (outs, idx_cache, stats)
+  run_stack_varlen(pattern, layers, k, q_len, pos0) -> (outs, idx_cache, stats)
+  run_stack_dynamic(pattern, layers, k, probe_stride, tau)
+                                        -> (outs, idx_cache, stats, refreshed, recall)
   decode_step(pattern, layers, seq_len, k) -> (outs, idx_cache, stats)
+  index_overlap(idx_a, idx_b)           -> (inter, jaccard, recall, means)
+  distill_kl(q_I, w, k_I, idx, qs, kvs) -> (kl [B, Lq], mean)
 """
 from __future__ import annotations
 
@@ -87,13 +93,17 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, sz, P(Stats), vp]
     L.ic_sparse_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_distill_kl.argtypes = [P(Shape), vp, vp, vp, vp, i32, P(vp), P(vp), vp, vp, vp, sz, vp]
+    L.ic_run_stack_dynamic.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), i32, ctypes.c_double, vp, vp, vp,
+                                       vp, sz, P(Stats), vp]
+    L.ic_run_stack_dynamic_ws.argtypes = [P(Shape), i32]
+    L.ic_run_stack_dynamic_ws.restype = sz
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
     for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
-               "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen", "ic_distill_kl",
+               "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen", "ic_distill_kl", "ic_run_stack_dynamic",
                "ic_decode_step", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
@@ -346,6 +356,30 @@ def run_stack(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, c
     _check(lib().ic_run_stack(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(idx_cache), _ptr(ws),
                               0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
     return outs, idx_cache, st.as_dict()
+
+
+def run_stack_dynamic(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, probe_stride: int,
+                      tau: float, chunk: int = 0, pos0: int = 0, outs: Optional[List[torch.Tensor]] = None,
+                      idx_cache=None, ws=None, stream=None):
+    """Prefill an F/S stack whose S layers that bring q_I, w, k_I probe the index cache and
+    re-index when the pooled recall of their own top-k in it is below tau.
+    Returns (outs, idx_cache, stats, refreshed [n_layers, B] int32 (-1: no probe),
+    recall [n_layers, B] fp32 (nan: no probe)), all tensors on the GPU."""
+    s = _stack_shape(pattern, layers, k, chunk, pos0)
+    dev = layers[0]["q"].device
+    if outs is None:
+        outs = [torch.empty_like(l["q"]) for l in layers]
+    if idx_cache is None:
+        idx_cache = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=dev)
+    refreshed = torch.full((len(layers), s.B), -1, dtype=torch.int32, device=dev)
+    recall = torch.full((len(layers), s.B), float("nan"), dtype=torch.float32, device=dev)
+    ws = _workspace(int(lib().ic_run_stack_dynamic_ws(ctypes.byref(s), probe_stride)), dev, ws)
+    arr = _layers_struct(pattern, layers, outs)
+    st = Stats()
+    _check(lib().ic_run_stack_dynamic(pattern.encode(), len(layers), arr, ctypes.byref(s), probe_stride, float(tau),
+                                      _ptr(idx_cache), _ptr(refreshed), _ptr(recall), _ptr(ws),
+                                      0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
+    return outs, idx_cache, st.as_dict(), refreshed, recall
 
 
 def run_stack_varlen(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, q_len: Sequence[int],

@@ -123,6 +123,27 @@ DecodeWs decode_layout(const ic_shape& s) {
 }
 size_t decode_ws(const ic_shape& s) { return decode_layout(s).total; }
 
+// Dynamic refresh: the indexer tile, then the probe's region: scores [P, round_up(pos0 + Lq, 4)]
+// fp32 | own top-k [P, k] int32 | intersections [P] int32 | refresh flag.
+struct DynWs {
+    int P;
+    int t0;                       // first probe query
+    int64_t score_stride;
+    size_t probe_scores_off, probe_idx_off, inter_off, flag_off, total;
+};
+DynWs dyn_layout(const ic_shape& s, int stride) {
+    DynWs d;
+    d.t0 = (s.Lq - 1) % stride;
+    d.P = (s.Lq - 1 - d.t0) / stride + 1;
+    d.score_stride = round_up((int64_t)s.pos0 + s.Lq, 4);
+    d.probe_scores_off = (size_t)round_up((int64_t)indexer_ws(s), 256);
+    d.probe_idx_off = d.probe_scores_off + (size_t)round_up((int64_t)d.P * d.score_stride * 4, 256);
+    d.inter_off = d.probe_idx_off + (size_t)round_up((int64_t)d.P * s.k * 4, 256);
+    d.flag_off = d.inter_off + (size_t)round_up((int64_t)d.P * 4, 256);
+    d.total = d.flag_off + 256;
+    return d;
+}
+
 ic_status check_ws(const void* ws, size_t have, size_t need) {
     if (need == 0) return IC_OK;
     if (!ws) return fail(IC_ERR_WORKSPACE, "workspace is NULL but %zu bytes are needed", need);
@@ -136,7 +157,8 @@ size_t elem_bytes(int dtype) { return dtype == IC_FP8_E4M3 ? 1 : 2; }
 // a1 + a2 for one sequence: its Lq queries at positions pos0.. against its keys, in score
 // tiles of <= chunk queries, then top-k into idx [Lq, k].
 ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_t* qb, const float* wb,
-                               const uint8_t* kb, int32_t* idx, void* ws, hipStream_t st, int64_t* tiles) {
+                               const uint8_t* kb, int32_t* idx, void* ws, hipStream_t st, int64_t* tiles,
+                               const int32_t* run_if = nullptr) {
     const int chunk = chunk_of(s);
     float* tile = static_cast<float*>(ws);
     for (int c0 = 0; c0 < Lq; c0 += chunk) {
@@ -154,9 +176,11 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         a.H_I = s.H_I;
         a.d_I = s.d_I;
         a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+        a.run_if = run_if;
         hipError_t e = launch_indexer_prefill(a, st);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
         ic_topk_args t;
+        t.run_if = run_if;
         t.scores = tile;
         t.row_stride = stride;
         t.rows = nq;
@@ -390,6 +414,115 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
             return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
         r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
+        if (r != IC_OK) return r;
+        ++cnt.attn_calls;
+        ++cnt.layers;
+    }
+    g_stats = cnt;
+    if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+size_t ic_run_stack_dynamic_ws(const ic_shape* shape, int32_t probe_stride) {
+    if (check_shape(shape, true, false) != IC_OK) return 0;
+    if (probe_stride < 1) {
+        fail(IC_ERR_ARG, "probe_stride must be >= 1 (got %d)", probe_stride);
+        return 0;
+    }
+    return dyn_layout(*shape, probe_stride).total;
+}
+
+ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape* shape,
+                               int32_t probe_stride, double tau, int32_t* idx_cache, int32_t* refreshed,
+                               float* recall, void* ws, size_t ws_bytes, ic_stats* stats, void* stream) {
+    ic_status r = check_shape(shape, true, false);
+    if (r != IC_OK) return r;
+    if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
+    if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if (probe_stride < 1) return fail(IC_ERR_ARG, "probe_stride must be >= 1 (got %d)", probe_stride);
+    if (!(tau >= 0.0 && tau <= 2.0)) return fail(IC_ERR_ARG, "tau must be in [0, 2] (got %g)", tau);
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        const int have = (L.q_I != nullptr) + (L.w != nullptr) + (L.k_I != nullptr);
+        if (have != 0 && have != 3)
+            return fail(IC_ERR_ARG, "layer %d: q_I, w and k_I must be all set or all NULL", l);
+    }
+    const ic_shape& s = *shape;
+    const DynWs d = dyn_layout(s, probe_stride);
+    if ((r = check_ws(ws, ws_bytes, d.total)) != IC_OK) return r;
+    hipStream_t st = (hipStream_t)stream;
+    uint8_t* wsb = static_cast<uint8_t*>(ws);
+    float* pscores = reinterpret_cast<float*>(wsb + d.probe_scores_off);
+    int32_t* pidx = reinterpret_cast<int32_t*>(wsb + d.probe_idx_off);
+    int32_t* inter = reinterpret_cast<int32_t*>(wsb + d.inter_off);
+    int32_t* flag = reinterpret_cast<int32_t*>(wsb + d.flag_off);
+    const size_t eb = elem_bytes(s.idx_dtype);
+    // own entries of the probe rows: every probe row is full once it sees k keys
+    int64_t own = 0;
+    for (int j = 0; j < d.P; ++j) own += std::min<int64_t>(s.k, (int64_t)s.pos0 + d.t0 + (int64_t)j * probe_stride + 1);
+    ic_stats cnt = {0, 0, 0, 0};
+    bool cached = false;
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        const bool full = pattern[l] == 'F' || pattern[l] == '1';
+        if (full) {
+            r = run_indexer_topk(s, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles);
+            if (r != IC_OK) return r;
+            cached = true;
+            ++cnt.indexer_calls;
+        } else if (!cached) {
+            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
+        } else if (L.q_I) {
+            for (int b = 0; b < s.B; ++b) {
+                const uint8_t* qb = static_cast<const uint8_t*>(L.q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
+                const float* wb = L.w + (size_t)b * s.Lq * s.H_I;
+                const uint8_t* kb = static_cast<const uint8_t*>(L.k_I) + (size_t)b * s.Lk * s.d_I * eb;
+                int32_t* idxb = idx_cache + (size_t)b * s.Lq * s.k;
+                // probe: this layer's own scores and top-k for every probe_stride-th query
+                ic_indexer_decode_args a{};
+                a.q_I = qb + (size_t)d.t0 * s.H_I * s.d_I * eb;
+                a.w = wb + (size_t)d.t0 * s.H_I;
+                a.k_I = kb;
+                a.seq_len = nullptr;
+                a.scores = pscores;
+                a.score_stride = d.score_stride;
+                a.B = d.P;
+                a.Lk = s.pos0 + s.Lq;
+                a.H_I = s.H_I;
+                a.d_I = s.d_I;
+                a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+                a.q_rows = probe_stride;
+                a.k_rows = 0;
+                a.len0 = s.pos0 + d.t0 + 1;
+                a.len_step = probe_stride;
+                hipError_t e = launch_indexer_decode(a, st);
+                if (e != hipSuccess) return hip_fail(e, "probe indexer launch");
+                ic_topk_args t{};
+                t.scores = pscores;
+                t.row_stride = d.score_stride;
+                t.rows = d.P;
+                t.first_len = s.pos0 + d.t0 + 1;
+                t.seq_len = nullptr;
+                t.k = s.k;
+                t.idx = pidx;
+                t.max_len = s.pos0 + s.Lq;
+                t.cand = nullptr;
+                t.len_step = probe_stride;
+                e = launch_topk(t, st);
+                if (e != hipSuccess) return hip_fail(e, "probe top-k launch");
+                // |cached row & own row| for the probe rows, then the decision on the device
+                e = launch_overlap(idxb + (size_t)d.t0 * s.k, pidx, d.P, s.k, inter, nullptr, nullptr, nullptr, st,
+                                   probe_stride);
+                if (e != hipSuccess) return hip_fail(e, "probe overlap launch");
+                e = launch_drift_decision(inter, d.P, own, tau, flag, refreshed ? refreshed + (size_t)l * s.B + b : nullptr,
+                                          recall ? recall + (size_t)l * s.B + b : nullptr, st);
+                if (e != hipSuccess) return hip_fail(e, "drift decision launch");
+                // the refresh: every launch of it returns at once unless the flag is set
+                r = run_indexer_topk_one(s, s.Lq, s.pos0, qb, wb, kb, idxb, ws, st, &cnt.score_tiles, flag);
+                if (r != IC_OK) return r;
+            }
+        }
+        r = run_attn(s, s.Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
         if (r != IC_OK) return r;
         ++cnt.attn_calls;
         ++cnt.layers;

@@ -94,17 +94,21 @@ struct ic_indexer_args {
     int32_t pos_begin;    // absolute position of query q_begin
     int32_t H_I, d_I;
     int32_t fp8;
+    const int32_t* run_if = nullptr;   // optional device flag: the launch does nothing while it is 0
 };
 hipError_t launch_indexer_prefill(const ic_indexer_args& a, hipStream_t st);
 
 struct ic_indexer_decode_args {
-    const void* q_I;      // [B, H_I, d_I]
-    const float* w;       // [B, H_I]
-    const void* k_I;      // [B, Lk, d_I]
-    const int32_t* seq_len;  // [B] device
+    const void* q_I;      // row b at q_I + b * q_rows query rows ([B, H_I, d_I] when q_rows = 1)
+    const float* w;       // row b at w + b * q_rows rows of H_I
+    const void* k_I;      // keys of row b at k_I + b * k_rows key rows ([B, Lk, d_I] when k_rows = Lk)
+    const int32_t* seq_len;  // [B] device; NULL: row b sees len0 + b * len_step keys
     float* scores;        // [B, score_stride]
     int64_t score_stride; // >= Lk
     int32_t B, Lk, H_I, d_I, fp8;
+    int64_t q_rows = 1;   // query rows between consecutive b (strided probe rows)
+    int64_t k_rows = -1;  // key rows between consecutive b; -1 means Lk, 0 shares one key set
+    int32_t len0 = 0, len_step = 0;
 };
 hipError_t launch_indexer_decode(const ic_indexer_decode_args& a, hipStream_t st);
 
@@ -118,6 +122,8 @@ struct ic_topk_args {
     int32_t* idx;         // [rows, k]
     int32_t max_len;      // upper bound of any row's visible length (host-known)
     int32_t* cand;        // optional workspace of topk_ws_bytes(): few long rows run segmented
+    int32_t len_step = 1; // without seq_len, row r has first_len + r * len_step visible entries
+    const int32_t* run_if = nullptr;   // optional device flag: the launch does nothing while it is 0
 };
 // Few long rows (decode) are ranked in TOPK_SEG-key segments first, then over the
 // segments' candidates; that needs topk_ws_bytes() of workspace (0 otherwise).
@@ -159,6 +165,11 @@ hipError_t launch_distill(const ic_distill_args& a, hipStream_t st);
 hipError_t launch_mean(const float* x, int64_t n, float* out, hipStream_t st);
 
 // Per-row overlap of two index caches [rows, k] (rows ascending, -1 padded); means may be NULL.
+// Row r of A is at ia + r * a_row_step * k (a_row_step = 1: contiguous).
 hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int64_t rows, int k, int32_t* inter, float* jac,
-                          float* rec, float* means, hipStream_t st);
+                          float* rec, float* means, hipStream_t st, int64_t a_row_step = 1);
+// Drift decision of one probe: hit = sum of inter[0..P), refresh iff hit < tau * own;
+// writes flag[0] (1 = refresh), refreshed[0] and recall[0] = hit / own.
+hipError_t launch_drift_decision(const int32_t* inter, int P, int64_t own, double tau, int32_t* flag,
+                                 int32_t* refreshed, float* recall, hipStream_t st);
 size_t sparse_attn_ws_bytes(int32_t nq, int32_t H, int32_t d, int32_t nsplit);

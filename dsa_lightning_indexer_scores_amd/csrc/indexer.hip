@@ -231,7 +231,9 @@ __device__ __forceinline__ void load_w(float (&wr)[HT][4], const float* wrow, in
 template <bool FP8, int D_I, int HT, int QW, int NW, int KB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_prefill_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    float* __restrict__ scores, int64_t row_stride, int q_begin, int nq, int pos_begin, int H_I, int seg_blocks) {
+    float* __restrict__ scores, int64_t row_stride, int q_begin, int nq, int pos_begin, int H_I, int seg_blocks,
+    const int32_t* __restrict__ run_if) {
+    if (run_if != nullptr && *run_if == 0) return;            // a refresh that was not needed
     using G = IdxGeom<FP8, D_I>;
     static_assert(KB % 64 == 0, "a key block is stored 64 keys per instruction");
     constexpr int QB = QW * NW;
@@ -393,16 +395,17 @@ constexpr int DEC_KEYS_PER_WG = DEC_NW * DEC_KEYS_PER_WAVE;
 template <bool FP8, int D_I, int HT>
 __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8 ? 3 : 2, FP8 ? 3 : 2))) void indexer_decode_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I) {
+    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I,
+    int64_t q_rows, int64_t k_rows, int len0, int len_step) {
     using G = IdxGeom<FP8, D_I>;
     const int b = blockIdx.y;
-    const int n = max(1, min(seq_len[b], Lk));                // visible keys (clamped to the cache)
+    const int n = max(1, min(seq_len ? seq_len[b] : len0 + b * len_step, Lk));   // visible keys (clamped to the cache)
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int key0 = blockIdx.x * DEC_KEYS_PER_WG + wv * DEC_KEYS_PER_WAVE;
     if (key0 >= n) return;
 
-    const uint8_t* kbase = kI + (int64_t)b * Lk * G::ROWB;
+    const uint8_t* kbase = kI + (int64_t)b * k_rows * G::ROWB;
     Frag<FP8, D_I> Bf[2][DEC_TILES];
     auto load_chunk = [&](Frag<FP8, D_I> (&B)[DEC_TILES], int c) {
 #pragma unroll
@@ -418,9 +421,9 @@ __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = 16 * ht + r;
-        load_frag<FP8, D_I>(A[ht], h < H_I ? qI + ((int64_t)b * H_I + h) * G::ROWB : nullptr, g);
+        load_frag<FP8, D_I>(A[ht], h < H_I ? qI + ((int64_t)b * q_rows * H_I + h) * G::ROWB : nullptr, g);
     }
-    load_w<HT>(wr, w + (int64_t)b * H_I, H_I, g);
+    load_w<HT>(wr, w + (int64_t)b * q_rows * H_I, H_I, g);
     float* srow = scores + (int64_t)b * score_stride;
 #pragma unroll
     for (int c = 0; c < DEC_CHUNKS; ++c) {
@@ -474,7 +477,7 @@ hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t 
     const dim3 grid(nblk, (nkb_max + seg_blocks - 1) / seg_blocks);
     hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D_I, HT, QW, NW, PREFILL_KB>), grid, dim3(NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.scores, a.row_stride,
-                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks);
+                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks, a.run_if);
     return hipGetLastError();
 }
 
@@ -494,7 +497,7 @@ hipError_t decode_dispatch(const ic_indexer_decode_args& a, hipStream_t st) {
     dim3 grid((a.Lk + DEC_KEYS_PER_WG - 1) / DEC_KEYS_PER_WG, a.B);
     hipLaunchKernelGGL((indexer_decode_kernel<FP8, D_I, HT>), grid, dim3(DEC_NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.seq_len, a.scores, a.score_stride,
-                       a.Lk, a.H_I);
+                       a.Lk, a.H_I, a.q_rows, a.k_rows < 0 ? (int64_t)a.Lk : a.k_rows, a.len0, a.len_step);
     return hipGetLastError();
 }
 

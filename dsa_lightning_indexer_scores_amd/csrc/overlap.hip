@@ -31,11 +31,12 @@ __device__ __forceinline__ int wave_isum(int x) {
 
 __global__ __launch_bounds__(OV_NT) void overlap_kernel(const int32_t* __restrict__ ia, const int32_t* __restrict__ ib,
                                                          int k, int32_t* __restrict__ inter,
-                                                         float* __restrict__ jac, float* __restrict__ rec) {
+                                                         float* __restrict__ jac, float* __restrict__ rec,
+                                                         int64_t a_row_step) {
     __shared__ int32_t bl[OV_MAXK];
     __shared__ int part[3][OV_NT / 64];
     const int64_t row = blockIdx.x;
-    const int32_t* a = ia + row * k;
+    const int32_t* a = ia + row * a_row_step * k;
     const int32_t* b = ib + row * k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     int na = 0, nb = 0;
@@ -108,12 +109,48 @@ __global__ __launch_bounds__(1024) void overlap_mean_kernel(const float* __restr
 }  // namespace
 
 hipError_t launch_overlap(const int32_t* ia, const int32_t* ib, int64_t rows, int k, int32_t* inter, float* jac,
-                          float* rec, float* means, hipStream_t st) {
+                          float* rec, float* means, hipStream_t st, int64_t a_row_step) {
     if (rows <= 0) return hipSuccess;
     if (k < 1 || k > OV_MAXK) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(overlap_kernel, dim3((unsigned)rows), dim3(OV_NT), 0, st, ia, ib, k, inter, jac, rec);
+    hipLaunchKernelGGL(overlap_kernel, dim3((unsigned)rows), dim3(OV_NT), 0, st, ia, ib, k, inter, jac, rec,
+                       a_row_step);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || means == nullptr) return e;
     hipLaunchKernelGGL(overlap_mean_kernel, dim3(1), dim3(1024), 0, st, jac, rec, rows, means);
+    return hipGetLastError();
+}
+
+namespace {
+
+// Drift decision of a probe: the pooled recall's numerator summed exactly (int64, one
+// workgroup, fixed order), the comparison taken in double.
+__global__ __launch_bounds__(256) void drift_decision_kernel(const int32_t* __restrict__ inter, int P, int64_t own,
+                                                             double tau, int32_t* __restrict__ flag,
+                                                             int32_t* __restrict__ refreshed,
+                                                             float* __restrict__ recall) {
+    __shared__ long long part[256];
+    long long s = 0;
+    for (int i = threadIdx.x; i < P; i += 256) s += inter[i];
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        const long long hit = part[0];
+        const int32_t go = (double)hit < tau * (double)own ? 1 : 0;
+        flag[0] = go;
+        if (refreshed) refreshed[0] = go;
+        if (recall) recall[0] = own > 0 ? (float)((double)hit / (double)own) : 0.f;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_drift_decision(const int32_t* inter, int P, int64_t own, double tau, int32_t* flag,
+                                 int32_t* refreshed, float* recall, hipStream_t st) {
+    if (P <= 0) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(drift_decision_kernel, dim3(1), dim3(256), 0, st, inter, P, own, tau, flag, refreshed, recall);
     return hipGetLastError();
 }

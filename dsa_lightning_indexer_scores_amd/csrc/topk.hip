@@ -112,7 +112,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
                                                   int first_len, const int32_t* __restrict__ seq_len, int k,
                                                   int32_t* __restrict__ idx, int max_len, int seg, int nseg,
                                                   const int32_t* __restrict__ cand, int cand_len,
-                                                  uint32_t* __restrict__ ckeys) {
+                                                  uint32_t* __restrict__ ckeys, int len_step,
+                                                  const int32_t* __restrict__ run_if) {
+    if (run_if != nullptr && *run_if == 0) return;            // a refresh that was not needed
     constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
     constexpr int BLOCK = NT * EPT;                  // keys per block
     // Long rows keep one histogram per wave: a concentrated score distribution puts
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ scor
     int32_t* out = idx + (int64_t)row * k;
     const int srow = MODE == TOPK_SEGS ? row / nseg : row;   // score row
     // visible length of the score row, clamped to the allocated row (a bad seq_len cannot overrun)
-    const int len = max(1, min(seq_len ? seq_len[srow] : first_len + srow,
+    const int len = max(1, min(seq_len ? seq_len[srow] : first_len + srow * len_step,
                                (STREAM || MODE != TOPK_ROWS) ? max_len : min(max_len, BLOCK)));
     int n = len, off = 0;                            // keys this workgroup ranks; position offset
     uint32_t* okey = ckeys + (int64_t)row * k;       // TOPK_SEGS: keys of the picks
@@ -533,11 +535,11 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
         if (vec)                                                                                            \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,      \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len, ckeys);                                                     \
+                               nseg, cand, len, ckeys, a.len_step, a.run_if);                               \
         else                                                                                                \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,     \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len, ckeys);                                                     \
+                               nseg, cand, len, ckeys, a.len_step, a.run_if);                               \
         return hipGetLastError();                                                                           \
     } while (0)
     if (len <= 2048) IC_TOPK_GO(256, 8, false);

@@ -209,6 +209,31 @@ IC_API ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, cons
                                      const ic_shape* shape, const int32_t* q_len, const int32_t* pos0,
                                      int32_t* idx_cache, void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
 
+/* Prefill through the stack with drift-triggered refresh (blog, Conclusion:
+ * decide at runtime whether a layer's neighbour is still a good proxy, and
+ * refresh only when the drift exceeds a threshold; agent skill page, Step 1:
+ * top-k set overlap as the measure).  Pattern, shapes and cache rules as
+ * ic_run_stack, except that an S layer may also bring its own q_I, w and k_I
+ * (all three, or none).  Such an S layer first probes the cache of each
+ * sequence: for the queries t = (Lq-1) mod probe_stride, ... , Lq-1 it takes
+ * its own top-k and counts hit = sum |cached row & own row| against own =
+ * sum |own row|; when hit < tau * own (tau in [0, 2]; 0 never refreshes,
+ * above 1 always does) it re-runs its indexer and top-k for every query of
+ * that sequence, overwriting the cache, as an F layer would.  The decision
+ * stays on the device (the refresh launches return at once when it is not
+ * taken), so the call never waits for the GPU.  refreshed [n_layers, B] int32
+ * and recall [n_layers, B] fp32 (device, each may be NULL) receive the
+ * decision and hit / own of every probed (layer, sequence); entries of layers
+ * without a probe are left untouched.  The workspace is
+ * ic_run_stack_dynamic_ws(shape, probe_stride) bytes. */
+IC_API ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_layer* layers,
+                                      const ic_shape* shape, int32_t probe_stride, double tau, int32_t* idx_cache,
+                                      int32_t* refreshed, float* recall, void* ws, size_t ws_bytes,
+                                      ic_stats* stats, void* stream);
+
+/* Workspace bytes of ic_run_stack_dynamic for this shape and probe stride (0 if invalid). */
+IC_API size_t ic_run_stack_dynamic_ws(const ic_shape* shape, int32_t probe_stride);
+
 /* One decode step through the stack.  shape.Lq must be 1 and shape.Lk is
  * the cache capacity.  seq_len [B] int32 (device) counts each sequence's
  * tokens including the new one, whose k_I (F layers) and kv rows the caller

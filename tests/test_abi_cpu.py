@@ -177,3 +177,23 @@ def test_distill_kl_validation(L):
     assert call(_shape(d=96), 2, ptrs, ptrs) == ic.IC_ERR_SHAPE
     assert call(_shape(idx_dtype=7), 2, ptrs, ptrs) == ic.IC_ERR_DTYPE
     assert call(s, 2, ptrs, ptrs, wsb=16) == ic.IC_ERR_WORKSPACE
+
+
+def test_run_stack_dynamic_validation(L):
+    s = _shape()
+    ws = ctypes.c_void_p(0x10000)
+    run = lambda pat, stride=16, tau=0.5, layers=None, wsb=1 << 30: L.ic_run_stack_dynamic(
+        pat.encode(), len(pat), layers if layers is not None else _layers(pat), ctypes.byref(s), stride, tau,
+        FAKE, None, None, ws, wsb, None, None)
+    assert run("SFSS") == ic.IC_ERR_NO_CACHED_INDICES
+    assert run("FSSS", stride=0) == ic.IC_ERR_ARG
+    assert run("FSSS", tau=-0.1) == ic.IC_ERR_ARG
+    assert run("FSSS", tau=float("nan")) == ic.IC_ERR_ARG
+    half = _layers("FSSS")
+    half[1].q_I = FAKE                                                    # q_I without w and k_I
+    assert run("FSSS", layers=half) == ic.IC_ERR_ARG
+    assert run("FSSS", wsb=16) == ic.IC_ERR_WORKSPACE
+    need = L.ic_run_stack_dynamic_ws(ctypes.byref(s), 16)
+    assert need > ic.workspace_size(s, ic.IC_OP_RUN_STACK)               # tile + probe region
+    assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 1) > need          # more probe rows
+    assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 0) == 0
