@@ -8,15 +8,17 @@
 //
 // One wave owns one (query, group of 16 heads[, key split]).  Per step of 32
 // selected rows:
-//   prefill: the rows' [K | V] are gathered with fully coalesced 16-byte loads
-//       (a row is 512 contiguous bytes, so one load instruction covers two whole
-//       rows and every 4-lane quad reads one 64-byte run) into the wave's LDS
-//       tile, and K fragments are read back from there.  Gathering K straight
-//       into fragments (lanes 0-15 on 16 different rows) makes each quad touch
-//       four rows; with every CU busy, the vector-memory address unit then bounds
-//       the kernel (measured 95% busy);
+//   prefill: the rows are gathered with fully coalesced 16-byte loads (one
+//       instruction covers two K or V halves of 256 bytes; every 4-lane quad
+//       reads one 64-byte run).  Gathering K straight into MFMA fragments
+//       (lanes 0-15 on 16 different rows) makes each quad touch four rows, and
+//       the vector-memory address unit then bounds the kernel.  The K halves go
+//       through a half-size wave LDS tile for the QK^T fragments, then the V
+//       halves through the same tile for the transposed PV reads.  One register
+//       set holds the next step's halves, so about 150 VGPRs and 35 KB of LDS
+//       per workgroup give three waves per SIMD;
 //   split-K decode, latency-bound with one or two steps per wave, gathers K
-//       straight into fragments and stages only V (one LDS round trip fewer);
+//       straight into fragments and stages only V;
 //   S^T (32 keys x 16 heads) = K Q^T;
 //   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
 //       lane % 16) is also the layout of O^T below, so the running max and
@@ -27,9 +29,9 @@
 //       k order matches the transposed read, so no shuffle is needed);
 //   l += ones^T P^T, one more MFMA, so the denominator sums the same bf16 P
 //       as the numerator and costs no VALU.
-// Row offsets of a step are staged through a few wave-private LDS words so each
-// lane reads its load addresses as one vector (no per-row lane reads).  Steps past
-// a query's last real idx entry are not run.
+// Prefill row offsets are staged through a few wave-private LDS words so each lane
+// reads its load addresses as one vector (no per-row lane reads).  Steps past a
+// query's last real idx entry are not run.
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
 // workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
 // the workgroups' partials in split order, so results are deterministic.  (A
@@ -49,38 +51,29 @@ constexpr int KT = 32;                  // selected rows per step
 // reference value gives the same softmax once O is divided by l.
 constexpr float RESCALE_LOG2 = 8.f;
 
-template <int D, bool ROWS>
-struct AttGeom {
+template <int D>
+struct AttGeom {                        // split-K decode
     static constexpr int NDC = D / 32;  // K=32 chunks of the QK^T contraction
     static constexpr int NDT = D / 16;  // 16-wide d tiles of the output
     static constexpr int RB = 4 * D;    // bytes per KV row: K[d] then V[d], bf16
-    // ROWS: whole rows staged in LDS
-    static constexpr int RSTR = RB + 16;   // LDS bytes per staged row (16-byte skew)
-    static constexpr int PPR = RB / 16;    // 16-byte pieces per row
-    static constexpr int RPI = 64 / PPR;   // rows per load instruction
-    static constexpr int NI = KT / RPI;    // load instructions per step
-    static_assert(PPR <= 64 && 64 % PPR == 0, "a load instruction covers whole rows");
-    // !ROWS: K gathered into fragments, V rows staged in LDS
-    static constexpr int VSTR = 2 * D + 16;           // LDS bytes per V row (padded)
+    static constexpr int STR = 2 * D + 16;            // LDS bytes per V row (padded)
     static constexpr int VPPR = D * 2 / 16;           // 16-byte pieces per V row
     static constexpr int VPL = KT * VPPR / 64;        // V pieces per lane
-    // staged row stride and where V starts in a staged row
-    static constexpr int STR = ROWS ? RSTR : VSTR;
-    static constexpr int VOFF = ROWS ? 2 * D : 0;
 };
 
 __device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-template <int D, bool SPLIT>
-__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_kernel(
+// Split-K decode: wave (query, head group, split) runs its slice of the idx row and the
+// workgroup's four splits merge into one partial.
+template <int D>
+__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
-    uint16_t* __restrict__ out, float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
+    float* __restrict__ part, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq,
     int H, int k, int nsplit, float scale_log2) {
-    constexpr bool ROWS = !SPLIT;
-    using G = AttGeom<D, ROWS>;
-    static_assert(!SPLIT || ATT_NW * 16 * D * 4 + ATT_NW * 16 * 8 <= ATT_NW * KT * G::STR,
+    using G = AttGeom<D>;
+    static_assert(ATT_NW * 16 * D * 4 + ATT_NW * 16 * 8 <= ATT_NW * KT * G::STR,
                   "the LDS merge reuses the row tiles");
     __shared__ __attribute__((aligned(16))) uint8_t vlds_all[ATT_NW][KT * G::STR];
     const int lane = threadIdx.x & 63;
@@ -93,8 +86,6 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int64_t qi = item / ((int64_t)nsplit * HG);
     if (qi >= nq) return;
     uint8_t* vlds = vlds_all[wv];
-    __shared__ __attribute__((aligned(16))) uint32_t idx_lds_all[ATT_NW][KT];   // ROWS: a step's row offsets
-    uint32_t* idx_lds = idx_lds_all[wv];
 
     const int seq = (int)(qi / q_per_seq);
     const uint16_t* kvs = kv + (int64_t)seq * kv_seq_stride;
@@ -122,7 +113,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     // step issued just ahead of it; its issue then never waits for those rows.
     auto load_idx = [&](int j0) -> int {
         const int jl = j0 + (lane & 31);
-        return (jl < j_end && lane < 32) ? irow[jl] : -1;
+        const int v = irow[min(jl, j_end - 1)];           // unconditional load: no branch around it
+        return (jl < j_end && lane < 32) ? v : -1;
     };
     int idxA = load_idx(j_begin), idxB = load_idx(j_begin + KT);   // in flight with the scan below
     // Only the steps up to the last entry that names a row are run (an idx row padded
@@ -131,9 +123,10 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int jb = j_begin; jb < j_end; jb += 64 * 8) {
         int v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < 8; ++u) {                    // unconditional (clamped) loads: one wait for all eight
             const int j = jb + 64 * u + lane;
-            v[u] = j < j_end ? irow[j] : -1;
+            v[u] = irow[min(j, j_end - 1)];
+            v[u] = j < j_end ? v[u] : -1;
         }
 #pragma unroll
         for (int u = 0; u < 8; ++u)
@@ -141,7 +134,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
-    const int nsteps = j_last < 0 ? 0 : (j_last - j_begin) / KT + 1;
+    const int nsteps = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : (j_last - j_begin) / KT + 1);
     // Ends with a wait for every load so far: the step loop below starts from a clean count.
     __builtin_amdgcn_s_waitcnt(0);
 
@@ -160,9 +153,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     // of -1 read a real row and are masked), so no branch separates a load from its
     // use and the compiler's in-order load counting stays exact.
     struct Tile {
-        i32x4 raw[ROWS ? G::NI : 1];                         // ROWS: whole rows, as loaded
-        i32x4 kf[ROWS ? 1 : 2][G::NDC];                      // !ROWS: K fragments, keys 16*kt + m
-        i32x4 vst[ROWS ? 1 : G::VPL];                        // !ROWS: V rows, staged for LDS
+        i32x4 kf[2][G::NDC];                                 // K fragments, keys 16*kt + m
+        i32x4 vst[G::VPL];                                   // V rows, staged for LDS
         uint32_t valid;                                      // bit e: entry e of the step is a row
     };
     auto issue = [&](Tile& T, int raw_idx) {
@@ -171,56 +163,29 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         __builtin_amdgcn_sched_barrier(0);
         const bool ok = (uint32_t)raw_idx < (uint32_t)Lk;   // -1 or past the KV rows: no row
         T.valid = (uint32_t)__ballot(ok);
-        const uint32_t row = ok ? (uint32_t)raw_idx : 0u;    // a real row, masked later
-        if constexpr (ROWS) {
-            // Row offsets go through the wave's LDS slots, de-interleaved so that the
-            // lanes of row r of every load instruction read theirs as one vector:
-            // entry RPI*i + r -> slot r*NI + i.
-            if (lane < KT) idx_lds[(lane % G::RPI) * G::NI + lane / G::RPI] = row * (uint32_t)G::RB;
-            lds_wave_sync();
-            uint32_t roff[G::NI];
+        const int safe_idx = ok ? raw_idx : 0;               // a real row, masked later
 #pragma unroll
-            for (int i = 0; i < G::NI; i += 4) {
-                const u32x4 v = *reinterpret_cast<const u32x4*>(idx_lds + (lane / G::PPR) * G::NI + i);
-                roff[i] = v[0]; roff[i + 1] = v[1]; roff[i + 2] = v[2]; roff[i + 3] = v[3];
-            }
-            const uint32_t piece = (lane % G::PPR) * 16;
+        for (int i = 0; i < G::VPL; ++i) {                   // V piece c -> row c / VPPR, byte (c % VPPR) * 16
+            const int c = lane + 64 * i;
+            const int r = __shfl(safe_idx, c / G::VPPR);
+            const uint32_t off = (uint32_t)r * G::RB + 2 * D + (c % G::VPPR) * 16;
+            T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
+        }
 #pragma unroll
-            for (int i = 0; i < G::NI; ++i)
-                T.raw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));   // scalar base + 32-bit offset
-        } else {
-            const int safe_idx = (int)row;
+        for (int kt = 0; kt < 2; ++kt) {                     // lane (m, g): key 16*kt + m, d = 32*dc + 8g
+            const int r = __shfl(safe_idx, 16 * kt + n);
+            const uint32_t off = (uint32_t)r * G::RB + 16 * g;
 #pragma unroll
-            for (int i = 0; i < G::VPL; ++i) {               // V piece c -> row c / VPPR, byte (c % VPPR) * 16
-                const int c = lane + 64 * i;
-                const int r = __shfl(safe_idx, c / G::VPPR);
-                const uint32_t off = (uint32_t)r * G::RB + 2 * D + (c % G::VPPR) * 16;
-                T.vst[i] = *reinterpret_cast<const i32x4*>(kvb + off);
-            }
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {                 // lane (m, g): key 16*kt + m, d = 32*dc + 8g
-                const int r = __shfl(safe_idx, 16 * kt + n);
-                const uint32_t off = (uint32_t)r * G::RB + 16 * g;
-#pragma unroll
-                for (int dc = 0; dc < G::NDC; ++dc)
-                    T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
-            }
+            for (int dc = 0; dc < G::NDC; ++dc)
+                T.kf[kt][dc] = *reinterpret_cast<const i32x4*>(kvb + off + 64 * dc);
         }
     };
     auto compute = [&](const Tile& T) {
         const uint32_t valid = T.valid;
-        if constexpr (ROWS) {
 #pragma unroll
-            for (int i = 0; i < G::NI; ++i)
-                *reinterpret_cast<i32x4*>(vlds + (G::RPI * i + lane / G::PPR) * G::RSTR + (lane % G::PPR) * 16) =
-                    T.raw[i];
-            lds_wave_sync();
-        } else {
-#pragma unroll
-            for (int i = 0; i < G::VPL; ++i) {
-                const int c = lane + 64 * i;
-                *reinterpret_cast<i32x4*>(vlds + (c / G::VPPR) * G::VSTR + (c % G::VPPR) * 16) = T.vst[i];
-            }
+        for (int i = 0; i < G::VPL; ++i) {
+            const int c = lane + 64 * i;
+            *reinterpret_cast<i32x4*>(vlds + (c / G::VPPR) * G::STR + (c % G::VPPR) * 16) = T.vst[i];
         }
         // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e.  K fragment: key 16*kt + n,
         // d = 32*dc + 8g .. +7.
@@ -229,14 +194,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         for (int kt = 0; kt < 2; ++kt) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) {
-                i32x4 kf;
-                if constexpr (ROWS)
-                    kf = *reinterpret_cast<const i32x4*>(vlds + (16 * kt + n) * G::RSTR + 64 * dc + 16 * g);
-                else
-                    kf = T.kf[kt][dc];
-                acc = mfma_bf16_k32(kf, qf[dc], acc);
-            }
+            for (int dc = 0; dc < G::NDC; ++dc) acc = mfma_bf16_k32(T.kf[kt][dc], qf[dc], acc);
             s[kt] = acc;
         }
         float x[8];                                          // raw scores; -inf for -1 entries
@@ -275,8 +233,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         // O^T += V^T P^T.  Transposed LDS reads: within each 16-lane row g, lane src
         // points at V[4g + src/4 (+16)][16dt + 4*(src%4)], and receives V[keys][d = 16dt + src].
         const int src = n;
-        if constexpr (!ROWS) lds_wave_sync();
-        const uint8_t* vr0 = vlds + (4 * g + (src >> 2)) * G::STR + G::VOFF + (4 * (src & 3)) * 2;
+        lds_wave_sync();
+        const uint8_t* vr0 = vlds + (4 * g + (src >> 2)) * G::STR + (4 * (src & 3)) * 2;
         const uint8_t* vr1 = vr0 + 16 * G::STR;
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) {
@@ -316,19 +274,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 
     const float l_run = lsum[0];
     if (l_run == 0.f) m_run = -INFINITY;                 // no selected row: an empty partial
-    if constexpr (!SPLIT) {
-        if (head < H) {
-            const float inv = 1.f / l_run;
-            uint16_t* op = out + (qi * H + head) * D + 4 * g;
-#pragma unroll
-            for (int dt = 0; dt < G::NDT; ++dt) {
-                uint2 v;
-                v.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
-                v.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
-                *reinterpret_cast<uint2*>(op + 16 * dt) = v;
-            }
-        }
-    } else {
+    {
         // Split-K: the workgroup's 4 waves hold 4 consecutive splits of one (query, head
         // group).  Merge them through LDS (the V tiles are no longer needed) and write
         // one partial: unnormalised O^T [16 heads][D] and (max, sum) per head.
@@ -363,6 +309,205 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
                 po[16 * D + 2 * hn] = M;
                 po[16 * D + 2 * hn + 1] = den;
             }
+        }
+    }
+}
+
+// Prefill: one wave per (query, group of 16 heads), staging each step's K half and then
+// its V half through one half-size LDS tile.  One register set holds the next step's
+// halves: its K loads go out as soon as this step's K is in LDS, its V loads as soon as
+// this step's V is, so loads stay in flight across the QK and PV work.  Half the LDS tile
+// and one register set (about 150 VGPRs) fit three waves per SIMD.
+template <int D>
+struct HalfGeom {
+    static constexpr int NDC = D / 32;  // K=32 chunks of the QK^T contraction
+    static constexpr int NDT = D / 16;  // 16-wide d tiles of the output
+    static constexpr int RB = 4 * D;    // bytes per KV row: K[d] then V[d], bf16
+    static constexpr int HB = 2 * D;    // bytes per half (K or V)
+    static constexpr int PPH = HB / 16; // 16-byte pieces per half
+    static constexpr int RPI = 64 / PPH;    // half rows per load instruction
+    static constexpr int NI = KT / RPI;     // load instructions per half per step
+    static constexpr int HSTR = HB + 16;    // LDS bytes per staged half row (16-byte skew)
+    static_assert(NI % 4 == 0 && 64 % PPH == 0, "row offsets are read four at a time");
+};
+
+template <int D>
+__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_half_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
+    uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
+    float scale_log2) {
+    using G = HalfGeom<D>;
+    __shared__ __attribute__((aligned(16))) uint8_t tile_all[ATT_NW][KT * G::HSTR];
+    __shared__ __attribute__((aligned(16))) uint32_t ioff_all[ATT_NW][KT];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15, g = lane >> 4;
+    const int HG = (H + 15) / 16;
+    const int64_t item = (int64_t)blockIdx.x * ATT_NW + wv;
+    const int hg = (int)(item % HG);
+    const int64_t qi = item / HG;
+    if (qi >= nq) return;
+    uint8_t* tile = tile_all[wv];
+    uint32_t* ioff = ioff_all[wv];
+    const int seq = (int)(qi / q_per_seq);
+    const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
+    const int32_t* irow = idx + qi * k;
+    const int head = 16 * hg + n;
+
+    i32x4 qf[G::NDC];                                    // Q^T fragments: head n, d = 32*dc + 8g .. +7
+#pragma unroll
+    for (int dc = 0; dc < G::NDC; ++dc) {
+        i32x4 v = {0, 0, 0, 0};
+        if (head < H) v = *reinterpret_cast<const i32x4*>(q + (qi * H + head) * D + 32 * dc + 8 * g);
+        qf[dc] = v;
+    }
+    // Entry j0 + (lane & 31), clamped into the row; stage() masks lanes past the row or >= 32.
+    // Nothing uses the value until that step is staged, so the wait for it lands there.
+    auto load_idx = [&](int j0) -> int { return irow[min(j0 + (lane & 31), k - 1)]; };
+    int idx_next = load_idx(0), idx_after = load_idx(KT);   // in flight with the scan below
+    int j_last = -1;                                      // steps after the last real entry are not run
+    for (int jb = 0; jb < k; jb += 64 * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {                    // unconditional (clamped) loads: one wait for all eight
+            const int j = jb + 64 * u + lane;
+            v[u] = irow[min(j, k - 1)];
+            v[u] = j < k ? v[u] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if ((uint32_t)v[u] < (uint32_t)Lk) j_last = max(j_last, jb + 64 * u + lane);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
+    const int nsteps = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / KT + 1);   // wave-uniform loop
+    __builtin_amdgcn_s_waitcnt(0);
+
+    f32x4 o[G::NDT];
+#pragma unroll
+    for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -1e30f;                                // reference max of the head (log2 units)
+    f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
+    const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
+    const uint32_t piece = (lane % G::PPH) * 16;
+    uint32_t roff[G::NI];                                // row offsets of the step being loaded
+    i32x4 kraw[G::NI], vraw[G::NI];                      // that step's K and V halves, as loaded
+    // Row offsets of a step through the wave's LDS words, de-interleaved so each lane reads
+    // its load addresses as one vector: entry RPI*i + r -> slot r*NI + i.  Returns the valid mask.
+    auto stage = [&](int raw, int j0) -> uint32_t {
+        __builtin_amdgcn_sched_barrier(0);
+        // -1, past the KV rows, past the idx row or a lane >= 32: no row
+        const bool ok = (uint32_t)raw < (uint32_t)Lk && j0 + lane < k && lane < 32;
+        const uint32_t valid = (uint32_t)__ballot(ok);
+        if (lane < KT) ioff[(lane % G::RPI) * G::NI + lane / G::RPI] = (ok ? (uint32_t)raw : 0u) * (uint32_t)G::RB;
+        lds_wave_sync();
+#pragma unroll
+        for (int i = 0; i < G::NI; i += 4) {
+            const u32x4 w = *reinterpret_cast<const u32x4*>(ioff + (lane / G::PPH) * G::NI + i);
+            roff[i] = w[0]; roff[i + 1] = w[1]; roff[i + 2] = w[2]; roff[i + 3] = w[3];
+        }
+        return valid;
+    };
+    auto write_half = [&](const i32x4* raw) {
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i)
+            *reinterpret_cast<i32x4*>(tile + (G::RPI * i + lane / G::PPH) * G::HSTR + (lane % G::PPH) * 16) = raw[i];
+        lds_wave_sync();
+    };
+
+    uint32_t valid = 0;
+    if (nsteps > 0) {
+        valid = stage(idx_next, 0);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) kraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));
+        __builtin_amdgcn_sched_barrier(0);               // every K load before any V load, as in the loop
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) vraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + G::HB + piece));
+        idx_next = idx_after;
+    }
+    for (int t = 0; t < nsteps; ++t) {
+        // K half of step t -> LDS; then the next step's K loads (its entries were fetched a step ago)
+        write_half(kraw);
+        const uint32_t valid_next = stage(idx_next, (t + 1) * KT);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) kraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));
+        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e
+        f32x4 s[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < G::NDC; ++dc) {
+                const i32x4 kf = *reinterpret_cast<const i32x4*>(tile + (16 * kt + n) * G::HSTR + 64 * dc + 16 * g);
+                acc = mfma_bf16_k32(kf, qf[dc], acc);
+            }
+            s[kt] = acc;
+        }
+        lds_wave_sync();                                 // K reads done: the tile takes V next
+        float x[8];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[4 * kt + e] = s[kt][e];
+        if (valid != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!((valid >> (16 * kt + 4 * g + e)) & 1u)) x[4 * kt + e] = -INFINITY;
+        }
+        float tmax = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tmax = fmax_nan(tmax, x[e]);
+        tmax = max_xor32(max_xor16(tmax)) * scale_log2;
+        if (__ballot(tmax > m_run + RESCALE_LOG2)) {
+            const float m_new = fmaxf(m_run, tmax);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int dt = 0; dt < G::NDT; ++dt) o[dt] *= alpha;
+            lsum *= alpha;
+            m_run = m_new;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
+        i32x4 pf;
+        pf[0] = (int)pack_bf16x2(x[0], x[1]);
+        pf[1] = (int)pack_bf16x2(x[2], x[3]);
+        pf[2] = (int)pack_bf16x2(x[4], x[5]);
+        pf[3] = (int)pack_bf16x2(x[6], x[7]);
+        // V half of step t -> LDS; then the entries two steps ahead, then the next step's V loads
+        write_half(vraw);
+        idx_next = load_idx((t + 2) * KT);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) vraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + G::HB + piece));
+        // O^T += V^T P^T (transposed LDS reads), l += ones^T P^T
+        const int src = n;
+        const uint8_t* vr0 = tile + (4 * g + (src >> 2)) * G::HSTR + (4 * (src & 3)) * 2;
+        const uint8_t* vr1 = vr0 + 16 * G::HSTR;
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) {
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr0 + 32 * dt));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr1 + 32 * dt));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, a0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, a1);
+            const i32x4 vf = {(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1]};
+            o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
+        }
+        lsum = mfma_bf16_k32(ones, pf, lsum);
+        lds_wave_sync();                                 // V reads done: the tile takes K next
+        valid = valid_next;
+    }
+    __builtin_amdgcn_s_waitcnt(0);                       // the last step's prefetches
+    if (head < H) {
+        const float inv = 1.f / lsum[0];
+        uint16_t* op = out + (qi * H + head) * D + 4 * g;
+#pragma unroll
+        for (int dt = 0; dt < G::NDT; ++dt) {
+            uint2 v;
+            v.x = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+            v.y = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+            *reinterpret_cast<uint2*>(op + 16 * dt) = v;
         }
     }
 }
@@ -426,13 +571,13 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     const int64_t blocks = (items + ATT_NW - 1) / ATT_NW;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
-        hipLaunchKernelGGL((sparse_attn_kernel<D, false>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
-                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.ws,
-                           a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, 1, scale_log2);
+        hipLaunchKernelGGL((sparse_attn_half_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+                           (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out,
+                           a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((sparse_attn_kernel<D, true>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
-                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out, a.ws,
+    hipLaunchKernelGGL((sparse_attn_split_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, a.ws,
                        a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, a.nsplit, scale_log2);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
     };
     auto load_entry = [&](int e0) -> int {                    // raw idx of entry e0 + lane (lanes < 32)
         const int e = e0 + (lane & 31);
-        return (e < e_end && lane < 32) ? irow[e] : -1;
+        const int v = irow[min(e, e_end - 1)];                // unconditional load: no branch around it
+        return (e < e_end && lane < 32) ? v : -1;
     };
     auto issue = [&](Tile& T, int raw, const uint8_t* kvb) {
         __builtin_amdgcn_sched_barrier(0);
@@ -242,12 +243,26 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
     }
 
     // The indexer's distribution over S_t: log2 r = I*log2(e) - log2 sum exp2(I*log2(e)).
+    // Entries go eight per lane at a time, with unconditional (clamped) loads, so each
+    // block costs one memory round trip.
     constexpr float LOG2E = 1.4426950408889634f;
+    auto for_entries = [&](auto&& f) {                        // f(entry, score*log2e) for the wave's entries in S_t
+        for (int eb = e_begin; eb < e_end; eb += 64 * 8) {
+            int sv[8];
+            float iv[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) sv[u] = irow[min(eb + 64 * u + lane, e_end - 1)];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) iv[u] = srow[min((uint32_t)sv[u], (uint32_t)(vis - 1))] * LOG2E;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int e = eb + 64 * u + lane;
+                if (e < e_end && (uint32_t)sv[u] < (uint32_t)vis) f(e, iv[u]);
+            }
+        }
+    };
     float imax = -INFINITY;
-    for (int e = e_begin + lane; e < e_end; e += 64) {
-        const int s = irow[e];
-        if ((uint32_t)s < (uint32_t)vis) imax = fmaxf(imax, srow[s] * LOG2E);
-    }
+    for_entries([&](int, float v) { imax = fmaxf(imax, v); });
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) imax = fmaxf(imax, __shfl_xor(imax, sh));
     if (lane == 0) wred[wv] = imax;
@@ -257,10 +272,7 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
     for (int w = 0; w < DW; ++w) GM = fmaxf(GM, wred[w]);
     __syncthreads();
     float isum = 0.f;
-    for (int e = e_begin + lane; e < e_end; e += 64) {
-        const int s = irow[e];
-        if ((uint32_t)s < (uint32_t)vis) isum += __builtin_amdgcn_exp2f(srow[s] * LOG2E - GM);
-    }
+    for_entries([&](int, float v) { isum += __builtin_amdgcn_exp2f(v - GM); });
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) isum += __shfl_xor(isum, sh);
     if (lane == 0) wred[wv] = isum;
@@ -271,12 +283,10 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
     __syncthreads();
     const float lse2 = GM + __builtin_amdgcn_logf(IZ);         // v_log_f32 is log2
     float part = 0.f;
-    for (int e = e_begin + lane; e < e_end; e += 64) {
-        const int s = irow[e];
+    for_entries([&](int e, float v) {
         const float p = p_lds[e];
-        if ((uint32_t)s < (uint32_t)vis && p > 0.f)
-            part += p * (__builtin_amdgcn_logf(p) - (srow[s] * LOG2E - lse2));
-    }
+        if (p > 0.f) part += p * (__builtin_amdgcn_logf(p) - (v - lse2));
+    });
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) part += __shfl_xor(part, sh);
     if (lane == 0) wred[wv] = part;
