@@ -204,6 +204,12 @@ def kernel_rooflines(cfg, layers, ws):
     out["attention"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                         "frac": round(gbs / PEAK_HBM_GBS, 4), "ms": round(ms, 4),
                         "work": f"{by:.4g} B = 512 B per selected [K|V] row x {rows} rows + q, out, idx"}
+    g_ms = gather_ceiling_ms(layers[1]["kv"], idx3)
+    if g_ms:
+        # the same rows read by a kernel that does nothing else (libicprobe.so): the
+        # attention's address stream without its math
+        out["attention"]["gather_only_ms"] = round(g_ms, 4)
+        out["attention"]["frac_of_gather_only"] = round(g_ms / ms, 4)
     # NEXT-3: distillation loss forward of the first F layer serving itself and its three S layers
     # (the call recomputes the indexer scores in the stack's tiles; the loss kernel's own time is
     # the call minus those indexer launches, timed above as chunked_ms)
@@ -225,6 +231,30 @@ def kernel_rooflines(cfg, layers, ws):
                                   f"{len(served)} + q, idx, scores, kl (read twice: two sweeps)",
                           "method": "call minus the indexer's tiled launches"}
     return out
+
+
+def gather_ceiling_ms(kv, idx3):
+    """Time of a pure gather of the rows idx3 [1, L, k] names from kv [1, L, 2, d] (libicprobe.so)."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "libicprobe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.icp_gather_rows.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nq, k = idx3.shape[1], idx3.shape[2]
+    Lk, row_bytes = kv.shape[1], kv.shape[2] * kv.shape[3] * 2
+    out = torch.empty(nq * 64, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream()
+
+    def launch():
+        r = lib.icp_gather_rows(ctypes.c_void_p(kv.data_ptr()), ctypes.c_void_p(idx3.data_ptr()), nq, k, Lk, row_bytes,
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        if r != 0:
+            raise RuntimeError(f"icp_gather_rows failed: hipError {r}")
+    launch()
+    return timed_events(launch, 5)
 
 
 def mfma_ceiling():

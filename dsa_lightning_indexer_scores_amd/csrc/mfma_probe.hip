@@ -1,6 +1,7 @@
 // Sustained rates of this GPU, measured so that the kernels' roofline fractions can
-// be read against what the hardware actually sustains: fp8 MFMA throughput, and the
-// HBM read bandwidth of a plain streaming kernel.
+// be read against what the hardware actually sustains: fp8 MFMA throughput, the
+// HBM read bandwidth of a plain streaming kernel, and the rate of a pure row gather
+// over a given index list (the sparse attention's address stream without its math).
 //
 // Each wave runs a stream of independent v_mfma_f32_16x16x128_f8f6f4 over 8 A
 // slabs and 2 B slabs (the shape of an indexer tile loop).  With random=0 the
@@ -78,7 +79,73 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const int4* __restrict
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
+// One wave per query row of idx [nq, k]: every 32 entries, the rows' bytes are read with
+// coalesced 16-byte loads (64 lanes cover 64 * 16 / row_bytes rows per instruction; row
+// offsets de-interleaved through LDS as in the attention kernel), two steps in flight,
+// and folded into an XOR that keeps the loads live.  Entries < 0 or >= Lk read row 0.
+template <int ROWB>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ kv, const int32_t* __restrict__ idx,
+                                                          int nq, int k, int Lk, int* __restrict__ out) {
+    constexpr int KTG = 32, PPR = ROWB / 16, RPI = 64 / PPR, NI = KTG / RPI;
+    __shared__ __attribute__((aligned(16))) uint32_t ioff_all[4][KTG];
+    const int lane = threadIdx.x & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int qi = blockIdx.x * 4 + wv;
+    if (qi >= nq) return;
+    const int32_t* irow = idx + (int64_t)qi * k;
+    uint32_t* ioff = ioff_all[wv];
+    const uint32_t piece = (lane % PPR) * 16;
+    const int nsteps = __builtin_amdgcn_readfirstlane((k + KTG - 1) / KTG);
+    int4 acc = make_int4(0, 0, 0, 0);
+    int4 raw[2][NI];
+    auto issue = [&](int s, int slot) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int j = s * KTG + (lane & 31);
+        const int v = irow[min(j, k - 1)];
+        const bool ok = j < k && lane < 32 && (uint32_t)v < (uint32_t)Lk;
+        if (lane < KTG) ioff[(lane % RPI) * NI + lane / RPI] = (ok ? (uint32_t)v : 0u) * (uint32_t)ROWB;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        uint32_t roff[NI];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) roff[i] = ioff[(lane / PPR) * NI + i];
+#pragma unroll
+        for (int i = 0; i < NI; ++i) raw[slot][i] = *reinterpret_cast<const int4*>(kv + (roff[i] + piece));
+    };
+    auto fold = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            acc.x ^= raw[slot][i].x; acc.y ^= raw[slot][i].y; acc.z ^= raw[slot][i].z; acc.w ^= raw[slot][i].w;
+        }
+    };
+    issue(0, 0);
+    for (int s = 0; s < nsteps; s += 2) {
+        issue(min(s + 1, nsteps - 1), 1);
+        fold(0);
+        issue(min(s + 2, nsteps - 1), 0);
+        if (s + 1 < nsteps) fold(1);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    out[(int64_t)qi * 64 + lane] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+}
+
 }  // namespace
+
+// Pure gather of the rows idx [nq, k] names from kv (row_bytes 256 or 512 per row, Lk
+// rows); out needs nq * 64 ints.  Returns a hipError_t.
+extern "C" __attribute__((visibility("default"))) int icp_gather_rows(const void* kv, const int32_t* idx, int nq, int k,
+                                                                     int Lk, int row_bytes, int* out, void* stream) {
+    if (kv == nullptr || idx == nullptr || out == nullptr || nq < 1 || k < 1 || Lk < 1) return (int)hipErrorInvalidValue;
+    const dim3 grid((nq + 3) / 4);
+    if (row_bytes == 512)
+        hipLaunchKernelGGL(gather_rows_kernel<512>, grid, dim3(256), 0, (hipStream_t)stream,
+                           static_cast<const uint8_t*>(kv), idx, nq, k, Lk, out);
+    else if (row_bytes == 256)
+        hipLaunchKernelGGL(gather_rows_kernel<256>, grid, dim3(256), 0, (hipStream_t)stream,
+                           static_cast<const uint8_t*>(kv), idx, nq, k, Lk, out);
+    else
+        return (int)hipErrorInvalidValue;
+    return (int)hipGetLastError();
+}
 
 // Reads `bytes` (a multiple of 16) from `src` with `blocks` workgroups of 256 threads;
 // out needs blocks * 256 ints.  Returns a hipError_t.
