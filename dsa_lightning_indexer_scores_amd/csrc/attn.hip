@@ -6,20 +6,16 @@
 //     out = sum_s softmax_s(q . K[s] / sqrt(d)) V[s],   s over idx (-1 skipped),
 // with one KV head shared by all query heads; a token's row is [K | V].
 //
-// One wave owns one (query, group of 16 heads[, key split]).  Per step of 32
-// selected rows:
-//   prefill: the rows are gathered with fully coalesced 16-byte loads (one
-//       instruction covers two K or V halves of 256 bytes; every 4-lane quad
-//       reads one 64-byte run).  Gathering K straight into MFMA fragments
-//       (lanes 0-15 on 16 different rows) makes each quad touch four rows, and
-//       the vector-memory address unit then bounds the kernel.  The K halves go
-//       through a half-size wave LDS tile for the QK^T fragments, then the V
-//       halves through the same tile for the transposed PV reads.  One register
-//       set holds the next step's halves, so about 150 VGPRs and 35 KB of LDS
-//       per workgroup give three waves per SIMD;
+// One wave owns one (query, group of 16 heads[, key split]).
+//   prefill: the selected rows go straight from memory into the wave's LDS with
+//       global_load_lds_dwordx4 (64 lanes x 16 bytes: two whole 512-byte rows per
+//       instruction, fully coalesced), with no VGPR round trip and no LDS write
+//       instructions; the idx row reaches LDS the same way.  Few registers and
+//       19 KB of LDS per wave give eight waves per CU, and the CU's LDS holds the
+//       bytes in flight.  Steps are units of 16 rows;
 //   split-K decode, latency-bound with one or two steps per wave, gathers K
 //       straight into fragments and stages only V;
-//   S^T (32 keys x 16 heads) = K Q^T;
+//   S^T (keys x 16 heads) = K Q^T;
 //   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
 //       lane % 16) is also the layout of O^T below, so the running max and
 //       rescale never leave the lane.  The reference max moves only when a
@@ -29,9 +25,7 @@
 //       k order matches the transposed read, so no shuffle is needed);
 //   l += ones^T P^T, one more MFMA, so the denominator sums the same bf16 P
 //       as the numerator and costs no VALU.
-// Prefill row offsets are staged through a few wave-private LDS words so each lane
-// reads its load addresses as one vector (no per-row lane reads).  Steps past a
-// query's last real idx entry are not run.
+// Steps past a query's last real idx entry are not run.
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
 // workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
 // the workgroups' partials in split order, so results are deterministic.  (A
@@ -313,32 +307,59 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
 }
 
-// Prefill: one wave per (query, group of 16 heads), staging each step's K half and then
-// its V half through one half-size LDS tile.  One register set holds the next step's
-// halves: its K loads go out as soon as this step's K is in LDS, its V loads as soon as
-// this step's V is, so loads stay in flight across the QK and PV work.  Half the LDS tile
-// and one register set (about 150 VGPRs) fit three waves per SIMD.
+// Prefill with the gather going straight into LDS (global_load_lds_dwordx4): a wave's
+// selected rows travel HBM/L2 -> LDS with no VGPR round trip and no LDS write
+// instructions, so the wave needs few registers and the CU's LDS holds the bytes in
+// flight.  Per wave: a ring of DG::NF units of 16 whole [K|V] rows and a ring of three
+// 256-entry chunks of its idx row, both filled by the same DMA.  While unit u is computed
+// (16 keys: S^T = K Q^T, online softmax, O^T += V^T P^T with K = 16), unit u + 1 is in
+// flight.  The waits are explicit vmcnt counts: the compiler does not track these loads.
+//
+// Row layout in LDS: 16-byte slot j of a unit row r holds the row's 16-byte chunk
+// j ^ swz(r), so that the K-fragment reads (16 rows, one chunk each) and the transposed
+// V reads (8 rows, two adjacent chunks each) fall on distinct banks.
 template <int D>
-struct HalfGeom {
-    static constexpr int NDC = D / 32;  // K=32 chunks of the QK^T contraction
-    static constexpr int NDT = D / 16;  // 16-wide d tiles of the output
-    static constexpr int RB = 4 * D;    // bytes per KV row: K[d] then V[d], bf16
-    static constexpr int HB = 2 * D;    // bytes per half (K or V)
-    static constexpr int PPH = HB / 16; // 16-byte pieces per half
-    static constexpr int RPI = 64 / PPH;    // half rows per load instruction
-    static constexpr int NI = KT / RPI;     // load instructions per half per step
-    static constexpr int HSTR = HB + 16;    // LDS bytes per staged half row (16-byte skew)
-    static_assert(NI % 4 == 0 && 64 % PPH == 0, "row offsets are read four at a time");
+struct DmaGeom {
+    static constexpr int NDC = D / 32;       // K=32 chunks of the QK^T contraction
+    static constexpr int NDT = D / 16;       // 16-wide d tiles of the output
+    static constexpr int RB = 4 * D;         // bytes per KV row: K[d] then V[d], bf16
+    static constexpr int NC = RB / 16;       // 16-byte chunks per row
+    static constexpr int UR = 16;            // rows per unit (one compute step)
+    static constexpr int RPI = 1024 / RB;    // rows per DMA instruction (64 lanes x 16 bytes)
+    static constexpr int NI = UR / RPI;      // DMA instructions per unit
+    static constexpr int UB = UR * RB;       // bytes per unit
+    static constexpr int NF = 2;             // units in the ring
+    static constexpr int ICH = 256;          // idx entries per ring chunk
+    static constexpr int NICH = 3;           // ring chunks
+    static constexpr int UPC = ICH / UR;     // units per chunk
+    static constexpr int VC0 = 2 * D / 16;   // first chunk of the V half
+    static_assert(NC >= 16 && 1024 % RB == 0 && UR % RPI == 0, "row must be 256 or 512 bytes");
 };
 
+__device__ __forceinline__ uint32_t dma_swz(int r) { return (uint32_t)(((r & 7) << 1) | ((r >> 3) & 1)); }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+// 4 bytes per lane from base + voff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
 template <int D>
-__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))) void sparse_attn_half_kernel(
+__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
     float scale_log2) {
-    using G = HalfGeom<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t tile_all[ATT_NW][KT * G::HSTR];
-    __shared__ __attribute__((aligned(16))) uint32_t ioff_all[ATT_NW][KT];
+    using G = DmaGeom<D>;
+    __shared__ __attribute__((aligned(1024))) uint8_t tile_all[ATT_NW][G::NF * G::UB];
+    __shared__ __attribute__((aligned(16))) int32_t ring_all[ATT_NW][G::NICH * G::ICH];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -348,7 +369,8 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))
     const int64_t qi = item / HG;
     if (qi >= nq) return;
     uint8_t* tile = tile_all[wv];
-    uint32_t* ioff = ioff_all[wv];
+    int32_t* ring = ring_all[wv];
+    const uint32_t tile_lds = lds_addr(tile), ring_lds = lds_addr(ring);
     const int seq = (int)(qi / q_per_seq);
     const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
     const int32_t* irow = idx + qi * k;
@@ -361,11 +383,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))
         if (head < H) v = *reinterpret_cast<const i32x4*>(q + (qi * H + head) * D + 32 * dc + 8 * g);
         qf[dc] = v;
     }
-    // Entry j0 + (lane & 31), clamped into the row; stage() masks lanes past the row or >= 32.
-    // Nothing uses the value until that step is staged, so the wait for it lands there.
-    auto load_idx = [&](int j0) -> int { return irow[min(j0 + (lane & 31), k - 1)]; };
-    int idx_next = load_idx(0), idx_after = load_idx(KT);   // in flight with the scan below
-    int j_last = -1;                                      // steps after the last real entry are not run
+    int j_last = -1;                                      // units after the last real entry are not run
     for (int jb = 0; jb < k; jb += 64 * 8) {
         int v[8];
 #pragma unroll
@@ -380,85 +398,95 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))
     }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
-    const int nsteps = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / KT + 1);   // wave-uniform loop
+    const int nunits = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / G::UR + 1);
     __builtin_amdgcn_s_waitcnt(0);
+
+    // chunk c of the idx row -> ring slot c % 3 (entries past the row repeat its last entry;
+    // the compute step masks them by position)
+    auto issue_chunk = [&](int c) {
+        const uint32_t dst = ring_lds + (uint32_t)(c % G::NICH) * (G::ICH * 4);
+#pragma unroll
+        for (int w = 0; w < G::ICH / 64; ++w)
+            dma_b32(irow, (uint32_t)min(c * G::ICH + 64 * w + lane, k - 1) * 4u, dst + 256u * w);
+    };
+    // unit u's rows -> ring stage u % NF.  Lane l of instruction i fetches chunk
+    // (l % NC) ^ swz(r) of unit row r = RPI*i + l / NC; entries outside [0, Lk) fetch row Lk - 1.
+    uint32_t cof[G::NI];
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i) {
+        const int r = G::RPI * i + lane / G::NC;
+        cof[i] = ((uint32_t)(lane % G::NC) ^ dma_swz(r)) * 16u;
+    }
+    // Returns the unit's valid rows as a 16-bit mask (wave-uniform): entry in [0, Lk) and
+    // position inside the idx row.
+    auto issue_unit = [&](int u) -> uint32_t {
+        const int32_t* ir = ring + ((u / G::UPC) % G::NICH) * G::ICH + (u % G::UPC) * G::UR;
+        const int ev = ir[lane & 15];
+        const uint32_t vmask =
+            (uint32_t)__ballot((uint32_t)ev < (uint32_t)Lk && u * G::UR + (lane & 15) < k) & 0xFFFFu;
+        uint32_t off[G::NI];
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) {
+            const uint32_t v = (uint32_t)ir[G::RPI * i + lane / G::NC];
+            off[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)G::RB + cof[i];
+        }
+        const uint32_t dst = tile_lds + (uint32_t)(u % G::NF) * G::UB;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the stage being refilled are done
+#pragma unroll
+        for (int i = 0; i < G::NI; ++i) dma_b128(kvb, off[i], dst + 1024u * i);
+        return __builtin_amdgcn_readfirstlane(vmask);
+    };
 
     f32x4 o[G::NDT];
 #pragma unroll
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -1e30f;                                // reference max of the head (log2 units)
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-    const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
-    const uint32_t piece = (lane % G::PPH) * 16;
-    uint32_t roff[G::NI];                                // row offsets of the step being loaded
-    i32x4 kraw[G::NI], vraw[G::NI];                      // that step's K and V halves, as loaded
-    // Row offsets of a step through the wave's LDS words, de-interleaved so each lane reads
-    // its load addresses as one vector: entry RPI*i + r -> slot r*NI + i.  Returns the valid mask.
-    auto stage = [&](int raw, int j0) -> uint32_t {
-        __builtin_amdgcn_sched_barrier(0);
-        // -1, past the KV rows, past the idx row or a lane >= 32: no row
-        const bool ok = (uint32_t)raw < (uint32_t)Lk && j0 + lane < k && lane < 32;
-        const uint32_t valid = (uint32_t)__ballot(ok);
-        if (lane < KT) ioff[(lane % G::RPI) * G::NI + lane / G::RPI] = (ok ? (uint32_t)raw : 0u) * (uint32_t)G::RB;
-        lds_wave_sync();
-#pragma unroll
-        for (int i = 0; i < G::NI; i += 4) {
-            const u32x4 w = *reinterpret_cast<const u32x4*>(ioff + (lane / G::PPH) * G::NI + i);
-            roff[i] = w[0]; roff[i + 1] = w[1]; roff[i + 2] = w[2]; roff[i + 3] = w[3];
-        }
-        return valid;
-    };
-    auto write_half = [&](const i32x4* raw) {
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i)
-            *reinterpret_cast<i32x4*>(tile + (G::RPI * i + lane / G::PPH) * G::HSTR + (lane % G::PPH) * 16) = raw[i];
-        lds_wave_sync();
-    };
+    const i16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
+    // lane-constant parts of the fragment addresses (row n for K, row 4g + n/4 for V)
+    const uint32_t swz_k = dma_swz(n);
+    const int vrow = 4 * g + (n >> 2);
+    const uint32_t swz_v = dma_swz(vrow);
 
-    uint32_t valid = 0;
-    if (nsteps > 0) {
-        valid = stage(idx_next, 0);
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i) kraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));
-        __builtin_amdgcn_sched_barrier(0);               // every K load before any V load, as in the loop
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i) vraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + G::HB + piece));
-        idx_next = idx_after;
+    uint32_t vmask = 0;
+    if (nunits > 0) {
+        issue_chunk(0);
+        issue_chunk(1);
+        wait_vm<G::ICH / 64>();                          // chunk 0 landed
+        vmask = issue_unit(0);
     }
-    for (int t = 0; t < nsteps; ++t) {
-        // K half of step t -> LDS; then the next step's K loads (its entries were fetched a step ago)
-        write_half(kraw);
-        const uint32_t valid_next = stage(idx_next, (t + 1) * KT);
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i) kraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));
-        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e
-        f32x4 s[2];
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) {
-                const i32x4 kf = *reinterpret_cast<const i32x4*>(tile + (16 * kt + n) * G::HSTR + 64 * dc + 16 * g);
-                acc = mfma_bf16_k32(kf, qf[dc], acc);
+    for (int u = 0; u < nunits; ++u) {
+        // the next unit goes out before this one is waited for; the idx chunk after the
+        // current one goes out when the next unit is the first of its chunk
+        uint32_t vmask_next = 0;
+        if (u + 1 < nunits) {
+            vmask_next = issue_unit(u + 1);
+            if ((u + 1) % G::UPC == 0) {
+                issue_chunk((u + 1) / G::UPC + 1);
+                wait_vm<G::NI + G::ICH / 64>();
+            } else {
+                wait_vm<G::NI>();
             }
-            s[kt] = acc;
+        } else {
+            wait_vm<0>();
         }
-        lds_wave_sync();                                 // K reads done: the tile takes V next
-        float x[8];
+        const uint8_t* st = tile + (u % G::NF) * G::UB;
+        // S^T = K Q^T: lane (n, g) gets head n, keys 4g + e
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) x[4 * kt + e] = s[kt][e];
-        if (valid != 0xFFFFFFFFu) {
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (!((valid >> (16 * kt + 4 * g + e)) & 1u)) x[4 * kt + e] = -INFINITY;
+        for (int dc = 0; dc < G::NDC; ++dc) {
+            const i32x4 kf = *reinterpret_cast<const i32x4*>(st + n * G::RB + (((uint32_t)(4 * dc + g) ^ swz_k) * 16u));
+            s = mfma_bf16_k32(kf, qf[dc], s);
         }
-        float tmax = x[0];
+        float x[4];
 #pragma unroll
-        for (int e = 1; e < 8; ++e) tmax = fmax_nan(tmax, x[e]);
+        for (int e = 0; e < 4; ++e) x[e] = s[e];
+        if (vmask != 0xFFFFu) {                          // keys 4g + e that name no row
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (!((vmask >> (4 * g + e)) & 1u)) x[e] = -INFINITY;
+        }
+        float tmax = fmax_nan(fmax_nan(x[0], x[1]), fmax_nan(x[2], x[3]));
         tmax = max_xor32(max_xor16(tmax)) * scale_log2;
         if (__ballot(tmax > m_run + RESCALE_LOG2)) {
             const float m_new = fmaxf(m_run, tmax);
@@ -469,36 +497,20 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(3))
             m_run = m_new;
         }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
-        i32x4 pf;
-        pf[0] = (int)pack_bf16x2(x[0], x[1]);
-        pf[1] = (int)pack_bf16x2(x[2], x[3]);
-        pf[2] = (int)pack_bf16x2(x[4], x[5]);
-        pf[3] = (int)pack_bf16x2(x[6], x[7]);
-        // V half of step t -> LDS; then the entries two steps ahead, then the next step's V loads
-        write_half(vraw);
-        idx_next = load_idx((t + 2) * KT);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i) vraw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + G::HB + piece));
-        // O^T += V^T P^T (transposed LDS reads), l += ones^T P^T
-        const int src = n;
-        const uint8_t* vr0 = tile + (4 * g + (src >> 2)) * G::HSTR + (4 * (src & 3)) * 2;
-        const uint8_t* vr1 = vr0 + 16 * G::HSTR;
+        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
+        const u32x2 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        const i16x4 pf = __builtin_bit_cast(i16x4, pw);
+        // O^T += V^T P^T: lane (n, g) reads 8 bytes of row 4g + n/4, d = 16*dt + 4*(n%4) .. +3
+        const uint8_t* vr = st + vrow * G::RB + 8 * (n & 1);
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) {
-            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr0 + 32 * dt));
-            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr1 + 32 * dt));
-            const u32x2 w0 = __builtin_bit_cast(u32x2, a0);
-            const u32x2 w1 = __builtin_bit_cast(u32x2, a1);
-            const i32x4 vf = {(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1]};
-            o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
+            const uint32_t c = (uint32_t)(G::VC0 + 2 * dt + ((n >> 1) & 1)) ^ swz_v;
+            const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + c * 16u));
+            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
         }
-        lsum = mfma_bf16_k32(ones, pf, lsum);
-        lds_wave_sync();                                 // V reads done: the tile takes K next
-        valid = valid_next;
+        lsum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lsum, 0, 0, 0);
+        vmask = vmask_next;
     }
-    __builtin_amdgcn_s_waitcnt(0);                       // the last step's prefetches
     if (head < H) {
         const float inv = 1.f / lsum[0];
         uint16_t* op = out + (qi * H + head) * D + 4 * g;
@@ -571,7 +583,8 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     const int64_t blocks = (items + ATT_NW - 1) / ATT_NW;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
-        hipLaunchKernelGGL((sparse_attn_half_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+        if ((int64_t)a.Lk * DmaGeom<D>::RB > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit row offsets
+        hipLaunchKernelGGL((sparse_attn_dma_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out,
                            a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2);
         return hipGetLastError();
