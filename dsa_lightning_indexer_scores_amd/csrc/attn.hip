@@ -11,11 +11,11 @@
 //       global_load_lds_dwordx4 (64 lanes x 16 bytes: two whole 512-byte rows per
 //       instruction, fully coalesced), with no VGPR round trip and no LDS write
 //       instructions; the idx row reaches LDS the same way.  Few registers and
-//       19 KB of LDS per wave give eight waves per CU, and the CU's LDS holds the
-//       bytes in flight.  Steps are units of 16 rows;
+//       18 KB of LDS per wave (one K and one V stage of 32 half rows, two idx
+//       chunks) give eight waves per CU, and the CU's LDS holds the bytes in flight;
 //   split-K decode, latency-bound with one or two steps per wave, gathers K
 //       straight into fragments and stages only V;
-//   S^T (keys x 16 heads) = K Q^T;
+//   S^T (32 keys x 16 heads) = K Q^T;
 //   online softmax in fp32 (exp2 domain) on S^T, whose lane layout (head =
 //       lane % 16) is also the layout of O^T below, so the running max and
 //       rescale never leave the lane.  The reference max moves only when a
@@ -308,14 +308,17 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 }
 
 // Prefill with the gather going straight into LDS (global_load_lds_dwordx4): a wave's
-// selected rows travel HBM/L2 -> LDS with no VGPR round trip and no LDS write
+// selected rows travel memory -> LDS with no VGPR round trip and no LDS write
 // instructions, so the wave needs few registers and the CU's LDS holds the bytes in
-// flight.  Per wave: a ring of DG::NF units of 16 whole [K|V] rows and a ring of three
-// 256-entry chunks of its idx row, both filled by the same DMA.  While unit u is computed
-// (16 keys: S^T = K Q^T, online softmax, O^T += V^T P^T with K = 16), unit u + 1 is in
-// flight.  The waits are explicit vmcnt counts: the compiler does not track these loads.
+// flight.  Per wave: one K stage and one V stage of 32 half rows each, and a ring of two
+// 256-entry chunks of its idx row, all filled by DMA.  Step s (32 keys):
+//   wait K(s); S^T = K Q^T; issue K(s+1); online softmax;
+//   wait V(s); O^T += V^T P^T, l += ones^T P^T; issue V(s+1)
+// so each half has about half a step of compute to land in, and eight waves per CU
+// overlap one another's waits.  The waits are explicit vmcnt counts: the compiler does
+// not see these loads.
 //
-// Row layout in LDS: 16-byte slot j of a unit row r holds the row's 16-byte chunk
+// Half-row layout in LDS: 16-byte slot j of staged row r holds the half's chunk
 // j ^ swz(r), so that the K-fragment reads (16 rows, one chunk each) and the transposed
 // V reads (8 rows, two adjacent chunks each) fall on distinct banks.
 template <int D>
@@ -323,20 +326,22 @@ struct DmaGeom {
     static constexpr int NDC = D / 32;       // K=32 chunks of the QK^T contraction
     static constexpr int NDT = D / 16;       // 16-wide d tiles of the output
     static constexpr int RB = 4 * D;         // bytes per KV row: K[d] then V[d], bf16
-    static constexpr int NC = RB / 16;       // 16-byte chunks per row
-    static constexpr int UR = 16;            // rows per unit (one compute step)
-    static constexpr int RPI = 1024 / RB;    // rows per DMA instruction (64 lanes x 16 bytes)
-    static constexpr int NI = UR / RPI;      // DMA instructions per unit
-    static constexpr int UB = UR * RB;       // bytes per unit
-    static constexpr int NF = 2;             // units in the ring
+    static constexpr int HB = 2 * D;         // bytes per half row
+    static constexpr int NCH = HB / 16;      // 16-byte chunks per half row
+    static constexpr int RPI = 1024 / HB;    // half rows per DMA instruction (64 lanes x 16 bytes)
+    static constexpr int NI = KT / RPI;      // DMA instructions per half step
+    static constexpr int SB = KT * HB;       // bytes per stage
     static constexpr int ICH = 256;          // idx entries per ring chunk
-    static constexpr int NICH = 3;           // ring chunks
-    static constexpr int UPC = ICH / UR;     // units per chunk
-    static constexpr int VC0 = 2 * D / 16;   // first chunk of the V half
-    static_assert(NC >= 16 && 1024 % RB == 0 && UR % RPI == 0, "row must be 256 or 512 bytes");
+    static constexpr int SPC = ICH / KT;     // steps per chunk
+    static_assert((NCH == 16 || NCH == 8) && KT % RPI == 0, "half row must be 256 or 128 bytes");
+    // Slot permutation of staged row r (only r % 16 matters).  Bijective on the 16 rows
+    // of a K tile modulo the row's bank phase, and the 8 rows of a transposed V read get
+    // distinct chunk pairs.
+    __device__ static uint32_t swz(int r) {
+        return NCH == 16 ? (uint32_t)(((r & 7) << 1) | ((r >> 3) & 1))
+                         : (uint32_t)((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+    }
 };
-
-__device__ __forceinline__ uint32_t dma_swz(int r) { return (uint32_t)(((r & 7) << 1) | ((r >> 3) & 1)); }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
     return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
@@ -358,8 +363,9 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
     float scale_log2) {
     using G = DmaGeom<D>;
-    __shared__ __attribute__((aligned(1024))) uint8_t tile_all[ATT_NW][G::NF * G::UB];
-    __shared__ __attribute__((aligned(16))) int32_t ring_all[ATT_NW][G::NICH * G::ICH];
+    constexpr int CI = G::ICH / 64;                      // DMA instructions per idx chunk
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[ATT_NW][2][G::SB];   // K, V
+    __shared__ __attribute__((aligned(16))) int32_t ring_all[ATT_NW][2 * G::ICH];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -368,9 +374,10 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const int hg = (int)(item % HG);
     const int64_t qi = item / HG;
     if (qi >= nq) return;
-    uint8_t* tile = tile_all[wv];
-    int32_t* ring = ring_all[wv];
-    const uint32_t tile_lds = lds_addr(tile), ring_lds = lds_addr(ring);
+    const uint8_t* kst = stage_all[wv][0];
+    const uint8_t* vst = stage_all[wv][1];
+    const int32_t* ring = ring_all[wv];
+    const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst), ring_lds = lds_addr(ring);
     const int seq = (int)(qi / q_per_seq);
     const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
     const int32_t* irow = idx + qi * k;
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         if (head < H) v = *reinterpret_cast<const i32x4*>(q + (qi * H + head) * D + 32 * dc + 8 * g);
         qf[dc] = v;
     }
-    int j_last = -1;                                      // units after the last real entry are not run
+    int j_last = -1;                                      // steps after the last real entry are not run
     for (int jb = 0; jb < k; jb += 64 * 8) {
         int v[8];
 #pragma unroll
@@ -398,43 +405,40 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
 #pragma unroll
     for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
-    const int nunits = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / G::UR + 1);
+    const int nsteps = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / KT + 1);
     __builtin_amdgcn_s_waitcnt(0);
 
-    // chunk c of the idx row -> ring slot c % 3 (entries past the row repeat its last entry;
-    // the compute step masks them by position)
+    // chunk c of the idx row -> ring slot c % 2 (entries past the row repeat its last entry;
+    // the valid mask drops them by position)
     auto issue_chunk = [&](int c) {
-        const uint32_t dst = ring_lds + (uint32_t)(c % G::NICH) * (G::ICH * 4);
+        const uint32_t dst = ring_lds + (uint32_t)(c & 1) * (G::ICH * 4);
 #pragma unroll
-        for (int w = 0; w < G::ICH / 64; ++w)
+        for (int w = 0; w < CI; ++w)
             dma_b32(irow, (uint32_t)min(c * G::ICH + 64 * w + lane, k - 1) * 4u, dst + 256u * w);
     };
-    // unit u's rows -> ring stage u % NF.  Lane l of instruction i fetches chunk
-    // (l % NC) ^ swz(r) of unit row r = RPI*i + l / NC; entries outside [0, Lk) fetch row Lk - 1.
+    // Lane l of instruction i fetches chunk (l % NCH) ^ swz(r) of half row r = RPI*i + l / NCH.
     uint32_t cof[G::NI];
 #pragma unroll
-    for (int i = 0; i < G::NI; ++i) {
-        const int r = G::RPI * i + lane / G::NC;
-        cof[i] = ((uint32_t)(lane % G::NC) ^ dma_swz(r)) * 16u;
-    }
-    // Returns the unit's valid rows as a 16-bit mask (wave-uniform): entry in [0, Lk) and
-    // position inside the idx row.
-    auto issue_unit = [&](int u) -> uint32_t {
-        const int32_t* ir = ring + ((u / G::UPC) % G::NICH) * G::ICH + (u % G::UPC) * G::UR;
-        const int ev = ir[lane & 15];
-        const uint32_t vmask =
-            (uint32_t)__ballot((uint32_t)ev < (uint32_t)Lk && u * G::UR + (lane & 15) < k) & 0xFFFFu;
-        uint32_t off[G::NI];
+    for (int i = 0; i < G::NI; ++i)
+        cof[i] = ((uint32_t)(lane % G::NCH) ^ G::swz(G::RPI * i + lane / G::NCH)) * 16u;
+    uint32_t roff[G::NI];                                // row offsets of the step being fetched
+    // Row offsets of step s from the ring (entries outside [0, Lk) fetch row Lk - 1) and its
+    // valid keys as a wave-uniform 32-bit mask (entry in [0, Lk) and inside the idx row).
+    auto offsets = [&](int s) -> uint32_t {
+        const int32_t* ir = ring + ((s / G::SPC) & 1) * G::ICH + (s % G::SPC) * KT;
+        const int ev = ir[lane & 31];
+        const uint32_t vm = (uint32_t)__ballot((uint32_t)ev < (uint32_t)Lk && s * KT + (lane & 31) < k);
 #pragma unroll
         for (int i = 0; i < G::NI; ++i) {
-            const uint32_t v = (uint32_t)ir[G::RPI * i + lane / G::NC];
-            off[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)G::RB + cof[i];
+            const uint32_t v = (uint32_t)ir[G::RPI * i + lane / G::NCH];
+            roff[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)G::RB + cof[i];
         }
-        const uint32_t dst = tile_lds + (uint32_t)(u % G::NF) * G::UB;
+        return __builtin_amdgcn_readfirstlane(vm);
+    };
+    auto issue_half = [&](uint32_t dst, uint32_t half_off) {
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // reads of the stage being refilled are done
 #pragma unroll
-        for (int i = 0; i < G::NI; ++i) dma_b128(kvb, off[i], dst + 1024u * i);
-        return __builtin_amdgcn_readfirstlane(vmask);
+        for (int i = 0; i < G::NI; ++i) dma_b128(kvb, roff[i] + half_off, dst + 1024u * i);
     };
 
     f32x4 o[G::NDT];
@@ -442,51 +446,58 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int dt = 0; dt < G::NDT; ++dt) o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -1e30f;                                // reference max of the head (log2 units)
     f32x4 lsum = {0.f, 0.f, 0.f, 0.f};
-    const i16x4 ones = {0x3F80, 0x3F80, 0x3F80, 0x3F80};
-    // lane-constant parts of the fragment addresses (row n for K, row 4g + n/4 for V)
-    const uint32_t swz_k = dma_swz(n);
-    const int vrow = 4 * g + (n >> 2);
-    const uint32_t swz_v = dma_swz(vrow);
+    const i32x4 ones = {0x3F803F80, 0x3F803F80, 0x3F803F80, 0x3F803F80};
+    const uint32_t swz_k = G::swz(n);
+    const int vrow = 4 * g + (n >> 2);                    // transposed V reads: rows vrow and vrow + 16
+    const uint32_t swz_v = G::swz(vrow);
 
     uint32_t vmask = 0;
-    if (nunits > 0) {
+    if (nsteps > 0) {
         issue_chunk(0);
         issue_chunk(1);
-        wait_vm<G::ICH / 64>();                          // chunk 0 landed
-        vmask = issue_unit(0);
+        wait_vm<CI>();                                   // chunk 0 landed
+        vmask = offsets(0);
+        issue_half(k_lds, 0);
+        issue_half(v_lds, G::HB);
     }
-    for (int u = 0; u < nunits; ++u) {
-        // the next unit goes out before this one is waited for; the idx chunk after the
-        // current one goes out when the next unit is the first of its chunk
-        uint32_t vmask_next = 0;
-        if (u + 1 < nunits) {
-            vmask_next = issue_unit(u + 1);
-            if ((u + 1) % G::UPC == 0) {
-                issue_chunk((u + 1) / G::UPC + 1);
-                wait_vm<G::NI + G::ICH / 64>();
-            } else {
-                wait_vm<G::NI>();
+    for (int s = 0; s < nsteps; ++s) {
+        const bool more = s + 1 < nsteps;
+        // a chunk issued after V(s) (at the end of step s - 1) is still allowed in flight
+        const bool chunk_after_v = s > 0 && s % G::SPC == 0;
+        if (chunk_after_v) wait_vm<G::NI + CI>(); else wait_vm<G::NI>();            // K(s) landed
+        // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e
+        f32x4 sc[2];
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int dc = 0; dc < G::NDC; ++dc) {
+                const i32x4 kf = *reinterpret_cast<const i32x4*>(kst + (16 * kt + n) * G::HB +
+                                                                 (((uint32_t)(4 * dc + g) ^ swz_k) * 16u));
+                acc = mfma_bf16_k32(kf, qf[dc], acc);
             }
-        } else {
-            wait_vm<0>();
+            sc[kt] = acc;
         }
-        const uint8_t* st = tile + (u % G::NF) * G::UB;
-        // S^T = K Q^T: lane (n, g) gets head n, keys 4g + e
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < G::NDC; ++dc) {
-            const i32x4 kf = *reinterpret_cast<const i32x4*>(st + n * G::RB + (((uint32_t)(4 * dc + g) ^ swz_k) * 16u));
-            s = mfma_bf16_k32(kf, qf[dc], s);
+        uint32_t vmask_next = 0;
+        if (more) {
+            vmask_next = offsets(s + 1);
+            issue_half(k_lds, 0);                        // K(s+1)
         }
-        float x[4];
+        float x[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = s[e];
-        if (vmask != 0xFFFFu) {                          // keys 4g + e that name no row
+        for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                if (!((vmask >> (4 * g + e)) & 1u)) x[e] = -INFINITY;
+            for (int e = 0; e < 4; ++e) x[4 * kt + e] = sc[kt][e];
+        if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (!((vmask >> (16 * kt + 4 * g + e)) & 1u)) x[4 * kt + e] = -INFINITY;
         }
-        float tmax = fmax_nan(fmax_nan(x[0], x[1]), fmax_nan(x[2], x[3]));
+        float tmax = x[0];
+#pragma unroll
+        for (int e = 1; e < 8; ++e) tmax = fmax_nan(tmax, x[e]);
         tmax = max_xor32(max_xor16(tmax)) * scale_log2;
         if (__ballot(tmax > m_run + RESCALE_LOG2)) {
             const float m_new = fmaxf(m_run, tmax);
@@ -497,20 +508,39 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
             m_run = m_new;
         }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
-        const u32x2 pw = {pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
-        const i16x4 pf = __builtin_bit_cast(i16x4, pw);
-        // O^T += V^T P^T: lane (n, g) reads 8 bytes of row 4g + n/4, d = 16*dt + 4*(n%4) .. +3
-        const uint8_t* vr = st + vrow * G::RB + 8 * (n & 1);
+        for (int e = 0; e < 8; ++e) x[e] = __builtin_amdgcn_exp2f(fmaf(x[e], scale_log2, -m_run));
+        i32x4 pf;
+        pf[0] = (int)pack_bf16x2(x[0], x[1]);
+        pf[1] = (int)pack_bf16x2(x[2], x[3]);
+        pf[2] = (int)pack_bf16x2(x[4], x[5]);
+        pf[3] = (int)pack_bf16x2(x[6], x[7]);
+        // V(s) landed: what may still be in flight is the chunk issued after it and K(s+1)
+        if (more) {
+            if (chunk_after_v) wait_vm<G::NI + CI>(); else wait_vm<G::NI>();
+        } else {
+            if (chunk_after_v) wait_vm<CI>(); else wait_vm<0>();
+        }
+        // O^T += V^T P^T: lane (n, g) reads 8 bytes of rows vrow and vrow + 16, d = 16*dt + 4*(n%4) .. +3
+        const uint8_t* vr0 = vst + vrow * G::HB + 8 * (n & 1);
+        const uint8_t* vr1 = vr0 + 16 * G::HB;
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) {
-            const uint32_t c = (uint32_t)(G::VC0 + 2 * dt + ((n >> 1) & 1)) ^ swz_v;
-            const i16x4 vf = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + c * 16u));
-            o[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, o[dt], 0, 0, 0);
+            const uint32_t c = ((uint32_t)(2 * dt + ((n >> 1) & 1)) ^ swz_v) * 16u;
+            const i16x4 a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr0 + c));
+            const i16x4 a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr1 + c));
+            const u32x2 w0 = __builtin_bit_cast(u32x2, a0);
+            const u32x2 w1 = __builtin_bit_cast(u32x2, a1);
+            const i32x4 vf = {(int)w0[0], (int)w0[1], (int)w1[0], (int)w1[1]};
+            o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
         }
-        lsum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones, pf, lsum, 0, 0, 0);
+        lsum = mfma_bf16_k32(ones, pf, lsum);
+        if (more) {
+            issue_half(v_lds, G::HB);                    // V(s+1)
+            if ((s + 1) % G::SPC == 0) issue_chunk((s + 1) / G::SPC + 1);
+        }
         vmask = vmask_next;
     }
+    __builtin_amdgcn_s_waitcnt(0);                       // an idx chunk may still be in flight
     if (head < H) {
         const float inv = 1.f / lsum[0];
         uint16_t* op = out + (qi * H + head) * D + 4 * g;
