@@ -8,8 +8,8 @@
 //
 // One wave owns one (query, group of 16 heads[, key split]).
 //   prefill: the selected rows go straight from memory into the wave's LDS with
-//       global_load_lds_dwordx4 (64 lanes x 16 bytes: two whole 512-byte rows per
-//       instruction, fully coalesced), with no VGPR round trip and no LDS write
+//       global_load_lds_dwordx4 (64 lanes x 16 bytes: four 256-byte K or V halves
+//       per instruction, fully coalesced), with no VGPR round trip and no LDS write
 //       instructions; the idx row reaches LDS the same way.  Few registers and
 //       18 KB of LDS per wave (one K and one V stage of 32 half rows, two idx
 //       chunks) give eight waves per CU, and the CU's LDS holds the bytes in flight;
@@ -39,6 +39,11 @@ namespace {
 
 constexpr int ATT_NW = 4;
 constexpr int KT = 32;                  // selected rows per step
+// Prefill: four waves (queries) per workgroup, one V stage per wave (18 KB of LDS per
+// wave, eight waves per CU).  Measured on a 32K layer: two V stages (six waves per CU)
+// and two- or eight-wave workgroups were all slower.
+constexpr int DMA_NW = 4;
+constexpr int DMA_NVS = 1;
 // The running max of a head is moved (and O, l rescaled) only when a step's max
 // exceeds it by more than this many powers of two, so most steps skip the rescale;
 // the probabilities stay <= 2^RESCALE_LOG2, far inside fp32 and bf16 range.  Any
@@ -356,28 +361,42 @@ __device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// vmcnt(n) for a wave-uniform n that is a multiple of 4 up to 32.
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 4: wait_vm<4>(); break;
+    case 8: wait_vm<8>(); break;
+    case 12: wait_vm<12>(); break;
+    case 16: wait_vm<16>(); break;
+    case 20: wait_vm<20>(); break;
+    case 24: wait_vm<24>(); break;
+    case 28: wait_vm<28>(); break;
+    default: wait_vm<32>(); break;
+    }
+}
 
-template <int D>
-__global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
+template <int D, int NW, int NVS>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
     float scale_log2) {
     using G = DmaGeom<D>;
     constexpr int CI = G::ICH / 64;                      // DMA instructions per idx chunk
-    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[ATT_NW][2][G::SB];   // K, V
-    __shared__ __attribute__((aligned(16))) int32_t ring_all[ATT_NW][2 * G::ICH];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[NW][1 + NVS][G::SB];   // K, V[NVS]
+    __shared__ __attribute__((aligned(16))) int32_t ring_all[NW][2 * G::ICH];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int HG = (H + 15) / 16;
-    const int64_t item = (int64_t)blockIdx.x * ATT_NW + wv;
+    const int64_t item = (int64_t)blockIdx.x * NW + wv;
     const int hg = (int)(item % HG);
     const int64_t qi = item / HG;
     if (qi >= nq) return;
     const uint8_t* kst = stage_all[wv][0];
-    const uint8_t* vst = stage_all[wv][1];
+    const uint8_t* vst0 = stage_all[wv][1];
     const int32_t* ring = ring_all[wv];
-    const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst), ring_lds = lds_addr(ring);
+    const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst0), ring_lds = lds_addr(ring);
     const int seq = (int)(qi / q_per_seq);
     const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
     const int32_t* irow = idx + qi * k;
@@ -460,11 +479,14 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         issue_half(k_lds, 0);
         issue_half(v_lds, G::HB);
     }
+    // DMA instructions issued after V(s) that may still be in flight when K(s) or V(s) is
+    // waited for.  chunk(s): an idx chunk went out right after V(s).
+    auto chunk_after = [&](int t) -> bool { return t > 0 && t % G::SPC == 0; };
     for (int s = 0; s < nsteps; ++s) {
         const bool more = s + 1 < nsteps;
-        // a chunk issued after V(s) (at the end of step s - 1) is still allowed in flight
-        const bool chunk_after_v = s > 0 && s % G::SPC == 0;
-        if (chunk_after_v) wait_vm<G::NI + CI>(); else wait_vm<G::NI>();            // K(s) landed
+        const int cs = chunk_after(s) ? CI : 0;
+        wait_vm_n(G::NI + cs);                           // K(s) landed (V(s) and its chunk may fly)
+        const uint8_t* vst = vst0 + (s % NVS) * G::SB;
         // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e
         f32x4 sc[2];
 #pragma unroll
@@ -482,6 +504,10 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         if (more) {
             vmask_next = offsets(s + 1);
             issue_half(k_lds, 0);                        // K(s+1)
+            if (NVS > 1) {                               // V(s+1) into the other V stage
+                issue_half(v_lds + ((s + 1) % NVS) * G::SB, G::HB);
+                if (chunk_after(s + 1)) issue_chunk((s + 1) / G::SPC + 1);
+            }
         }
         float x[8];
 #pragma unroll
@@ -514,12 +540,10 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
         pf[1] = (int)pack_bf16x2(x[2], x[3]);
         pf[2] = (int)pack_bf16x2(x[4], x[5]);
         pf[3] = (int)pack_bf16x2(x[6], x[7]);
-        // V(s) landed: what may still be in flight is the chunk issued after it and K(s+1)
-        if (more) {
-            if (chunk_after_v) wait_vm<G::NI + CI>(); else wait_vm<G::NI>();
-        } else {
-            if (chunk_after_v) wait_vm<CI>(); else wait_vm<0>();
-        }
+        // V(s) landed: still in flight may be its chunk, K(s+1) and (two V stages) V(s+1) and its chunk
+        int after_v = cs;
+        if (more) after_v += G::NI + (NVS > 1 ? G::NI + (chunk_after(s + 1) ? CI : 0) : 0);
+        wait_vm_n(after_v);
         // O^T += V^T P^T: lane (n, g) reads 8 bytes of rows vrow and vrow + 16, d = 16*dt + 4*(n%4) .. +3
         const uint8_t* vr0 = vst + vrow * G::HB + 8 * (n & 1);
         const uint8_t* vr1 = vr0 + 16 * G::HB;
@@ -534,9 +558,9 @@ __global__ __launch_bounds__(ATT_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
             o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
         }
         lsum = mfma_bf16_k32(ones, pf, lsum);
-        if (more) {
+        if (NVS == 1 && more) {
             issue_half(v_lds, G::HB);                    // V(s+1)
-            if ((s + 1) % G::SPC == 0) issue_chunk((s + 1) / G::SPC + 1);
+            if (chunk_after(s + 1)) issue_chunk((s + 1) / G::SPC + 1);
         }
         vmask = vmask_next;
     }
@@ -614,7 +638,8 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)D));
     if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
         if ((int64_t)a.Lk * DmaGeom<D>::RB > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit row offsets
-        hipLaunchKernelGGL((sparse_attn_dma_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,
+        const int64_t dblocks = (items + DMA_NW - 1) / DMA_NW;
+        hipLaunchKernelGGL((sparse_attn_dma_kernel<D, DMA_NW, DMA_NVS>), dim3((unsigned)dblocks), dim3(DMA_NW * 64), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out,
                            a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2);
         return hipGetLastError();
