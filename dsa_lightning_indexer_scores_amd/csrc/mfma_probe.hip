@@ -79,53 +79,102 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const int4* __restrict
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
 
-// One wave per query row of idx [nq, k]: every 32 entries, the rows' bytes are read with
-// coalesced 16-byte loads (64 lanes cover 64 * 16 / row_bytes rows per instruction; row
-// offsets de-interleaved through LDS as in the attention kernel), two steps in flight,
-// and folded into an XOR that keeps the loads live.  Entries < 0 or >= Lk read row 0.
-template <int ROWB>
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+
+// The sparse attention's data movement with no math: one wave per query row of idx
+// [nq, k], four waves per workgroup; per step of 32 entries the K halves and then the V
+// halves of the named rows (row_bytes = 2 * HB) go straight into a K and a V stage of
+// the wave's LDS (global_load_lds_dwordx4, 64 lanes x 16 bytes), K(s+1) issued once K(s)
+// has landed and V(s+1) once V(s) has, and the idx row reaches LDS through a ring of two
+// 256-entry chunks the same way.  Entries outside [0, Lk) read row Lk - 1; steps past the
+// row's last real entry are not run.  One LDS word per lane is written to out at the end.
+template <int HB>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ kv, const int32_t* __restrict__ idx,
                                                           int nq, int k, int Lk, int* __restrict__ out) {
-    constexpr int KTG = 32, PPR = ROWB / 16, RPI = 64 / PPR, NI = KTG / RPI;
-    __shared__ __attribute__((aligned(16))) uint32_t ioff_all[4][KTG];
+    constexpr int KT = 32, NCH = HB / 16, RPI = 1024 / HB, NI = KT / RPI, SB = KT * HB, ICH = 256, SPC = ICH / KT;
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[4][2][SB];
+    __shared__ __attribute__((aligned(16))) int32_t ring_all[4][2 * ICH];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int qi = blockIdx.x * 4 + wv;
     if (qi >= nq) return;
     const int32_t* irow = idx + (int64_t)qi * k;
-    uint32_t* ioff = ioff_all[wv];
-    const uint32_t piece = (lane % PPR) * 16;
-    const int nsteps = __builtin_amdgcn_readfirstlane((k + KTG - 1) / KTG);
-    int4 acc = make_int4(0, 0, 0, 0);
-    int4 raw[2][NI];
-    auto issue = [&](int s, int slot) {
-        __builtin_amdgcn_sched_barrier(0);
-        const int j = s * KTG + (lane & 31);
-        const int v = irow[min(j, k - 1)];
-        const bool ok = j < k && lane < 32 && (uint32_t)v < (uint32_t)Lk;
-        if (lane < KTG) ioff[(lane % RPI) * NI + lane / RPI] = (ok ? (uint32_t)v : 0u) * (uint32_t)ROWB;
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        uint32_t roff[NI];
+    const int32_t* ring = ring_all[wv];
+    const uint32_t k_lds = lds_addr(stage_all[wv][0]), v_lds = lds_addr(stage_all[wv][1]), ring_lds = lds_addr(ring);
+    int j_last = -1;                                     // as the attention: steps past the last real entry are not run
+    for (int jb = 0; jb < k; jb += 64 * 8) {
+        int v[8];
 #pragma unroll
-        for (int i = 0; i < NI; ++i) roff[i] = ioff[(lane / PPR) * NI + i];
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + 64 * u + lane;
+            v[u] = irow[min(j, k - 1)];
+            v[u] = j < k ? v[u] : -1;
+        }
 #pragma unroll
-        for (int i = 0; i < NI; ++i) raw[slot][i] = *reinterpret_cast<const int4*>(kv + (roff[i] + piece));
+        for (int u = 0; u < 8; ++u)
+            if ((uint32_t)v[u] < (uint32_t)Lk) j_last = max(j_last, jb + 64 * u + lane);
+    }
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) j_last = max(j_last, __shfl_xor(j_last, sh));
+    const int nsteps = __builtin_amdgcn_readfirstlane(j_last < 0 ? 0 : j_last / KT + 1);
+    __builtin_amdgcn_s_waitcnt(0);
+    if (nsteps == 0) return;
+    auto issue_chunk = [&](int c) {
+        const uint32_t dst = ring_lds + (uint32_t)(c & 1) * (ICH * 4);
+#pragma unroll
+        for (int w = 0; w < ICH / 64; ++w)
+            dma_b32(irow, (uint32_t)min(c * ICH + 64 * w + lane, k - 1) * 4u, dst + 256u * w);
     };
-    auto fold = [&](int slot) {
+    uint32_t roff[NI];
+    auto offsets = [&](int s) {
+        const int32_t* ir = ring + ((s / SPC) & 1) * ICH + (s % SPC) * KT;
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            acc.x ^= raw[slot][i].x; acc.y ^= raw[slot][i].y; acc.z ^= raw[slot][i].z; acc.w ^= raw[slot][i].w;
+            const uint32_t v = (uint32_t)ir[RPI * i + lane / NCH];
+            roff[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)(2 * HB) + (uint32_t)(lane % NCH) * 16u;
         }
     };
-    issue(0, 0);
-    for (int s = 0; s < nsteps; s += 2) {
-        issue(min(s + 1, nsteps - 1), 1);
-        fold(0);
-        issue(min(s + 2, nsteps - 1), 0);
-        if (s + 1 < nsteps) fold(1);
+    auto issue_half = [&](uint32_t dst, uint32_t half_off) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int i = 0; i < NI; ++i) dma_b128(kv, roff[i] + half_off, dst + 1024u * i);
+    };
+    issue_chunk(0);
+    issue_chunk(1);
+    wait_vm<ICH / 64>();
+    offsets(0);
+    issue_half(k_lds, 0);
+    issue_half(v_lds, HB);
+    for (int s = 0; s < nsteps; ++s) {
+        const bool more = s + 1 < nsteps;
+        const bool cs = s > 0 && s % SPC == 0;           // an idx chunk went out after V(s)
+        if (cs) wait_vm<NI + ICH / 64>(); else wait_vm<NI>();                    // K(s) landed
+        if (more) {
+            offsets(s + 1);
+            issue_half(k_lds, 0);
+        }
+        if (more) {                                                              // V(s) landed
+            if (cs) wait_vm<NI + ICH / 64>(); else wait_vm<NI>();
+        } else {
+            wait_vm<0>();
+        }
+        if (more) {
+            issue_half(v_lds, HB);
+            if ((s + 1) % SPC == 0) issue_chunk((s + 1) / SPC + 1);
+        }
     }
-    __builtin_amdgcn_s_waitcnt(0);
-    out[(int64_t)qi * 64 + lane] = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    wait_vm<0>();
+    out[(int64_t)qi * 64 + lane] = reinterpret_cast<const int*>(stage_all[wv][1])[lane];
 }
 
 }  // namespace
@@ -137,10 +186,10 @@ extern "C" __attribute__((visibility("default"))) int icp_gather_rows(const void
     if (kv == nullptr || idx == nullptr || out == nullptr || nq < 1 || k < 1 || Lk < 1) return (int)hipErrorInvalidValue;
     const dim3 grid((nq + 3) / 4);
     if (row_bytes == 512)
-        hipLaunchKernelGGL(gather_rows_kernel<512>, grid, dim3(256), 0, (hipStream_t)stream,
+        hipLaunchKernelGGL(gather_rows_kernel<256>, grid, dim3(256), 0, (hipStream_t)stream,
                            static_cast<const uint8_t*>(kv), idx, nq, k, Lk, out);
     else if (row_bytes == 256)
-        hipLaunchKernelGGL(gather_rows_kernel<256>, grid, dim3(256), 0, (hipStream_t)stream,
+        hipLaunchKernelGGL(gather_rows_kernel<128>, grid, dim3(256), 0, (hipStream_t)stream,
                            static_cast<const uint8_t*>(kv), idx, nq, k, Lk, out);
     else
         return (int)hipErrorInvalidValue;
