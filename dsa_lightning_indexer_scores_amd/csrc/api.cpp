@@ -15,6 +15,7 @@
 #include <cstdio>
 #include <climits>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "../../include/indexcache.h"
@@ -44,6 +45,36 @@ ic_status hip_fail(hipError_t e, const char* what) {
 }
 
 int chunk_of(const ic_shape& s) { return s.chunk == 0 ? kDefaultChunk : s.chunk; }
+
+// A second stream per device, at the default priority, for work that overlaps the
+// caller's stream inside one call: an F layer's attention over a finished score tile runs
+// there while the next tile is scored.  Created on first use, kept until the process ends.
+// Concurrent calls on one device share it, which can only add waiting, never reorder a
+// call's own work (each call forks and joins through its own events).  nullptr if it
+// cannot be created; the caller then keeps everything on its own stream.
+hipStream_t side_stream() {
+    static std::mutex mu;
+    static hipStream_t streams[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!streams[dev]) {
+        hipStream_t h = nullptr;
+        if (hipStreamCreateWithFlags(&h, hipStreamNonBlocking) != hipSuccess) return nullptr;
+        streams[dev] = h;
+    }
+    return streams[dev];
+}
+
+// The F layer's own attention, run tile by tile on the side stream as the tiles' top-k
+// rows land (tile t's attention overlaps tile t + 1's scoring).
+struct TileAttn {
+    const void* q;          // the layer's q [B, Lq, H, d]
+    const void* kv;         // kv [B, Lk, 2, d]
+    void* out;              // out [B, Lq, H, d]
+    hipStream_t side;
+    hipEvent_t fork;
+};
 
 // Sizes the kernels support; `decode` relaxes the prefill position checks, and `varlen`
 // leaves them to the per-sequence check (Lq is then the packed query count).
@@ -158,7 +189,7 @@ size_t elem_bytes(int dtype) { return dtype == IC_FP8_E4M3 ? 1 : 2; }
 // tiles of <= chunk queries, then top-k into idx [Lq, k].
 ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_t* qb, const float* wb,
                                const uint8_t* kb, int32_t* idx, void* ws, hipStream_t st, int64_t* tiles,
-                               const int32_t* run_if = nullptr) {
+                               const int32_t* run_if = nullptr, const TileAttn* ta = nullptr, int b = 0) {
     const int chunk = chunk_of(s);
     float* tile = static_cast<float*>(ws);
     for (int c0 = 0; c0 < Lq; c0 += chunk) {
@@ -193,19 +224,40 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         e = launch_topk(t, st);
         if (e != hipSuccess) return hip_fail(e, "top-k launch");
         if (tiles) ++*tiles;
+        if (ta) {                                           // this tile's attention, on the side stream
+            if ((e = hipEventRecord(ta->fork, st)) != hipSuccess) return hip_fail(e, "event record");
+            if ((e = hipStreamWaitEvent(ta->side, ta->fork, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+            const size_t row = (size_t)s.H * s.d;          // bf16 elements per query row
+            ic_attn_args at;
+            at.q = static_cast<const uint16_t*>(ta->q) + ((size_t)b * s.Lq + c0) * row;
+            at.kv = static_cast<const uint16_t*>(ta->kv) + (size_t)b * s.Lk * 2 * s.d;
+            at.idx = t.idx;
+            at.out = static_cast<uint16_t*>(ta->out) + ((size_t)b * s.Lq + c0) * row;
+            at.kv_seq_stride = (int64_t)s.Lk * 2 * s.d;
+            at.Lk = s.Lk;
+            at.nq = nq;
+            at.q_per_seq = nq;
+            at.H = s.H;
+            at.d = s.d;
+            at.k = s.k;
+            at.nsplit = 1;
+            at.ws = nullptr;
+            if ((e = launch_sparse_attn(at, ta->side)) != hipSuccess) return hip_fail(e, "sparse attention launch");
+        }
     }
     return IC_OK;
 }
 
 // a1 + a2 for every sequence of the call (all with Lq queries at pos0).
 ic_status run_indexer_topk(const ic_shape& s, const void* q_I, const float* w, const void* k_I, int32_t* idx,
-                           void* ws, hipStream_t st, int64_t* tiles) {
+                           void* ws, hipStream_t st, int64_t* tiles, const TileAttn* ta = nullptr) {
     const size_t eb = elem_bytes(s.idx_dtype);
     for (int b = 0; b < s.B; ++b) {
         const uint8_t* qb = static_cast<const uint8_t*>(q_I) + (size_t)b * s.Lq * s.H_I * s.d_I * eb;
         const float* wb = w + (size_t)b * s.Lq * s.H_I;
         const uint8_t* kb = static_cast<const uint8_t*>(k_I) + (size_t)b * s.Lk * s.d_I * eb;
-        ic_status r = run_indexer_topk_one(s, s.Lq, s.pos0, qb, wb, kb, idx + (size_t)b * s.Lq * s.k, ws, st, tiles);
+        ic_status r = run_indexer_topk_one(s, s.Lq, s.pos0, qb, wb, kb, idx + (size_t)b * s.Lq * s.k, ws, st, tiles,
+                                           nullptr, ta, b);
         if (r != IC_OK) return r;
     }
     return IC_OK;
@@ -401,20 +453,42 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
     if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
     if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
     hipStream_t st = (hipStream_t)stream;
+    // An F layer's attention runs tile by tile on a side stream, overlapping the scoring of
+    // the layer's next tile; the caller's stream waits for it before the next layer.
+    hipStream_t side = side_stream();
+    hipEvent_t ev[2] = {nullptr, nullptr};
+    if (side && (hipEventCreateWithFlags(&ev[0], hipEventDisableTiming) != hipSuccess ||
+                 hipEventCreateWithFlags(&ev[1], hipEventDisableTiming) != hipSuccess))
+        side = nullptr;
+    struct Events {
+        hipEvent_t* e;
+        ~Events() {
+            for (int i = 0; i < 2; ++i)
+                if (e[i]) (void)hipEventDestroy(e[i]);
+        }
+    } release{ev};
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;                       // the index cache starts empty on every call
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
-        if (pattern[l] == 'F' || pattern[l] == '1') {
-            r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles);
+        const bool full = pattern[l] == 'F' || pattern[l] == '1';
+        if (full) {
+            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0]};
+            r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side ? &ta : nullptr);
             if (r != IC_OK) return r;
             cached = true;
             ++cnt.indexer_calls;
         } else if (!cached) {
             return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
-        r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
-        if (r != IC_OK) return r;
+        if (full && side) {                    // join: the layer's tile attentions are done
+            hipError_t e = hipEventRecord(ev[1], side);
+            if (e == hipSuccess) e = hipStreamWaitEvent(st, ev[1], 0);
+            if (e != hipSuccess) return hip_fail(e, "stream join");
+        } else {
+            r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
+            if (r != IC_OK) return r;
+        }
         ++cnt.attn_calls;
         ++cnt.layers;
     }
