@@ -62,3 +62,59 @@ def test_decode_graph_replays_match_eager():
         assert torch.equal(got_idx, ref_idx), f"replay {step}: idx differs"
         for l in range(len(pattern)):
             assert torch.equal(got[l], ref_outs[l]), f"replay {step}: layer {l} differs"
+
+
+def test_prefill_stack_graph_replays_match_eager():
+    """run_stack with several score tiles per F layer (its attention runs tile by tile on a
+    side stream) captured in a graph: every replay with new inputs equals the eager call."""
+    cfg = synth.WORKLOADS["tiny"]
+    pattern, chunk = "FSFS", 96                                  # 512 queries: six tiles, the last ragged
+    layers = synth.prefill_stack(cfg, device="cuda", pattern=pattern)
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((1, cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    shape = ic._stack_shape(pattern, layers, cfg.k, chunk, 0)
+    ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_RUN_STACK), dtype=torch.uint8, device="cuda")
+    ic.run_stack(pattern, layers, cfg.k, chunk=chunk, outs=outs, idx_cache=idx, ws=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ic.run_stack(pattern, layers, cfg.k, chunk=chunk, outs=outs, idx_cache=idx, ws=ws)
+    g = torch.Generator(device="cuda").manual_seed(11)
+    for rep in range(1, 4):
+        for lay in layers:                                     # new small-integer inputs in place
+            for name in ("q", "kv", "q_I", "k_I"):
+                if name in lay:
+                    lay[name].copy_(torch.randint(-3, 4, lay[name].shape, generator=g, device="cuda").to(lay[name].dtype))
+            if "w" in lay:
+                lay["w"].copy_(torch.randint(0, 4, lay["w"].shape, generator=g, device="cuda").to(lay["w"].dtype))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        got_idx = idx.clone()
+        ref_outs, ref_idx, _ = ic.run_stack(pattern, layers, cfg.k, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, ref_idx), f"replay {rep}: idx differs"
+        for l in range(len(pattern)):
+            assert torch.equal(got[l], ref_outs[l]), f"replay {rep}: layer {l} differs"
+
+
+def test_prefill_stacks_on_two_caller_streams():
+    """Two run_stack calls in flight at once on two caller streams (they share the side
+    stream) give the same results as the same calls made one after the other."""
+    cfg = synth.WORKLOADS["tiny"]
+    a = synth.prefill_stack(cfg, device="cuda", pattern="FSSS")
+    b = [{k: v.flip(1).contiguous() for k, v in lay.items()}                # other inputs, F layers at 0 and 2
+         for lay in synth.prefill_stack(cfg, device="cuda", pattern="FSFS")]
+    ref_a = ic.run_stack("FSSS", a, cfg.k, chunk=128)
+    ref_b = ic.run_stack("FSFS", b, cfg.k, chunk=64)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        got_a = ic.run_stack("FSSS", a, cfg.k, chunk=128, stream=s1)
+    with torch.cuda.stream(s2):
+        got_b = ic.run_stack("FSFS", b, cfg.k, chunk=64, stream=s2)
+    torch.cuda.synchronize()
+    for ref, got in ((ref_a, got_a), (ref_b, got_b)):
+        assert torch.equal(ref[1], got[1])
+        assert all(torch.equal(x, y) for x, y in zip(ref[0], got[0]))
