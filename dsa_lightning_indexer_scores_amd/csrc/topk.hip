@@ -107,12 +107,14 @@ __device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wt
 // keys from ckeys, positions from cand).
 enum { TOPK_ROWS = 0, TOPK_SEGS = 1, TOPK_GATHER = 2 };
 
-// Many-row launches of 1024-thread shapes with up to 24 keys per thread are held to 64
-// VGPRs, so two rows' workgroups share a CU and one row's barriers and memory waits hide
-// behind the other's work (a few spilled scalars cost less than that); 32 keys per thread
-// do not fit.  The decode shapes (a few rows per launch) gain nothing from it and keep
-// their registers.
-constexpr int topk_waves_per_eu(int NT, int EPT, int MODE) { return (MODE == TOPK_ROWS && NT == 1024 && EPT <= 24) ? 8 : 1; }
+// Many-row launches of 1024-thread shapes with up to 24 keys per thread, and of the
+// 512 x 16 shape, are held to 64 VGPRs, so two (four) rows' workgroups share a CU and one
+// row's barriers and memory waits hide behind the others' work (a few spilled scalars cost
+// less than that); 32 keys per thread do not fit.  The decode shapes (a few rows per
+// launch) gain nothing from it and keep their registers.
+constexpr int topk_waves_per_eu(int NT, int EPT, int MODE) {
+    return (MODE == TOPK_ROWS && ((NT == 1024 && EPT <= 24) || (NT == 512 && EPT <= 16))) ? 8 : 1;
+}
 
 template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_per_eu(NT, EPT, MODE)))) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
@@ -551,6 +553,7 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
     } while (0)
     if (len <= 2048) IC_TOPK_GO(256, 8, false);
     if (len <= 4096) IC_TOPK_GO(256, 16, false);
+    if (MODE == TOPK_ROWS && len <= 8192) IC_TOPK_GO(512, 16, false);
     if (len <= 16384) IC_TOPK_GO(1024, 16, false);
     if (MODE == TOPK_ROWS && len <= 24576) IC_TOPK_GO(1024, 24, false);
     if (MODE != TOPK_ROWS || len <= 32768) IC_TOPK_GO(1024, 32, false);

@@ -44,9 +44,11 @@ def test_topk_rows_small(kind, k):
     _run(m, first, k)
 
 
-@pytest.mark.parametrize("n0", [4000, 20000, 40000, 70000])
+@pytest.mark.parametrize("n0", [4000, 4091, 6000, 8187, 12000, 20000, 40000, 70000])
 def test_topk_long_rows(n0):
-    """Rows on both sides of the LDS staging limit; k = 2048 as in the DSA configs."""
+    """Rows on both sides of the LDS staging limit and of each block shape's key capacity
+    (4096, 8192: the last row of n0 = 4091 and 8187 is exactly that long); k = 2048 as in
+    the DSA configs."""
     rng = np.random.default_rng(n0)
     rows = 6
     m = np.abs(rng.standard_normal((rows, n0 + rows)).astype(np.float32)) * 30
