@@ -339,44 +339,8 @@ struct DmaGeom {
     static constexpr int ICH = 256;          // idx entries per ring chunk
     static constexpr int SPC = ICH / KT;     // steps per chunk
     static_assert((NCH == 16 || NCH == 8) && KT % RPI == 0, "half row must be 256 or 128 bytes");
-    // Slot permutation of staged row r (only r % 16 matters).  For 256-byte half rows,
-    // r ^ (r << 1) was the fastest of a dozen candidates for both read patterns in an LDS
-    // microbenchmark (K-fragment reads 1.3x and transposed V reads 1.03x faster than the
-    // next best common choice); for 128-byte half rows the 8 even (odd) rows of a K tile
-    // get distinct slots and the rows of a transposed V read distinct chunk pairs.
-    __device__ static uint32_t swz(int r) {
-        return NCH == 16 ? (uint32_t)((r ^ (r << 1)) & 15)
-                         : (uint32_t)((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
-    }
+    __device__ static uint32_t swz(int r) { return dma_swz<NCH>(r); }
 };
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
-__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
-// 4 bytes per lane from base + voff into LDS at lds + 4 * lane.
-__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-// vmcnt(n) for a wave-uniform n that is a multiple of 4 up to 32.
-__device__ __forceinline__ void wait_vm_n(int n) {
-    switch (n) {
-    case 0: wait_vm<0>(); break;
-    case 4: wait_vm<4>(); break;
-    case 8: wait_vm<8>(); break;
-    case 12: wait_vm<12>(); break;
-    case 16: wait_vm<16>(); break;
-    case 20: wait_vm<20>(); break;
-    case 24: wait_vm<24>(); break;
-    case 28: wait_vm<28>(); break;
-    default: wait_vm<32>(); break;
-    }
-}
 
 template <int D, int NW, int NVS>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(

@@ -64,6 +64,48 @@ __device__ __forceinline__ float max_xor32(float x) {
     return fmax_nan(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
+// ---- memory -> LDS DMA (global_load_lds), waited for by explicit vmcnt counts ----
+// The loads are inline asm with M0 as an operand, so the compiler neither counts them nor
+// inserts its own waits for LDS reads behind them: every wait is the caller's.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+// 16 bytes per lane from base + voff into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+// 4 bytes per lane from base + voff into LDS at lds + 4 * lane.
+__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
+// vmcnt(n) for a wave-uniform n that is a multiple of 4 up to 32.
+__device__ __forceinline__ void wait_vm_n(int n) {
+    switch (n) {
+    case 0: wait_vm<0>(); break;
+    case 4: wait_vm<4>(); break;
+    case 8: wait_vm<8>(); break;
+    case 12: wait_vm<12>(); break;
+    case 16: wait_vm<16>(); break;
+    case 20: wait_vm<20>(); break;
+    case 24: wait_vm<24>(); break;
+    case 28: wait_vm<28>(); break;
+    default: wait_vm<32>(); break;
+    }
+}
+// Slot permutation of a staged K or V half row r (only r % 16 matters): 16-byte slot j holds
+// the half's chunk j ^ dma_swz(r).  For 256-byte halves (16 chunks), r ^ (r << 1) was the
+// fastest of a dozen candidates for both read patterns (K fragments with ds_read_b128,
+// transposed V with ds_read_b64_tr_b16) in an LDS microbenchmark; for 128-byte halves the
+// 8 even (odd) rows of a K tile get distinct slots and the rows of a transposed V read
+// distinct chunk pairs.
+template <int NCH>
+__device__ __forceinline__ uint32_t dma_swz(int r) {
+    static_assert(NCH == 16 || NCH == 8, "half row must be 256 or 128 bytes");
+    return NCH == 16 ? (uint32_t)((r ^ (r << 1)) & 15) : (uint32_t)((((r >> 1) & 3) << 1) | ((r >> 3) & 1));
+}
+
 // Order-preserving map of an fp32 score to u32 (larger float -> larger key).
 // -0.0 is folded onto +0.0 first so that the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float f) {

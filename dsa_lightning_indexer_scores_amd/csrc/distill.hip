@@ -12,12 +12,13 @@
 // An entry of -1, or one outside the keys the query sees, is not part of S_t.
 //
 // One workgroup per query; its four waves split the entries.  For every served
-// layer and group of 16 heads: a first sweep gathers the entries' K rows
-// (coalesced whole-row loads through the wave's LDS tile, as in the sparse
-// attention) and keeps each head's running max and exp-sum; the waves merge
-// those; a second sweep recomputes the logits and adds each entry's
-// probability, summed over the 16 heads with DPP row adds, into a per-entry
-// LDS accumulator.  Then the indexer scores at the entries (read from the score
+// layer and group of 16 heads: a first sweep gathers the entries' K halves
+// straight into the wave's LDS stage (global_load_lds_dwordx4, as in the sparse
+// attention; the next step's halves fly while a step's statistics are computed)
+// and keeps each head's running max and exp-sum; the waves merge those; a second
+// sweep recomputes the logits and adds each entry's probability, summed over the
+// 16 heads with DPP row adds, into a per-entry LDS accumulator.  Each wave's row
+// offsets are read from the idx row once, into LDS, for all of its sweeps.  Then the indexer scores at the entries (read from the score
 // tile the indexer kernel wrote) give log r, and the workgroup sums p (log p -
 // log r).  Everything runs in the exp2/log2 domain (v_exp_f32, v_log_f32);
 // every sum is taken in a fixed order, so the result is deterministic.
@@ -35,14 +36,13 @@ struct DGeom {
     static constexpr int NDC = D / 32;  // K=32 chunks of the contraction
     static constexpr int RB = 4 * D;    // bytes per [K | V] row
     static constexpr int KB = 2 * D;    // bytes of its K part
-    static constexpr int PPR = KB / 16; // 16-byte pieces of a K part
-    static constexpr int RPI = 64 / PPR;    // K parts per load instruction
-    static constexpr int NI = DKT / RPI;    // load instructions per step
-    static constexpr int STR = KB + 16;     // LDS bytes per staged K part (16-byte skew)
+    static constexpr int NCH = KB / 16; // 16-byte chunks of a K part
+    static constexpr int RPI = 1024 / KB;   // K parts per DMA instruction (64 lanes x 16 bytes)
+    static constexpr int NI = DKT / RPI;    // DMA instructions per step
+    static constexpr int SB = DKT * KB;     // bytes of a staged step
     static_assert(NI % 4 == 0, "row offsets are read four at a time");
 };
-
-__device__ __forceinline__ void lds_wave_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+constexpr uint32_t NO_ROW = 0xFFFFFFFFu;   // an entry outside S_t
 
 // Sum over the 16 lanes of each lane row (DPP), result in every lane of the row.
 __device__ __forceinline__ float row16_sum(float x) {
@@ -62,13 +62,13 @@ __device__ __forceinline__ void merge_stat(float& m, float& z, float m2, float z
 }
 
 template <int D>
-__global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, float scale_log2) {
+__global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, float scale_log2, int per) {
     using G = DGeom<D>;
-    __shared__ __attribute__((aligned(16))) uint8_t ktile_all[DW][DKT * G::STR];
-    __shared__ __attribute__((aligned(16))) uint32_t ioff_all[DW][DKT];
-    __shared__ float p_lds[IC_DISTILL_MAX_K];
+    __shared__ __attribute__((aligned(1024))) uint8_t ktile_all[DW][G::SB];
     __shared__ float wstat[DW][16][2];
     __shared__ float wred[DW];
+    // dynamic: p [round_up(k, 4)] floats, then each wave's row offsets [DW][per]
+    extern __shared__ __attribute__((aligned(16))) uint32_t dyn_lds[];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
@@ -78,15 +78,32 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
     const int k = a.k;
     const int32_t* irow = a.idx + (int64_t)t * k;
     const float* srow = a.scores + (int64_t)r * a.score_stride;
-    uint8_t* ktile = ktile_all[wv];
-    uint32_t* ioff = ioff_all[wv];
-    const int per = ((k + DW - 1) / DW + DKT - 1) / DKT * DKT;
+    float* p_lds = reinterpret_cast<float*>(dyn_lds);
+    uint32_t* offs = dyn_lds + ((k + 3) & ~3) + wv * per;    // this wave's entries' row offsets
+    const uint8_t* ktile = ktile_all[wv];
+    const uint32_t k_lds = lds_addr(ktile);
     const int e_begin = wv * per, e_end = min(k, e_begin + per);
     const int nsteps = e_end > e_begin ? (e_end - e_begin + DKT - 1) / DKT : 0;
     const int HG = (a.H + 15) / 16;
     const float inv_cnt = 1.f / (float)(a.nserved * a.H);
 
     for (int e = e_begin + lane; e < e_end; e += 64) p_lds[e] = 0.f;   // the wave's own entries
+    // Row byte offsets of the wave's entries (NO_ROW outside S_t), step by step and
+    // de-interleaved so that a lane reads its DMA addresses as one vector: entry RPI*i + q
+    // of a step -> slot q*NI + i.  Eight unconditional (clamped) loads per lane per block.
+    for (int xb = 0; xb < nsteps * DKT; xb += 64 * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = irow[min(e_begin + xb + 64 * u + lane, e_end - 1)];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int x = xb + 64 * u + lane, j = x % DKT;
+            const bool ok = e_begin + x < e_end && (uint32_t)v[u] < (uint32_t)vis;
+            if (x < nsteps * DKT)
+                offs[x - j + (j % G::RPI) * G::NI + j / G::RPI] = ok ? (uint32_t)v[u] * (uint32_t)G::RB : NO_ROW;
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");       // the wave reads only its own offsets
     // emask[e]: all ones in the lanes with n % 4 == e (kept opaque so the selection by it
     // stays bitwise and is not turned into an indexed scratch access)
     uint32_t emask[4];
@@ -95,82 +112,54 @@ __global__ __launch_bounds__(DW * 64) void distill_kl_kernel(ic_distill_args a, 
         emask[e] = ((n & 3) == e) ? 0xFFFFFFFFu : 0u;
         asm volatile("" : "+v"(emask[e]));
     }
-
-    struct Tile {
-        i32x4 raw[G::NI];                                     // the step's K parts, as loaded
-        uint32_t valid;                                       // bit e: entry e of the step is in S_t
-    };
-    auto load_entry = [&](int e0) -> int {                    // raw idx of entry e0 + lane (lanes < 32)
-        const int e = e0 + (lane & 31);
-        const int v = irow[min(e, e_end - 1)];                // unconditional load: no branch around it
-        return (e < e_end && lane < 32) ? v : -1;
-    };
-    auto issue = [&](Tile& T, int raw, const uint8_t* kvb) {
-        __builtin_amdgcn_sched_barrier(0);
-        const bool ok = (uint32_t)raw < (uint32_t)vis;
-        T.valid = (uint32_t)__ballot(ok);
-        const uint32_t row = ok ? (uint32_t)raw : 0u;          // a real row, masked later
-        // row offsets through the wave's LDS words, de-interleaved: entry RPI*i + q -> slot q*NI + i
-        if (lane < DKT) ioff[(lane % G::RPI) * G::NI + lane / G::RPI] = row * (uint32_t)G::RB;
-        lds_wave_sync();
+    // Lane l of DMA instruction i fetches chunk (l % NCH) ^ swz(row) of staged row RPI*i + l / NCH.
+    uint32_t cof[G::NI];
+#pragma unroll
+    for (int i = 0; i < G::NI; ++i)
+        cof[i] = ((uint32_t)(lane % G::NCH) ^ dma_swz<G::NCH>(G::RPI * i + lane / G::NCH)) * 16u;
+    const uint32_t swz_k = dma_swz<G::NCH>(n);
+    // Step s's K halves -> the wave's stage (entries outside S_t fetch row 0); returns the
+    // step's valid entries as a wave-uniform mask.
+    auto issue = [&](const uint8_t* kvb, int s) -> uint32_t {
+        const uint32_t* so = offs + s * DKT;
+        const uint32_t ev = so[(lane % G::RPI) * G::NI + (lane & 31) / G::RPI];   // entry lane % 32
+        const uint32_t valid = (uint32_t)__ballot(ev != NO_ROW);
         uint32_t roff[G::NI];
 #pragma unroll
         for (int i = 0; i < G::NI; i += 4) {
-            const u32x4 v = *reinterpret_cast<const u32x4*>(ioff + (lane / G::PPR) * G::NI + i);
-            roff[i] = v[0]; roff[i + 1] = v[1]; roff[i + 2] = v[2]; roff[i + 3] = v[3];
+            const u32x4 w = *reinterpret_cast<const u32x4*>(so + (lane / G::NCH) * G::NI + i);
+            roff[i] = w[0]; roff[i + 1] = w[1]; roff[i + 2] = w[2]; roff[i + 3] = w[3];
         }
-        const uint32_t piece = (lane % G::PPR) * 16;
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the stage's previous reads are done
 #pragma unroll
-        for (int i = 0; i < G::NI; ++i) T.raw[i] = *reinterpret_cast<const i32x4*>(kvb + (roff[i] + piece));
+        for (int i = 0; i < G::NI; ++i) dma_b128(kvb, (roff[i] == NO_ROW ? 0u : roff[i]) + cof[i], k_lds + 1024u * i);
+        return __builtin_amdgcn_readfirstlane(valid);
     };
-    // S^T of a step: lane (n, g) gets head n of the group, entries 16*kt + 4g + e (log2 units,
-    // -inf for entries outside S_t).
-    auto logits = [&](const Tile& T, const i32x4* qf, float x[8]) {
-#pragma unroll
-        for (int i = 0; i < G::NI; ++i)
-            *reinterpret_cast<i32x4*>(ktile + (G::RPI * i + lane / G::PPR) * G::STR + (lane % G::PPR) * 16) = T.raw[i];
-        lds_wave_sync();
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int dc = 0; dc < G::NDC; ++dc) {
-                const i32x4 kf = *reinterpret_cast<const i32x4*>(ktile + (16 * kt + n) * G::STR + 64 * dc + 16 * g);
-                acc = mfma_bf16_k32(kf, qf[dc], acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                x[4 * kt + e] = ((T.valid >> (16 * kt + 4 * g + e)) & 1u) ? acc[e] * scale_log2 : -INFINITY;
-        }
-        lds_wave_sync();                                      // the tile is rewritten by the next step
-    };
-    // One sweep over the wave's entries; f(x, step_begin) sees each step's logits.
+    // One sweep over the wave's entries; f(x, step_begin) sees each step's logits: lane (n, g)
+    // gets head n of the group, entries 16*kt + 4g + e (log2 units, -inf outside S_t).
+    // Step s+1's halves are issued as soon as step s's are read, and land while f runs.
     auto sweep = [&](const uint8_t* kvb, const i32x4* qf, auto&& f) {
         if (nsteps == 0) return;
-        Tile TA, TB;
-        int iA = load_entry(e_begin), iB = load_entry(e_begin + DKT);
-        issue(TA, iA, kvb);
-        float x[8];
-        int s = 0;
-        for (; s + 2 < nsteps; s += 2) {
-            iA = load_entry(e_begin + (s + 2) * DKT);
-            issue(TB, iB, kvb);
-            logits(TA, qf, x);
+        uint32_t valid = issue(kvb, 0);
+        for (int s = 0; s < nsteps; ++s) {
+            wait_vm<0>();                                    // step s landed
+            float x[8];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int dc = 0; dc < G::NDC; ++dc) {
+                    const i32x4 kf = *reinterpret_cast<const i32x4*>(ktile + (16 * kt + n) * G::KB +
+                                                                     (((uint32_t)(4 * dc + g) ^ swz_k) * 16u));
+                    acc = mfma_bf16_k32(kf, qf[dc], acc);
+                }
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    x[4 * kt + e] = ((valid >> (16 * kt + 4 * g + e)) & 1u) ? acc[e] * scale_log2 : -INFINITY;
+            }
+            const uint32_t valid_next = s + 1 < nsteps ? issue(kvb, s + 1) : 0u;
             f(x, e_begin + s * DKT);
-            iB = load_entry(e_begin + (s + 3) * DKT);
-            issue(TA, iA, kvb);
-            logits(TB, qf, x);
-            f(x, e_begin + (s + 1) * DKT);
-        }
-        if (s + 1 < nsteps) {
-            issue(TB, iB, kvb);
-            logits(TA, qf, x);
-            f(x, e_begin + s * DKT);
-            logits(TB, qf, x);
-            f(x, e_begin + (s + 1) * DKT);
-        } else {
-            logits(TA, qf, x);
-            f(x, e_begin + s * DKT);
+            valid = valid_next;
         }
     };
 
@@ -320,10 +309,12 @@ hipError_t launch_distill(const ic_distill_args& a, hipStream_t st) {
     if (a.k < 1 || a.k > IC_DISTILL_MAX_K || a.nserved < 1 || a.nserved > IC_DISTILL_MAX_SERVED)
         return hipErrorInvalidValue;
     const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)a.d));
+    const int per = ((a.k + DW - 1) / DW + DKT - 1) / DKT * DKT;              // entries per wave
+    const size_t dyn = (size_t)(((a.k + 3) & ~3) + DW * per) * sizeof(uint32_t);
     if (a.d == 128)
-        hipLaunchKernelGGL((distill_kl_kernel<128>), dim3((unsigned)a.nrows), dim3(DW * 64), 0, st, a, scale_log2);
+        hipLaunchKernelGGL((distill_kl_kernel<128>), dim3((unsigned)a.nrows), dim3(DW * 64), dyn, st, a, scale_log2, per);
     else if (a.d == 64)
-        hipLaunchKernelGGL((distill_kl_kernel<64>), dim3((unsigned)a.nrows), dim3(DW * 64), 0, st, a, scale_log2);
+        hipLaunchKernelGGL((distill_kl_kernel<64>), dim3((unsigned)a.nrows), dim3(DW * 64), dyn, st, a, scale_log2, per);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
