@@ -11,7 +11,7 @@
 //     loss_t = KL(p_t || r_t) = sum_s p_t[s] (ln p_t[s] - ln r_t[s])
 // An entry of -1, or one outside the keys the query sees, is not part of S_t.
 //
-// One workgroup per query; its four waves split the entries.  For every served
+// One workgroup per query; its eight waves split the entries.  For every served
 // layer and group of 16 heads: a first sweep gathers the entries' K halves
 // straight into the wave's LDS stage (global_load_lds_dwordx4, as in the sparse
 // attention; the next step's halves fly while a step's statistics are computed)
@@ -28,7 +28,10 @@ using namespace ic;
 
 namespace {
 
-constexpr int DW = 4;                   // waves per workgroup
+// Waves per workgroup (one query): each keeps one step in flight, so more waves per CU
+// hide more of the gather latency.  Eight (80 KB of LDS per workgroup at k = 2048, two
+// workgroups per CU) measured faster than four or two.
+constexpr int DW = 8;
 constexpr int DKT = 32;                 // entries per step
 
 template <int D>
