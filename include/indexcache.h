@@ -38,7 +38,13 @@
  *  - Tensors are dense and row-major in the layouts given below.
  *      bf16 = IEEE binary32 upper half; fp8 = OCP E4M3FN byte codes.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
- *    work and return; nothing synchronises the host.
+ *    work and return; nothing synchronises the host.  All of a call's work is
+ *    ordered on `stream`: work after the call on `stream` sees its results.
+ *    ic_run_stack also runs part of its work on a second stream of the
+ *    library's (one per device, default priority, created on first use),
+ *    forked from and joined back to `stream` with events inside the call, so
+ *    the call stays capturable in a HIP graph.  Concurrent calls on one device
+ *    share that stream: they may wait on each other there, never reorder.
  *  - Arguments are validated before any launch; a failing call returns a
  *    non-zero ic_status, launches nothing and leaves outputs untouched.
  *    ic_last_error() then describes the failure (thread-local string).
@@ -188,7 +194,9 @@ IC_API ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void
  * (each call is a fresh sequence batch), so a pattern whose first layer is
  * S fails with IC_ERR_NO_CACHED_INDICES before any launch.
  * idx_cache: [B, Lq, k] int32, caller-owned, holds the last F layer's
- * indices on return.  stats (may be NULL) receives the counters. */
+ * indices on return.  stats (may be NULL) receives the counters.
+ * An F layer's own attention runs score tile by score tile on the library's
+ * second stream, overlapping the scoring of the layer's next tile. */
 IC_API ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
                        const ic_shape* shape, int32_t* idx_cache, void* ws, size_t ws_bytes,
                        ic_stats* stats, void* stream);
