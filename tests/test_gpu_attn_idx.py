@@ -56,3 +56,25 @@ def test_attention_any_idx_layout(d, H, k):
     err = attn_rel_err(dec(out)[0], ref)
     summary(f"attention idx layouts d={d} H={H} k={k}", {"max_rel_err": err})
     assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("k", [1, 33, 257, 520, 4096])
+def test_attention_idx_ring_boundaries(k):
+    """The prefill kernel reads each idx row in 256-entry chunks and runs 32-entry steps:
+    k = 1 (one partial step), 33 (one entry into a second step), 257 (one entry into a
+    second chunk), 520 (three chunks, ragged) and 4096 (the largest k, sixteen chunks),
+    with the same idx layouts as above."""
+    torch.manual_seed(k)
+    H, d = 16, 128
+    Lq, Lk = (16, 4200) if k == 4096 else (48, max(700, k + 64))
+    q = (torch.randn(1, Lq, H, d) * 0.5).to(torch.bfloat16).cuda()
+    kv = (torch.randn(1, Lk, 2, d) * 0.5).to(torch.bfloat16).cuda()
+    idx = idx_patterns(Lq, Lk, k, seed=k)
+    if k < 2:                                                    # the layouts need room for holes
+        idx = np.random.default_rng(k).integers(0, Lk, size=(Lq, k)).astype(np.int32)
+    out = ic.sparse_attn(q, kv, torch.from_numpy(idx)[None].cuda())
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(dec(q)[0], dec(kv)[0], idx)
+    err = attn_rel_err(dec(out)[0], ref)
+    summary(f"attention ring boundaries k={k}", {"max_rel_err": err})
+    assert err <= ATTN_TOL
