@@ -19,6 +19,7 @@ Functions mirror the C entry points (without the ``ic_`` prefix):
                                         -> (outs, idx_cache, stats, refreshed, recall)
   decode_step(pattern, layers, seq_len, k) -> (outs, idx_cache, stats)
   index_overlap(idx_a, idx_b)           -> (inter, jaccard, recall, means)
+  overlap_matrix(idx_list)              -> (J [n, n], R [n, n]) mean Jaccard / recall of every pair
   distill_kl(q_I, w, k_I, idx, qs, kvs) -> (kl [B, Lq], mean)
 """
 from __future__ import annotations
@@ -27,6 +28,7 @@ import ctypes
 import os
 from typing import Dict, List, Optional, Sequence
 
+import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -260,6 +262,35 @@ def index_overlap(idx_a, idx_b, stream=None):
     _check(lib().ic_index_overlap(_ptr(idx_a), _ptr(idx_b), rows, k, _ptr(inter), _ptr(jac), _ptr(rec), _ptr(means),
                                   _stream(stream)))
     return inter, jac, rec, means
+
+
+def overlap_matrix(idx_list, stream=None):
+    """Cross-layer overlap heatmap (the skill page's Step 1 over every pair of layers):
+    for index caches idx_list[a] [..., k] int32 (rows ascending, -1 padded, all of one
+    shape), returns two [n, n] float64 numpy arrays, J[a, b] = mean over rows of the
+    Jaccard of idx_a and idx_b and R[a, b] = mean over rows of |A & B| / |B|, each entry
+    from one ic_index_overlap call (the diagonal too).  Synchronises the stream."""
+    n = len(idx_list)
+    J = np.zeros((n, n))
+    R = np.zeros((n, n))
+    pending = []
+    for a in range(n):
+        for b in range(n):
+            pending.append((a, b, index_overlap(idx_list[a], idx_list[b], stream=stream)[3]))
+    for a, b, means in pending:
+        m = means.cpu().numpy()
+        J[a, b], R[a, b] = float(m[0]), float(m[1])
+    return J, R
+
+
+def format_heatmap(M, labels=None, fmt="{:5.2f}") -> str:
+    """A plain-text rendering of a square matrix such as overlap_matrix's J."""
+    n = M.shape[0]
+    labels = labels or [str(i) for i in range(n)]
+    w = max(len(fmt.format(1.0)), max(len(x) for x in labels))
+    head = " " * w + " " + " ".join(x.rjust(w) for x in labels)
+    rows = [labels[i].rjust(w) + " " + " ".join(fmt.format(M[i, j]).rjust(w) for j in range(n)) for i in range(n)]
+    return "\n".join([head] + rows)
 
 
 def _attn_shape(q, kv, k, pos0=0) -> Shape:

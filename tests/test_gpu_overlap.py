@@ -68,3 +68,22 @@ def test_overlap_of_stack_layers():
     layers = synth.prefill_stack(cfg, device="cuda", pattern="FF")
     idx = [ic.indexer_topk(l["q_I"], l["w"], l["k_I"], cfg.k) for l in layers]
     _check(idx[0].cpu().numpy()[0], idx[1].cpu().numpy()[0])
+
+
+def test_overlap_matrix_of_four_layers():
+    """The all-pairs heatmap over four F layers of the tiny stack (bit-exact idx on integer
+    inputs): every entry against the oracle's Jaccard and set counts, the diagonal 1."""
+    cfg = synth.WORKLOADS["tiny"]
+    layers = synth.prefill_stack(cfg, device="cuda", pattern="FFFF")
+    idx = [ic.indexer_topk(l["q_I"], l["w"], l["k_I"], cfg.k) for l in layers]
+    J, R = ic.overlap_matrix(idx)
+    cpu = [i.cpu().numpy()[0] for i in idx]
+    for a in range(4):
+        for b in range(4):
+            want_j = O.jaccard_rows(cpu[a], cpu[b]).mean()
+            sets = [(set(x[x >= 0]), set(y[y >= 0])) for x, y in zip(cpu[a], cpu[b])]
+            want_r = np.mean([len(sa & sb) / len(sb) for sa, sb in sets])
+            assert abs(J[a, b] - want_j) <= 1e-5 and abs(R[a, b] - want_r) <= 1e-5, (a, b)
+    assert np.allclose(np.diag(J), 1.0, atol=1e-6) and np.allclose(J, J.T, atol=1e-6)
+    text = ic.format_heatmap(J, [f"L{l}" for l in range(4)])
+    assert text.count("\n") == 4 and "L3" in text
