@@ -14,6 +14,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <climits>
+#include <cstdint>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -94,6 +95,9 @@ ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode, bool v
     if (s.k < 1 || s.k > kMaxK) return fail(IC_ERR_SHAPE, "k must be in 1..%d (got %d)", kMaxK, s.k);
     if (s.H < 1 || s.H > 4096) return fail(IC_ERR_SHAPE, "H must be in 1..4096 (got %d)", s.H);
     if (s.d != 64 && s.d != 128) return fail(IC_ERR_SHAPE, "d must be 64 or 128 (got %d)", s.d);
+    // the gather kernels address a sequence's KV rows with 32-bit byte offsets
+    if ((int64_t)s.Lk * 4 * s.d > (int64_t)UINT32_MAX)
+        return fail(IC_ERR_SHAPE, "Lk (%d) x %d-byte KV rows exceeds 4 GiB per sequence", s.Lk, 4 * s.d);
     if (need_indexer) {
         if (s.idx_dtype != IC_BF16 && s.idx_dtype != IC_FP8_E4M3)
             return fail(IC_ERR_DTYPE, "idx_dtype must be IC_BF16 or IC_FP8_E4M3 (got %d)", s.idx_dtype);

@@ -86,8 +86,9 @@ typedef enum ic_dtype {
 } ic_dtype;
 
 /* Sizes of one call.  Limits: B >= 1; 1 <= Lq; pos0 >= 0; pos0 + Lq <= Lk
- * (prefill); H_I in 1..64; d_I in {32, 64, 128}; k in 1..4096; H >= 1;
- * d in {64, 128}; chunk 0 (= 4096) or 16..65536 in steps of 16. */
+ * (prefill); H_I in 1..64; d_I in {32, 64, 128}; k in 1..4096; H in 1..4096;
+ * d in {64, 128}; Lk * 4 * d < 4 GiB (one sequence's KV rows, addressed with
+ * 32-bit offsets); chunk 0 (= 4096) or 16..65536 in steps of 16. */
 typedef struct ic_shape {
     int32_t B;          /* sequences in the batch */
     int32_t Lq;         /* queries per sequence in this call (decode: 1) */

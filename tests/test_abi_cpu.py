@@ -76,6 +76,8 @@ def test_shape_and_workspace_errors(L):
     assert _stack("FSSS", shape=_shape(Lq=600)) == ic.IC_ERR_SHAPE        # pos0 + Lq > Lk
     assert _stack("FSSS", shape=_shape(idx_dtype=7)) == ic.IC_ERR_DTYPE
     assert _stack("FSSS", shape=_shape(chunk=100)) == ic.IC_ERR_SHAPE
+    assert _stack("FSSS", shape=_shape(Lk=1 << 24, d=64)) == ic.IC_ERR_SHAPE   # 4 GiB of KV rows
+    assert "4 GiB" in ic.last_error()
     assert _stack("FSSS", ws_bytes=16) == ic.IC_ERR_WORKSPACE
     need = ic.workspace_size(_shape(), ic.IC_OP_RUN_STACK)
     assert need >= 512 * 512 * 4                                           # one chunk x visible keys, fp32
