@@ -68,13 +68,19 @@ hipStream_t side_stream() {
 }
 
 // The F layer's own attention, run tile by tile on the side stream as the tiles' top-k
-// rows land (tile t's attention overlaps tile t + 1's scoring).
+// rows land (tile t's attention overlaps tile t + 1's scoring).  With a second score
+// tile, tile t's top-k runs there too: the caller's stream scores tile t + 1 into the
+// other buffer meanwhile, and waits only for the top-k of tile t - 1 (which read that
+// buffer) before doing so.
 struct TileAttn {
     const void* q;          // the layer's q [B, Lq, H, d]
     const void* kv;         // kv [B, Lk, 2, d]
     void* out;              // out [B, Lq, H, d]
     hipStream_t side;
     hipEvent_t fork;
+    float* tile2;           // second score tile, or nullptr (top-k on the caller's stream)
+    hipEvent_t freed[2];    // recorded on the side stream after the top-k reading buffer i
+    int64_t* ntiles;        // tiles scored so far in the call (buffer parity)
 };
 
 // Sizes the kernels support; `decode` relaxes the prefill position checks, and `varlen`
@@ -195,10 +201,18 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
                                const uint8_t* kb, int32_t* idx, void* ws, hipStream_t st, int64_t* tiles,
                                const int32_t* run_if = nullptr, const TileAttn* ta = nullptr, int b = 0) {
     const int chunk = chunk_of(s);
-    float* tile = static_cast<float*>(ws);
+    const bool two = ta && ta->tile2;                       // top-k and attention both on the side stream
     for (int c0 = 0; c0 < Lq; c0 += chunk) {
         const int nq = std::min(chunk, Lq - c0);
         const int64_t stride = round_up((int64_t)pos0 + c0 + nq, 4);
+        float* tile = static_cast<float*>(ws);
+        hipError_t e;
+        if (two) {
+            const int64_t n = (*ta->ntiles)++;
+            if (n & 1) tile = ta->tile2;
+            if (n >= 2 && (e = hipStreamWaitEvent(st, ta->freed[n & 1], 0)) != hipSuccess)
+                return hip_fail(e, "stream wait");
+        }
         ic_indexer_args a;
         a.q_I = qb;
         a.w = wb;
@@ -212,7 +226,7 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         a.d_I = s.d_I;
         a.fp8 = s.idx_dtype == IC_FP8_E4M3;
         a.run_if = run_if;
-        hipError_t e = launch_indexer_prefill(a, st);
+        e = launch_indexer_prefill(a, st);
         if (e != hipSuccess) return hip_fail(e, "indexer launch");
         ic_topk_args t;
         t.run_if = run_if;
@@ -225,12 +239,20 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         t.idx = idx + (size_t)c0 * s.k;
         t.max_len = pos0 + c0 + nq;
         t.cand = nullptr;
-        e = launch_topk(t, st);
+        // fork to the side stream once the work it depends on is enqueued: the scores
+        // (two tiles: the top-k goes there too) or the top-k rows (one tile)
+        auto fork = [&]() -> hipError_t {
+            hipError_t r = hipEventRecord(ta->fork, st);
+            return r == hipSuccess ? hipStreamWaitEvent(ta->side, ta->fork, 0) : r;
+        };
+        if (two && (e = fork()) != hipSuccess) return hip_fail(e, "stream fork");
+        e = launch_topk(t, two ? ta->side : st);
         if (e != hipSuccess) return hip_fail(e, "top-k launch");
+        if (two && (e = hipEventRecord(ta->freed[((*ta->ntiles) - 1) & 1], ta->side)) != hipSuccess)
+            return hip_fail(e, "event record");
         if (tiles) ++*tiles;
         if (ta) {                                           // this tile's attention, on the side stream
-            if ((e = hipEventRecord(ta->fork, st)) != hipSuccess) return hip_fail(e, "event record");
-            if ((e = hipStreamWaitEvent(ta->side, ta->fork, 0)) != hipSuccess) return hip_fail(e, "stream wait");
+            if (!two && (e = fork()) != hipSuccess) return hip_fail(e, "stream fork");
             const size_t row = (size_t)s.H * s.d;          // bf16 elements per query row
             ic_attn_args at;
             at.q = static_cast<const uint16_t*>(ta->q) + ((size_t)b * s.Lq + c0) * row;
@@ -322,9 +344,11 @@ extern "C" {
 size_t ic_workspace_size(const ic_shape* shape, int op) {
     switch (op) {
         case IC_OP_INDEXER_TOPK:
-        case IC_OP_RUN_STACK:
             if (check_shape(shape, true, false) != IC_OK) return 0;
             return indexer_ws(*shape);
+        case IC_OP_RUN_STACK:                       // two score tiles (one is enough to run)
+            if (check_shape(shape, true, false) != IC_OK) return 0;
+            return 2 * (size_t)round_up((int64_t)indexer_ws(*shape), 256);
         case IC_OP_SPARSE_ATTN:
         case IC_OP_INDEXER_SCORES:
             if (check_shape(shape, op == IC_OP_INDEXER_SCORES, false) != IC_OK) return 0;
@@ -460,24 +484,28 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
     // An F layer's attention runs tile by tile on a side stream, overlapping the scoring of
     // the layer's next tile; the caller's stream waits for it before the next layer.
     hipStream_t side = side_stream();
-    hipEvent_t ev[2] = {nullptr, nullptr};
-    if (side && (hipEventCreateWithFlags(&ev[0], hipEventDisableTiming) != hipSuccess ||
-                 hipEventCreateWithFlags(&ev[1], hipEventDisableTiming) != hipSuccess))
-        side = nullptr;
+    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};   // fork, join, two tile-freed events
+    for (int i = 0; side && i < 4; ++i)
+        if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
     struct Events {
         hipEvent_t* e;
         ~Events() {
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 4; ++i)
                 if (e[i]) (void)hipEventDestroy(e[i]);
         }
     } release{ev};
+    // With room for two score tiles, a tile's top-k also leaves the caller's stream.
+    const size_t tile_bytes = (size_t)round_up((int64_t)indexer_ws(*shape), 256);
+    float* tile2 = side && ws_bytes >= 2 * tile_bytes
+                       ? reinterpret_cast<float*>(static_cast<char*>(ws) + tile_bytes) : nullptr;
+    int64_t ntiles = 0;
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;                       // the index cache starts empty on every call
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const bool full = pattern[l] == 'F' || pattern[l] == '1';
         if (full) {
-            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0]};
+            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0], tile2, {ev[2], ev[3]}, &ntiles};
             r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side ? &ta : nullptr);
             if (r != IC_OK) return r;
             cached = true;

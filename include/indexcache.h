@@ -197,7 +197,11 @@ IC_API ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void
  * idx_cache: [B, Lq, k] int32, caller-owned, holds the last F layer's
  * indices on return.  stats (may be NULL) receives the counters.
  * An F layer's own attention runs score tile by score tile on the library's
- * second stream, overlapping the scoring of the layer's next tile. */
+ * second stream, overlapping the scoring of the layer's next tile.  With a
+ * workspace of ic_workspace_size(IC_OP_RUN_STACK) bytes (two score tiles) a
+ * tile's top-k runs there too, and the caller's stream scores the next tile
+ * into the other buffer meanwhile; one tile's worth is the minimum (then the
+ * top-k stays on `stream`). */
 IC_API ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* layers,
                        const ic_shape* shape, int32_t* idx_cache, void* ws, size_t ws_bytes,
                        ic_stats* stats, void* stream);
