@@ -381,7 +381,10 @@ def run_stack(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, c
         outs = [torch.empty_like(l["q"]) for l in layers]
     if idx_cache is None:
         idx_cache = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_size(s, IC_OP_RUN_STACK), dev, ws)
+    # a caller's workspace of one score tile is enough (top-k then stays on the stream);
+    # otherwise allocate the recommended two tiles
+    if ws is None or ws.numel() < workspace_size(s, IC_OP_INDEXER_TOPK) or ws.data_ptr() % 256:
+        ws = _workspace(workspace_size(s, IC_OP_RUN_STACK), dev, None)
     arr = _layers_struct(pattern, layers, outs)
     st = Stats()
     _check(lib().ic_run_stack(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(idx_cache), _ptr(ws),

@@ -118,3 +118,22 @@ def test_prefill_stacks_on_two_caller_streams():
     for ref, got in ((ref_a, got_a), (ref_b, got_b)):
         assert torch.equal(ref[1], got[1])
         assert all(torch.equal(x, y) for x, y in zip(ref[0], got[0]))
+
+
+def test_prefill_stack_one_tile_workspace_matches_two():
+    """run_stack with the minimum workspace (one score tile: every top-k on the caller's
+    stream) gives bitwise the results of the two-tile pipeline (top-k on the side stream)."""
+    cfg = synth.WORKLOADS["tiny"]
+    pattern, chunk = "FSFS", 128
+    layers = synth.prefill_stack(cfg, device="cuda", pattern=pattern)
+    shape = ic._stack_shape(pattern, layers, cfg.k, chunk, 0)
+    two = ic.workspace_size(shape, ic.IC_OP_RUN_STACK)
+    one = ic.workspace_size(shape, ic.IC_OP_INDEXER_TOPK)
+    assert two >= 2 * one
+    res = []
+    for nbytes in (one, two):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        res.append(ic.run_stack(pattern, layers, cfg.k, chunk=chunk, ws=ws))
+    torch.cuda.synchronize()
+    assert torch.equal(res[0][1], res[1][1])
+    assert all(torch.equal(a, b) for a, b in zip(res[0][0], res[1][0]))
