@@ -196,6 +196,6 @@ def test_run_stack_dynamic_validation(L):
     assert run("FSSS", layers=half) == ic.IC_ERR_ARG
     assert run("FSSS", wsb=16) == ic.IC_ERR_WORKSPACE
     need = L.ic_run_stack_dynamic_ws(ctypes.byref(s), 16)
-    assert need > ic.workspace_size(s, ic.IC_OP_RUN_STACK)               # tile + probe region
+    assert need > ic.workspace_size(s, ic.IC_OP_INDEXER_TOPK)            # one tile + probe region
     assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 1) > need          # more probe rows
     assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 0) == 0
