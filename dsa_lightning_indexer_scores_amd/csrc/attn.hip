@@ -39,11 +39,10 @@ namespace {
 
 constexpr int ATT_NW = 4;
 constexpr int KT = 32;                  // selected rows per step
-// Prefill: four waves (queries) per workgroup, one V stage per wave (18 KB of LDS per
-// wave, eight waves per CU).  Measured on a 32K layer: two V stages (six waves per CU)
-// and two- or eight-wave workgroups were all slower.
+// Prefill: four waves (queries) per workgroup with one K and one V stage each (18 KB of
+// LDS per wave, eight waves per CU).  Measured on a 32K layer: a second V stage (six waves
+// per CU) and two- or eight-wave workgroups were all slower.
 constexpr int DMA_NW = 4;
-constexpr int DMA_NVS = 1;
 // The running max of a head is moved (and O, l rescaled) only when a step's max
 // exceeds it by more than this many powers of two, so most steps skip the rescale;
 // the probabilities stay <= 2^RESCALE_LOG2, far inside fp32 and bf16 range.  Any
@@ -342,27 +341,27 @@ struct DmaGeom {
     __device__ static uint32_t swz(int r) { return dma_swz<NCH>(r); }
 };
 
-template <int D, int NW, int NVS>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
+template <int D>
+__global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
     float scale_log2) {
     using G = DmaGeom<D>;
     constexpr int CI = G::ICH / 64;                      // DMA instructions per idx chunk
-    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[NW][1 + NVS][G::SB];   // K, V[NVS]
-    __shared__ __attribute__((aligned(16))) int32_t ring_all[NW][2 * G::ICH];
+    __shared__ __attribute__((aligned(1024))) uint8_t stage_all[DMA_NW][2][G::SB];   // K, V
+    __shared__ __attribute__((aligned(16))) int32_t ring_all[DMA_NW][2 * G::ICH];
     const int lane = threadIdx.x & 63;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, g = lane >> 4;
     const int HG = (H + 15) / 16;
-    const int64_t item = (int64_t)blockIdx.x * NW + wv;
+    const int64_t item = (int64_t)blockIdx.x * DMA_NW + wv;
     const int hg = (int)(item % HG);
     const int64_t qi = item / HG;
     if (qi >= nq) return;
     const uint8_t* kst = stage_all[wv][0];
-    const uint8_t* vst0 = stage_all[wv][1];
+    const uint8_t* vst = stage_all[wv][1];
     const int32_t* ring = ring_all[wv];
-    const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst0), ring_lds = lds_addr(ring);
+    const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst), ring_lds = lds_addr(ring);
     const int seq = (int)(qi / q_per_seq);
     const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
     const int32_t* irow = idx + qi * k;
@@ -452,7 +451,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         const bool more = s + 1 < nsteps;
         const int cs = chunk_after(s) ? CI : 0;
         wait_vm_n(G::NI + cs);                           // K(s) landed (V(s) and its chunk may fly)
-        const uint8_t* vst = vst0 + (s % NVS) * G::SB;
         // S^T = K Q^T: lane (n, g) gets head n, keys 16*kt + 4g + e
         f32x4 sc[2];
 #pragma unroll
@@ -470,10 +468,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         if (more) {
             vmask_next = offsets(s + 1);
             issue_half(k_lds, 0);                        // K(s+1)
-            if (NVS > 1) {                               // V(s+1) into the other V stage
-                issue_half(v_lds + ((s + 1) % NVS) * G::SB, G::HB);
-                if (chunk_after(s + 1)) issue_chunk((s + 1) / G::SPC + 1);
-            }
         }
         float x[8];
 #pragma unroll
@@ -506,10 +500,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
         pf[1] = (int)pack_bf16x2(x[2], x[3]);
         pf[2] = (int)pack_bf16x2(x[4], x[5]);
         pf[3] = (int)pack_bf16x2(x[6], x[7]);
-        // V(s) landed: still in flight may be its chunk, K(s+1) and (two V stages) V(s+1) and its chunk
-        int after_v = cs;
-        if (more) after_v += G::NI + (NVS > 1 ? G::NI + (chunk_after(s + 1) ? CI : 0) : 0);
-        wait_vm_n(after_v);
+        // V(s) landed: still in flight may be the chunk issued after it and K(s+1)
+        wait_vm_n(cs + (more ? G::NI : 0));
         // O^T += V^T P^T: lane (n, g) reads 8 bytes of rows vrow and vrow + 16, d = 16*dt + 4*(n%4) .. +3
         const uint8_t* vr0 = vst + vrow * G::HB + 8 * (n & 1);
         const uint8_t* vr1 = vr0 + 16 * G::HB;
@@ -524,7 +516,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2))) vo
             o[dt] = mfma_bf16_k32(vf, pf, o[dt]);
         }
         lsum = mfma_bf16_k32(ones, pf, lsum);
-        if (NVS == 1 && more) {
+        if (more) {
             issue_half(v_lds, G::HB);                    // V(s+1)
             if (chunk_after(s + 1)) issue_chunk((s + 1) / G::SPC + 1);
         }
@@ -605,7 +597,7 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
         if ((int64_t)a.Lk * DmaGeom<D>::RB > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit row offsets
         const int64_t dblocks = (items + DMA_NW - 1) / DMA_NW;
-        hipLaunchKernelGGL((sparse_attn_dma_kernel<D, DMA_NW, DMA_NVS>), dim3((unsigned)dblocks), dim3(DMA_NW * 64), 0, st,
+        hipLaunchKernelGGL((sparse_attn_dma_kernel<D>), dim3((unsigned)dblocks), dim3(DMA_NW * 64), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out,
                            a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2);
         return hipGetLastError();
