@@ -207,11 +207,11 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         const int64_t stride = round_up((int64_t)pos0 + c0 + nq, 4);
         float* tile = static_cast<float*>(ws);
         hipError_t e;
+        const int64_t n = two ? (*ta->ntiles)++ : 0;        // this tile's number in the call
         if (two) {
-            const int64_t n = (*ta->ntiles)++;
             if (n & 1) tile = ta->tile2;
             if (n >= 2 && (e = hipStreamWaitEvent(st, ta->freed[n & 1], 0)) != hipSuccess)
-                return hip_fail(e, "stream wait");
+                return hip_fail(e, "stream wait");           // tile n - 2's top-k read this buffer
         }
         ic_indexer_args a;
         a.q_I = qb;
@@ -248,7 +248,7 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         if (two && (e = fork()) != hipSuccess) return hip_fail(e, "stream fork");
         e = launch_topk(t, two ? ta->side : st);
         if (e != hipSuccess) return hip_fail(e, "top-k launch");
-        if (two && (e = hipEventRecord(ta->freed[((*ta->ntiles) - 1) & 1], ta->side)) != hipSuccess)
+        if (two && (e = hipEventRecord(ta->freed[n & 1], ta->side)) != hipSuccess)
             return hip_fail(e, "event record");
         if (tiles) ++*tiles;
         if (ta) {                                           // this tile's attention, on the side stream

@@ -12,13 +12,11 @@
 //
 // This is measurement support only (built into libicprobe.so, loaded by the
 // benchmark); nothing on the indexer path uses it.
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+#include "common.h"
+
+using namespace ic;
 
 namespace {
-
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 __device__ uint32_t mix(uint32_t x) {
     x ^= x >> 16;
@@ -78,18 +76,6 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const int4* __restrict
     }
     out[(size_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-__device__ __forceinline__ void dma_b128(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
-__device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(lds) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
 
 // The sparse attention's data movement with no math: one wave per query row of idx
 // [nq, k], four waves per workgroup; per step of 32 entries the K halves and then the V
