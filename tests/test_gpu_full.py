@@ -1,6 +1,7 @@
 """GPU parity at the full workload sizes, in the launch configuration the benchmark
 times, on sampled rows the oracle computes one by one:
 
+  pair8k     L=8192, 'FS', bf16 indexer on scaled Gaussian inputs, k=2048
   stack32k   L=32768, 16 layers 'FSSS'x4, fp8 indexer, k=2048, chunk 4096
   long128k   L=131072, 8 layers 'FSSSSSSS', fp8 indexer, 4096-query chunks
   decode64k  B=32, 65536 cached tokens, 24 layers 'FSSS'x6 (two steps)
@@ -68,6 +69,26 @@ def test_stack32k_sampled():
         summary(f"stack32k {name}", {"certified": f"{cert}/{len(rows)}", "mean_overlap": mean_o,
                                      "min_overlap": min_o, "attn_max_rel_err": worst})
         assert mean_o >= 0.99 and worst <= ATTN_TOL
+
+
+def test_pair8k_sampled():
+    """One F + S pair at L = 8192 with a bf16 indexer on scaled Gaussian inputs (scores are
+    not exactly representable: rows are certified where the k-th and (k+1)-th oracle scores
+    separate beyond the fp32 error bound, else held to the top-k overlap bar)."""
+    cfg = synth.WORKLOADS["pair8k"]
+    print("[full] pair8k: generating inputs", flush=True)
+    layers = synth.prefill_stack(cfg, device="cuda")
+    outs, idx, st = ic.run_stack(cfg.pattern, layers, cfg.k)
+    torch.cuda.synchronize()
+    assert cfg.pattern == "FS" and st["indexer_calls"] == 1 and st["attn_calls"] == 2
+    rows = sample_rows(cfg.L, 128, seed=13)
+    print(f"[full] pair8k: checking {len(rows)} rows", flush=True)
+    idx_np = idx.cpu().numpy()[0]
+    cert, mean_o, min_o = _check_f_rows(layers[0], idx_np, rows, lambda t: t, cfg.k, cfg.H_I, cfg.d_I)
+    worst = max(_check_attn_rows(layers[l], outs[l], idx_np, rows, cfg.d) for l in range(2))
+    summary("pair8k", {"certified": f"{cert}/{len(rows)}", "mean_overlap": mean_o, "min_overlap": min_o,
+                       "attn_max_rel_err": worst})
+    assert mean_o >= 0.99 and worst <= ATTN_TOL
 
 
 def test_long128k_sampled():
