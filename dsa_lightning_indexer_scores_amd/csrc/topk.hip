@@ -257,9 +257,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
     }
     lo = wave_reduce(lo, OpMin());
     hi = wave_reduce(hi, OpMax());
-    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; }
-    // the first pass's histogram starts zeroed (both buffers when they alternate)
+    if (tid == 0) { kminmax[0] = 0xFFFFFFFFu; kminmax[1] = 0u; ncand = 0u; }
+    // the first pass's histogram starts zeroed (both buffers when they alternate); the
+    // candidate list starts as padding (key 0, below and unequal to every real key), so a
+    // ranking over it rounded up to 16 entries needs no padding step of its own
     for (int b = tid; b < NHB * NH * HIST_BINS; b += NT) (&hist[0][0])[b] = 0u;
+    for (int c = tid; c < CAND_CAP; c += NT) { cand_key[c] = 0u; cand_idx[c] = INT32_MAX; }
     __syncthreads();
     if (lane == 0) {
         atomicMin(&kminmax[0], lo);
@@ -415,9 +418,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
     if (ranked) {
         // Gather the bin's keys (with their positions) into LDS and find the k_rem-th of
         // them in (key descending, position ascending) order: the exact threshold pair,
-        // and how many keys share its value.
-        if (tid == 0) ncand = 0u;
-        __syncthreads();
+        // and how many keys share its value.  (ncand and the padded list were set up
+        // before the first pass.)
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
 #pragma unroll
@@ -438,11 +440,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
         }
         __syncthreads();
         const int nc = (int)min(ncand, (uint32_t)CAND_CAP);
-        // Pad the list to a multiple of 16 with key 0 (below and unequal to every real key),
-        // so the ranking reads 16 candidates per step with vector LDS loads.
+        // the ranking reads 16 candidates per step with vector LDS loads; the slots past nc
+        // still hold the padding written before the first pass
         const int ncp = (nc + 15) & ~15;
-        for (int c = nc + tid; c < ncp; c += NT) { cand_key[c] = 0u; cand_idx[c] = INT32_MAX; }
-        __syncthreads();
         for (int c = tid; c < nc; c += NT) {
             const uint32_t ck = cand_key[c];
             const int32_t ci = cand_idx[c];
