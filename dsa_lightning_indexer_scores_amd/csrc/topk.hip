@@ -107,13 +107,14 @@ __device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wt
 // keys from ckeys, positions from cand).
 enum { TOPK_ROWS = 0, TOPK_SEGS = 1, TOPK_GATHER = 2 };
 
-// Many-row launches of 1024-thread shapes with up to 24 keys per thread, and of the
-// 512 x 16 shape, are held to 64 VGPRs, so two (four) rows' workgroups share a CU and one
-// row's barriers and memory waits hide behind the others' work (a few spilled scalars cost
-// less than that); 32 keys per thread do not fit.  The decode shapes (a few rows per
-// launch) gain nothing from it and keep their registers.
+// Many-row launches of the 1024 x 16 and 512 x 16 shapes are held to 64 VGPRs, so two
+// (four) rows' workgroups share a CU and one row's barriers and memory waits hide behind
+// the others' work.  Measured in the stack's chunked launches: 1024 x 16 loses 8% without
+// the cap; 1024 x 24 is about 0.5% faster with one row per CU (at two, the rows' phases
+// contend and each takes about twice as long); 32 keys per thread do not fit.  The decode
+// shapes (a few rows per launch) keep their registers.
 constexpr int topk_waves_per_eu(int NT, int EPT, int MODE) {
-    return (MODE == TOPK_ROWS && ((NT == 1024 && EPT <= 24) || (NT == 512 && EPT <= 16))) ? 8 : 1;
+    return (MODE == TOPK_ROWS && ((NT == 1024 && EPT <= 16) || (NT == 512 && EPT <= 16))) ? 8 : 1;
 }
 
 template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
