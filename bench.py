@@ -531,6 +531,15 @@ def main():
         result["roofline"] = dict({k: v for k, v in kr[dom].items() if k in ("bound", "achieved", "peak", "unit",
                                                                           "frac")}, kernel=dom,
                                   traffic=measured_traffic(dom))
+        # Context for an algorithmic rate above the HBM peak (rows re-read from L2 / MALL):
+        # the measured HBM rate (counter bytes / the same launch time) and the fraction of
+        # a pure gather of the same rows, when the kernel has them.
+        rl = result["roofline"]
+        if rl["traffic"] is not None and rl["unit"] == "GB/s":
+            rl["traffic_gbs"] = round(rl["traffic"] / (kr[dom]["ms"] * 1e6), 1)
+            rl["traffic_frac"] = round(rl["traffic_gbs"] / rl["peak"], 4)
+        if "frac_of_gather_only" in kr[dom]:
+            rl["frac_of_gather_only"] = kr[dom]["frac_of_gather_only"]
         for name in kr:
             kr[name]["traffic"] = measured_traffic(name)
         result["kernels"] = kr
