@@ -475,8 +475,9 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(see the sharding notes in DESIGN.md); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
+              "(sequences and query blocks would shard across GPUs, but nothing here runs that); "
+              "use --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.only:
         only_kernel(args.only, args.reps)
