@@ -82,6 +82,7 @@ def parse():
     p.add_argument("--no-decode", action="store_true")
     p.add_argument("--no-kernels", action="store_true")
     p.add_argument("--no-allf", action="store_true")
+    p.add_argument("--no-long", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=640)
     p.add_argument("--only", choices=["indexer", "topk", "attention", "distill", "decode", "copy"], default=None,
@@ -239,6 +240,39 @@ def kernel_rooflines(cfg, layers, ws):
                           "work": f"{by:.4g} B = 256 B K per (selected row, served layer) x {rows} rows x "
                                   f"{len(served)} + q, idx, scores, kl (read twice: two sweeps)",
                           "method": "call minus the indexer's tiled launches"}
+    return out
+
+
+def bench_long():
+    """long128k (one 131072-token sequence, 8 layers 'FSSSSSSS'): ms per step of the
+    pattern and of the all-F stack on the same seeded layers, the closest in-build
+    analogue of the pages' long-context speedups."""
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+    cfg = synth.WORKLOADS["long128k"]
+    layers = synth.prefill_stack(cfg, device="cuda", pattern="F" * len(cfg.pattern))
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((cfg.B, cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    shape = ic._stack_shape(cfg.pattern, layers, cfg.k, cfg.chunk, 0)
+    ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_RUN_STACK), dtype=torch.uint8, device="cuda")
+    out = {"workload": f"long128k: B=1, L={cfg.L}, {len(cfg.pattern)} layers '{cfg.pattern}', H_I=64, d_I=128 fp8, "
+                       f"k={cfg.k}, H=16, d=128 bf16"}
+    ms = {}
+    for name, pat, n in (("pattern", cfg.pattern, 3), ("all_f", "F" * len(cfg.pattern), 2)):
+        ic.run_stack(pat, layers, cfg.k, chunk=cfg.chunk, outs=outs, idx_cache=idx, ws=ws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            ic.run_stack(pat, layers, cfg.k, chunk=cfg.chunk, outs=outs, idx_cache=idx, ws=ws)
+        torch.cuda.synchronize()
+        ms[name] = (time.perf_counter() - t0) * 1e3 / n
+    out["ms_per_step"] = round(ms["pattern"], 3)
+    out["tokens_per_s"] = round(cfg.B * cfg.L / (ms["pattern"] * 1e-3), 1)
+    out["all_f_ms_per_step"] = round(ms["all_f"], 3)
+    out["speedup_of_pattern"] = round(ms["all_f"] / ms["pattern"], 3)
+    del layers, outs, idx, ws
+    torch.cuda.empty_cache()
     return out
 
 
@@ -586,6 +620,10 @@ def main():
             dyn[name + "_refreshed_layers"] = int((r[3] == 1).sum().item())
         dyn["probe_ms_per_s_layer"] = round((dyn["never_ms_per_step"] - ms_step) / max(n_s, 1), 4)
         result["dynamic_refresh"] = dyn
+
+    if not args.no_long:
+        log("timing long128k")
+        result["long128k"] = bench_long()
 
     if not args.no_decode:
         log("timing decode64k")
