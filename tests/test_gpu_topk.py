@@ -56,6 +56,18 @@ def test_topk_long_rows(n0):
     _run(m, n0, 2048)
 
 
+@pytest.mark.parametrize("n0", [6000, 20000, 30000, 40000])
+def test_topk_long_rows_largest_k(n0):
+    """The largest k (4096) in the many-row mode: rows held in registers by each block
+    shape (512 x 16, 1024 x 24, 1024 x 32) and streamed rows, with the output staged in the
+    histograms' LDS at its full size and a heavy tie near the threshold."""
+    rng = np.random.default_rng(n0 + 1)
+    rows = 5
+    m = np.abs(rng.standard_normal((rows, n0 + rows)).astype(np.float32)) * 30
+    m[:, 2::9] = np.float32(27.0)
+    _run(m, n0, 4096)
+
+
 def test_topk_k_larger_than_rows():
     m = np.random.default_rng(1).standard_normal((8, 40)).astype(np.float32)
     _run(m, 10, 64)
