@@ -37,6 +37,9 @@ CASES = [
     (1, 1500, 0, 20, 64, 100, 20, 64, "bf16", "gauss_scaled", 512),
     (1, 1203, 0, 64, 128, 2048, 16, 128, "fp8", "gauss", 400),
     (1, 640, 0, 7, 32, 64, 5, 128, "fp8", "int3", 0),
+    # a single indexer head (the score is then a masked GEMM), both dtypes, bit-exact idx
+    (1, 900, 100, 1, 64, 128, 16, 64, "fp8", "int3", 0),
+    (1, 500, 0, 1, 32, 50, 3, 64, "bf16", "int3", 128),
 ]
 
 
