@@ -138,17 +138,30 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _need(t: torch.Tensor, name: str, dtypes, ndim: int):
+def _need(t: torch.Tensor, name: str, dtypes, ndim: int, gpu: bool = True):
+    """dtype, rank and layout of one tensor argument; gpu=False leaves the device to a
+    later check (the stack calls check every layer's shapes first)."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a tensor")
     if t.dtype not in dtypes:
         raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
     if t.dim() != ndim:
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if gpu and not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _on_gpu(named, device):
+    """Every (name, tensor) pair must live on the one GPU `device`."""
+    for name, t in named:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+        if t.device != device:
+            raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
 _IDX_DTYPES = (torch.bfloat16, torch.uint8, torch.float8_e4m3fn)
@@ -174,10 +187,10 @@ def _workspace(nbytes: int, device, ws: Optional[torch.Tensor]) -> Optional[torc
     return torch.empty(nbytes, dtype=torch.uint8, device=device)
 
 
-def _indexer_shape(q_I, w, k_I, k, pos0, chunk, H=1, d=64) -> Shape:
-    _need(q_I, "q_I", _IDX_DTYPES, 4)
-    _need(w, "w", (torch.float32,), 3)
-    _need(k_I, "k_I", _IDX_DTYPES, 3)
+def _indexer_shape(q_I, w, k_I, k, pos0, chunk, H=1, d=64, gpu=True) -> Shape:
+    _need(q_I, "q_I", _IDX_DTYPES, 4, gpu)
+    _need(w, "w", (torch.float32,), 3, gpu)
+    _need(k_I, "k_I", _IDX_DTYPES, 3, gpu)
     if k_I.dtype != q_I.dtype:
         raise TypeError("q_I and k_I must have the same dtype")
     B, Lq, H_I, d_I = q_I.shape
@@ -293,9 +306,9 @@ def format_heatmap(M, labels=None, fmt="{:5.2f}") -> str:
     return "\n".join([head] + rows)
 
 
-def _attn_shape(q, kv, k, pos0=0) -> Shape:
-    _need(q, "q", (torch.bfloat16,), 4)
-    _need(kv, "kv", (torch.bfloat16,), 4)
+def _attn_shape(q, kv, k, pos0=0, gpu=True) -> Shape:
+    _need(q, "q", (torch.bfloat16,), 4, gpu)
+    _need(kv, "kv", (torch.bfloat16,), 4, gpu)
     B, Lq, H, d = q.shape
     if kv.shape[0] != B or kv.shape[2] != 2 or kv.shape[3] != d:
         raise ValueError(f"kv must be [B, Lk, 2, d]; got {tuple(kv.shape)} for q {tuple(q.shape)}")
@@ -355,20 +368,97 @@ def _layers_struct(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], outs
     return arr
 
 
-def _stack_shape(pattern, layers, k, chunk, pos0):
-    first_f = next((l for c, l in zip(pattern, layers) if c in "F1" and "q_I" in l), None)
+def _check_like(t, name: str, dtype, shape):
+    """t must be a contiguous tensor of exactly this dtype and shape (the device is
+    checked afterwards, once every shape is known to be right)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_indexer_layers(pattern, layers, ref_shapes, dtype, optional_on_s: bool):
+    """Every F layer (and, with optional_on_s, every S layer that brings them) must carry
+    q_I, w, k_I of the reference shapes and dtype: the kernels read them at those sizes."""
+    q_shape, w_shape, k_shape = ref_shapes
+    for l, (c, lay) in enumerate(zip(pattern, layers)):
+        have = [lay.get(name) is not None for name in ("q_I", "w", "k_I")]
+        if c in "F1":
+            if not all(have):
+                raise ValueError(f"F layer {l} needs q_I, w and k_I")
+        elif not optional_on_s or not any(have):
+            continue
+        elif not all(have):
+            raise ValueError(f"layer {l}: q_I, w and k_I must be all present or all absent")
+        _check_like(lay["q_I"], f"layers[{l}].q_I", dtype, q_shape)
+        _check_like(lay["w"], f"layers[{l}].w", torch.float32, w_shape)
+        _check_like(lay["k_I"], f"layers[{l}].k_I", dtype, k_shape)
+
+
+def _stack_outputs(layers, outs, idx_cache, idx_shape, extra=()):
+    """Shape-check caller outputs, then put every tensor of the call on one GPU, then
+    allocate the outputs the caller did not pass.  Returns (outs, idx_cache)."""
     q = layers[0]["q"]
-    s = _attn_shape(q, layers[0]["kv"], k, pos0)
-    if first_f is not None:
-        si = _indexer_shape(first_f["q_I"], first_f["w"], first_f["k_I"], k, pos0, chunk)
-        s.H_I, s.d_I, s.idx_dtype, s.chunk = si.H_I, si.d_I, si.idx_dtype, si.chunk
-        if si.Lk != s.Lk:
-            raise ValueError("k_I and kv must have the same row capacity")
-    for lay in layers:
-        _need(lay["q"], "q", (torch.bfloat16,), 4)
-        _need(lay["kv"], "kv", (torch.bfloat16,), 4)
-        if tuple(lay["q"].shape) != tuple(q.shape) or tuple(lay["kv"].shape) != tuple(layers[0]["kv"].shape):
-            raise ValueError("every layer must have the same q and kv shapes")
+    if outs is not None:
+        if len(outs) != len(layers):
+            raise ValueError(f"outs must list {len(layers)} tensors, got {len(outs)}")
+        for l, o in enumerate(outs):
+            _check_like(o, f"outs[{l}]", torch.bfloat16, q.shape)
+    if idx_cache is not None:
+        _check_like(idx_cache, "idx_cache", torch.int32, idx_shape)
+    named = [(f"layers[{l}].{key}", lay.get(key)) for l, lay in enumerate(layers)
+             for key in ("q_I", "w", "k_I", "q", "kv")]
+    named += [(f"outs[{l}]", o) for l, o in enumerate(outs or [])]
+    named += [("idx_cache", idx_cache)] + list(extra)
+    _on_gpu(named, q.device)
+    if outs is None:
+        outs = [torch.empty_like(lay["q"]) for lay in layers]
+    if idx_cache is None:
+        idx_cache = torch.empty(idx_shape, dtype=torch.int32, device=q.device)
+    return outs, idx_cache
+
+
+def _check_pattern(pattern: str, n_layers: int):
+    """The library's pattern rules, checked before any tensor: length, the F/S/1/0
+    alphabet, and no S layer before the first F layer (nothing cached to reuse)."""
+    if len(pattern) != n_layers:
+        raise ValueError(f"pattern length {len(pattern)} != {n_layers} layers")
+    bad = [c for c in pattern if c not in "FS10"]
+    if bad:
+        raise ICError(IC_ERR_PATTERN, f"pattern char {bad[0]!r} is not one of F, S, 1, 0")
+    first_f = next((i for i, c in enumerate(pattern) if c in "F1"), len(pattern))
+    if first_f > 0:
+        raise NoCachedIndices(IC_ERR_NO_CACHED_INDICES,
+                              "no cached indices: layer 0 is S and no F layer precedes it")
+
+
+def _stack_shape(pattern, layers, k, chunk, pos0, optional_on_s: bool = False):
+    """Shape of a prefill or decode stack call, after checking the pattern and the dtype,
+    shape and layout of every layer's tensors (not yet their device: see _stack_outputs)."""
+    _check_pattern(pattern, len(layers))
+    q, kv = layers[0]["q"], layers[0]["kv"]
+    s = _attn_shape(q, kv, k, pos0, gpu=False)
+    for l, lay in enumerate(layers):
+        _check_like(lay["q"], f"layers[{l}].q", torch.bfloat16, q.shape)
+        _check_like(lay["kv"], f"layers[{l}].kv", torch.bfloat16, kv.shape)
+    src = next((l for c, l in zip(pattern, layers) if c in "F1" and l.get("q_I") is not None), None)
+    if src is None and optional_on_s:
+        src = next((l for l in layers if l.get("q_I") is not None), None)
+    if src is None:
+        _check_indexer_layers(pattern, layers, (None, None, None), None, optional_on_s)
+        return s
+    si = _indexer_shape(src["q_I"], src["w"], src["k_I"], k, pos0, chunk, gpu=False)
+    s.H_I, s.d_I, s.idx_dtype, s.chunk = si.H_I, si.d_I, si.idx_dtype, si.chunk
+    if si.Lk != s.Lk:
+        raise ValueError("k_I and kv must have the same row capacity")
+    if si.B != s.B or si.Lq != s.Lq:
+        raise ValueError("q_I and q must have the same batch and query count")
+    _check_indexer_layers(pattern, layers, (src["q_I"].shape, src["w"].shape, src["k_I"].shape),
+                          src["q_I"].dtype, optional_on_s)
     return s
 
 
@@ -376,11 +466,8 @@ def run_stack(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k: int, c
               outs: Optional[List[torch.Tensor]] = None, idx_cache=None, ws=None, stream=None):
     """Prefill an F/S stack.  layers[l]: q, kv (+ q_I, w, k_I on F layers)."""
     s = _stack_shape(pattern, layers, k, chunk, pos0)
+    outs, idx_cache = _stack_outputs(layers, outs, idx_cache, (s.B, s.Lq, k))
     dev = layers[0]["q"].device
-    if outs is None:
-        outs = [torch.empty_like(l["q"]) for l in layers]
-    if idx_cache is None:
-        idx_cache = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=dev)
     # a caller's workspace of one score tile is enough (top-k then stays on the stream);
     # otherwise allocate the recommended two tiles
     if ws is None or ws.numel() < workspace_size(s, IC_OP_INDEXER_TOPK) or ws.data_ptr() % 256:
@@ -399,12 +486,9 @@ def run_stack_dynamic(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k
     re-index when the pooled recall of their own top-k in it is below tau.
     Returns (outs, idx_cache, stats, refreshed [n_layers, B] int32 (-1: no probe),
     recall [n_layers, B] fp32 (nan: no probe)), all tensors on the GPU."""
-    s = _stack_shape(pattern, layers, k, chunk, pos0)
+    s = _stack_shape(pattern, layers, k, chunk, pos0, optional_on_s=True)
+    outs, idx_cache = _stack_outputs(layers, outs, idx_cache, (s.B, s.Lq, k))
     dev = layers[0]["q"].device
-    if outs is None:
-        outs = [torch.empty_like(l["q"]) for l in layers]
-    if idx_cache is None:
-        idx_cache = torch.empty((s.B, s.Lq, k), dtype=torch.int32, device=dev)
     refreshed = torch.full((len(layers), s.B), -1, dtype=torch.int32, device=dev)
     recall = torch.full((len(layers), s.B), float("nan"), dtype=torch.float32, device=dev)
     ws = _workspace(int(lib().ic_run_stack_dynamic_ws(ctypes.byref(s), probe_stride)), dev, ws)
@@ -425,31 +509,27 @@ def run_stack_varlen(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k:
     B, T = len(q_len), int(sum(q_len))
     if len(pos0) != B:
         raise ValueError("q_len and pos0 must have one entry per sequence")
+    _check_pattern(pattern, len(layers))
     q0, kv0 = layers[0]["q"], layers[0]["kv"]
-    _need(q0, "q", (torch.bfloat16,), 3)
-    _need(kv0, "kv", (torch.bfloat16,), 4)
+    _need(q0, "q", (torch.bfloat16,), 3, gpu=False)
+    _need(kv0, "kv", (torch.bfloat16,), 4, gpu=False)
     if q0.shape[0] != T or kv0.shape[0] != B or kv0.shape[2] != 2 or kv0.shape[3] != q0.shape[2]:
         raise ValueError(f"q {tuple(q0.shape)} / kv {tuple(kv0.shape)} do not match q_len (B={B}, T={T})")
     s = make_shape(B, T, kv0.shape[1], k, q0.shape[1], q0.shape[2], chunk=chunk)
-    first_f = next((l for c, l in zip(pattern, layers) if c in "F1" and "q_I" in l), None)
+    for l, lay in enumerate(layers):
+        _check_like(lay["q"], f"layers[{l}].q", torch.bfloat16, q0.shape)
+        _check_like(lay["kv"], f"layers[{l}].kv", torch.bfloat16, kv0.shape)
+    first_f = next((l for c, l in zip(pattern, layers) if c in "F1" and l.get("q_I") is not None), None)
     if first_f is not None:
-        _need(first_f["q_I"], "q_I", _IDX_DTYPES, 3)
-        _need(first_f["w"], "w", (torch.float32,), 2)
-        _need(first_f["k_I"], "k_I", _IDX_DTYPES, 3)
+        _need(first_f["q_I"], "q_I", _IDX_DTYPES, 3, gpu=False)
         s.H_I, s.d_I = first_f["q_I"].shape[1], first_f["q_I"].shape[2]
         s.idx_dtype = _idx_dtype(first_f["q_I"])
-        if (first_f["q_I"].shape[0] != T or tuple(first_f["w"].shape) != (T, s.H_I)
-                or tuple(first_f["k_I"].shape) != (B, s.Lk, s.d_I)):
-            raise ValueError("q_I [T,H_I,d_I], w [T,H_I] and k_I [B,Lk,d_I] do not match q / kv")
-    for lay in layers:
-        if tuple(lay["q"].shape) != tuple(q0.shape) or tuple(lay["kv"].shape) != tuple(kv0.shape):
-            raise ValueError("every layer must have the same q and kv shapes")
-    dev = q0.device
-    if outs is None:
-        outs = [torch.empty_like(l["q"]) for l in layers]
-    if idx_cache is None:
-        idx_cache = torch.empty((T, k), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_size(s, IC_OP_RUN_STACK_VARLEN), dev, ws)
+        _check_indexer_layers(pattern, layers, ((T, s.H_I, s.d_I), (T, s.H_I), (B, s.Lk, s.d_I)),
+                              first_f["q_I"].dtype, False)
+    else:
+        _check_indexer_layers(pattern, layers, (None, None, None), None, False)
+    outs, idx_cache = _stack_outputs(layers, outs, idx_cache, (T, k))
+    ws = _workspace(workspace_size(s, IC_OP_RUN_STACK_VARLEN), q0.device, ws)
     arr = _layers_struct(pattern, layers, outs)
     st = Stats()
     ql = (ctypes.c_int32 * B)(*[int(x) for x in q_len])
@@ -462,15 +542,13 @@ def run_stack_varlen(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], k:
 def decode_step(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], seq_len: torch.Tensor, k: int,
                 outs: Optional[List[torch.Tensor]] = None, idx_cache=None, ws=None, stream=None):
     """One decode step.  layers[l]: q [B,1,H,d], kv [B,cap,2,d] (+ q_I [B,1,H_I,d_I], w [B,1,H_I], k_I [B,cap,d_I])."""
-    _need(seq_len, "seq_len", (torch.int32,), 1)
     s = _stack_shape(pattern, layers, k, 0, 0)
     s.pos0 = 0
-    dev = layers[0]["q"].device
-    if outs is None:
-        outs = [torch.empty_like(l["q"]) for l in layers]
-    if idx_cache is None:
-        idx_cache = torch.empty((s.B, 1, k), dtype=torch.int32, device=dev)
-    ws = _workspace(workspace_size(s, IC_OP_DECODE_STEP), dev, ws)
+    if s.Lq != 1:
+        raise ValueError(f"decode takes one query per sequence; q has {s.Lq}")
+    _check_like(seq_len, "seq_len", torch.int32, (s.B,))
+    outs, idx_cache = _stack_outputs(layers, outs, idx_cache, (s.B, 1, k), extra=[("seq_len", seq_len)])
+    ws = _workspace(workspace_size(s, IC_OP_DECODE_STEP), layers[0]["q"].device, ws)
     arr = _layers_struct(pattern, layers, outs)
     st = Stats()
     _check(lib().ic_decode_step(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(seq_len), _ptr(idx_cache),

@@ -81,6 +81,7 @@ struct TileAttn {
     float* tile2;           // second score tile, or nullptr (top-k on the caller's stream)
     hipEvent_t freed[2];    // recorded on the side stream after the top-k reading buffer i
     int64_t* ntiles;        // tiles scored so far in the call (buffer parity)
+    bool* forked;           // set once any work of the call went to the side stream
 };
 
 // Sizes the kernels support; `decode` relaxes the prefill position checks, and `varlen`
@@ -243,7 +244,9 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
         // (two tiles: the top-k goes there too) or the top-k rows (one tile)
         auto fork = [&]() -> hipError_t {
             hipError_t r = hipEventRecord(ta->fork, st);
-            return r == hipSuccess ? hipStreamWaitEvent(ta->side, ta->fork, 0) : r;
+            if (r == hipSuccess) r = hipStreamWaitEvent(ta->side, ta->fork, 0);
+            if (r == hipSuccess) *ta->forked = true;
+            return r;
         };
         if (two && (e = fork()) != hipSuccess) return hip_fail(e, "stream fork");
         e = launch_topk(t, two ? ta->side : st);
@@ -499,23 +502,35 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
     float* tile2 = side && ws_bytes >= 2 * tile_bytes
                        ? reinterpret_cast<float*>(static_cast<char*>(ws) + tile_bytes) : nullptr;
     int64_t ntiles = 0;
+    bool forked = false;
+    // Joins the side stream back into the caller's: after every F layer, and on every
+    // return once work went there (an error part-way through a layer included), so no
+    // work of the call is left running on the library's stream unordered with `stream`.
+    auto join = [&]() -> hipError_t {
+        if (!forked) return hipSuccess;
+        forked = false;
+        hipError_t e = hipEventRecord(ev[1], side);
+        return e == hipSuccess ? hipStreamWaitEvent(st, ev[1], 0) : e;
+    };
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;                       // the index cache starts empty on every call
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const bool full = pattern[l] == 'F' || pattern[l] == '1';
         if (full) {
-            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0], tile2, {ev[2], ev[3]}, &ntiles};
+            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0], tile2, {ev[2], ev[3]}, &ntiles, &forked};
             r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side ? &ta : nullptr);
-            if (r != IC_OK) return r;
+            if (r != IC_OK) {
+                (void)join();                  // keeps the failure's own status and message
+                return r;
+            }
             cached = true;
             ++cnt.indexer_calls;
         } else if (!cached) {
             return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
         if (full && side) {                    // join: the layer's tile attentions are done
-            hipError_t e = hipEventRecord(ev[1], side);
-            if (e == hipSuccess) e = hipStreamWaitEvent(st, ev[1], 0);
+            hipError_t e = join();
             if (e != hipSuccess) return hip_fail(e, "stream join");
         } else {
             r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);

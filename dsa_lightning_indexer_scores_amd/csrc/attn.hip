@@ -25,7 +25,8 @@
 //       k order matches the transposed read, so no shuffle is needed);
 //   l += ones^T P^T, one more MFMA, so the denominator sums the same bf16 P
 //       as the numerator and costs no VALU.
-// Steps past a query's last real idx entry are not run.
+// Steps past a query's last real idx entry are not run; a query whose idx row has
+// no valid entry at all gets a zero output vector.
 // Decode splits a query's rows over several waves (split-K): the 4 waves of a
 // workgroup merge their partial (max, sum, O) in LDS, and a small kernel merges
 // the workgroups' partials in split order, so results are deterministic.  (A
@@ -524,7 +525,8 @@ __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     }
     __builtin_amdgcn_s_waitcnt(0);                       // an idx chunk may still be in flight
     if (head < H) {
-        const float inv = 1.f / lsum[0];
+        // a row without a single valid entry has nothing to attend to: its output is zero
+        const float inv = lsum[0] > 0.f ? 1.f / lsum[0] : 0.f;
         uint16_t* op = out + (qi * H + head) * D + 4 * g;
 #pragma unroll
         for (int dt = 0; dt < G::NDT; ++dt) {
@@ -582,7 +584,7 @@ __global__ __launch_bounds__(D) void attn_combine_kernel(const float* __restrict
             den += c * ps[16 * D + 2 * hn + 1];
         }
     }
-    const float v = num / den;
+    const float v = den > 0.f ? num / den : 0.f;             // no valid entry in any split: zero
     uint32_t u = __float_as_uint(v);
     u += 0x7FFFu + ((u >> 16) & 1u);
     out[(qi * H + head) * D + dd] = (uint16_t)(u >> 16);

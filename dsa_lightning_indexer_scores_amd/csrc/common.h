@@ -171,6 +171,7 @@ struct ic_topk_args {
 // segments' candidates; that needs topk_ws_bytes() of workspace (0 otherwise).
 constexpr int TOPK_SEG = 16384;                 // keys per segment (one register-resident block)
 constexpr int TOPK_SEG_MAX_ROWS = 1024;
+constexpr int TOPK_GATHER_MAX = 16384;          // candidates per row the second launch ranks
 int topk_segments(const ic_topk_args& a);
 size_t topk_ws_bytes(const ic_topk_args& a);
 hipError_t launch_topk(const ic_topk_args& a, hipStream_t st);

@@ -554,11 +554,18 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
     } while (0)
     if (len <= 2048) IC_TOPK_GO(256, 8, false);
     if (len <= 4096) IC_TOPK_GO(256, 16, false);
-    if (MODE == TOPK_ROWS && len <= 8192) IC_TOPK_GO(512, 16, false);
-    if (len <= 16384) IC_TOPK_GO(1024, 16, false);
-    if (MODE == TOPK_ROWS && len <= 24576) IC_TOPK_GO(1024, 24, false);
-    if (MODE != TOPK_ROWS || len <= 32768) IC_TOPK_GO(1024, 32, false);
-    IC_TOPK_GO(1024, 32, true);
+    if constexpr (MODE == TOPK_ROWS) {
+        if (len <= 8192) IC_TOPK_GO(512, 16, false);
+        if (len <= 16384) IC_TOPK_GO(1024, 16, false);
+        if (len <= 24576) IC_TOPK_GO(1024, 24, false);
+        if (len <= 32768) IC_TOPK_GO(1024, 32, false);
+        IC_TOPK_GO(1024, 32, true);
+    } else {
+        // a segment, or a candidate list of at most TOPK_GATHER_MAX keys: one register-resident
+        // block of 1024 x 16 (32 keys per thread spill in these modes)
+        if (len <= 16384) IC_TOPK_GO(1024, 16, false);
+        return hipErrorInvalidValue;
+    }
 #undef IC_TOPK_GO
 }
 
@@ -567,7 +574,8 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
 int topk_segments(const ic_topk_args& a) {
     if (a.max_len <= 32768 || a.rows > TOPK_SEG_MAX_ROWS) return 0;
     const int nseg = (a.max_len + TOPK_SEG - 1) / TOPK_SEG;
-    return (int64_t)nseg * a.k <= 32768 ? nseg : 0;          // the candidate list must stay register-resident
+    // the candidate list must fit one register-resident 1024 x 16 block
+    return (int64_t)nseg * a.k <= TOPK_GATHER_MAX ? nseg : 0;
 }
 
 size_t topk_ws_bytes(const ic_topk_args& a) {

@@ -45,10 +45,13 @@
  *    forked from and joined back to `stream` with events inside the call, so
  *    the call stays capturable in a HIP graph.  Concurrent calls on one device
  *    share that stream: they may wait on each other there, never reorder.
- *  - Arguments are validated before any launch; a failing call returns a
- *    non-zero ic_status, launches nothing and leaves outputs untouched.
- *    ic_last_error() then describes the failure (thread-local string).
- *    A fault inside a kernel surfaces later, at the caller's next sync.
+ *  - Arguments are validated before any launch; a call that fails validation
+ *    returns a non-zero ic_status, launches nothing and leaves outputs
+ *    untouched.  A HIP error part-way through a call (IC_ERR_HIP) can leave
+ *    outputs partly written; work the call already sent to the library's
+ *    second stream is joined back into `stream` before it returns.
+ *    ic_last_error() describes any failure (thread-local string).  A fault
+ *    inside a kernel surfaces later, at the caller's next sync.
  *  - No C++ exception crosses this interface.
  */
 #ifndef INDEXCACHE_H
@@ -181,9 +184,11 @@ IC_API ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32
 IC_API size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k);
 
 /* Sparse attention of one layer (arXiv abstract: core attention over the k
- * selected tokens): out [B, Lq, H, d] bf16 from q, kv and idx [B, Lq, k]
- * (entries < 0 are skipped; every row must hold at least one entry >= 0 and
- * every entry must be < Lk).  Softmax scale 1/sqrt(d), fp32 accumulation. */
+ * selected tokens): out [B, Lq, H, d] bf16 from q, kv and idx [B, Lq, k].
+ * Entries outside [0, Lk) (the top-k's -1 padding) are skipped; a row with no
+ * entry inside [0, Lk) has nothing to attend to and its output vectors are
+ * zero.  The rows named may repeat and need not be sorted.  Softmax scale
+ * 1/sqrt(d), fp32 accumulation.  ws is unused (NULL, 0). */
 IC_API ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx,
                          void* out, void* ws, size_t ws_bytes, void* stream);
 

@@ -96,15 +96,6 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, val).astype(np.float64)
 
 
-def decode(raw: np.ndarray, dtype: str) -> np.ndarray:
-    """Decode a raw storage array: 'bf16' (uint16 bits), 'fp8' (uint8 e4m3fn codes) or fp32/fp64."""
-    if dtype == "bf16":
-        return decode_bf16(raw)
-    if dtype == "fp8":
-        return decode_e4m3(raw)
-    return np.asarray(raw, dtype=np.float64)
-
-
 # ---------------------------------------------------------------------------
 # O1: lightning-indexer scores      [Abstract; Blog, Introduction; Note, How It Works]
 # ---------------------------------------------------------------------------

@@ -124,9 +124,12 @@ def test_topk_rows_seq_workspace_sizes():
     assert ic.topk_rows_seq_ws(4096, 65600, 2048) == 0
     assert ic.topk_rows_seq_ws(32, 65600, 2048) == 2 * 32 * 5 * 2048 * 4
     assert ic.topk_rows_seq_ws(3, 40000, 100) == 2 * 3 * 3 * 100 * 4
-    assert ic.topk_rows_seq_ws(8, 200000, 2048) == 2 * 8 * 13 * 2048 * 4
-    # a candidate list longer than one register-resident block falls back to streaming
-    assert ic.topk_rows_seq_ws(8, 300000, 2048) == 0
+    assert ic.topk_rows_seq_ws(8, 131072, 2048) == 2 * 8 * 8 * 2048 * 4
+    # a candidate list longer than one register-resident 1024 x 16 block (16384 keys)
+    # falls back to streaming
+    assert ic.topk_rows_seq_ws(8, 131073, 2048) == 0
+    assert ic.topk_rows_seq_ws(8, 65536, 4096) == 2 * 8 * 4 * 4096 * 4
+    assert ic.topk_rows_seq_ws(8, 65537, 4096) == 0
 
 
 def test_mfma_probe_library_exports_its_entry():
@@ -199,3 +202,15 @@ def test_run_stack_dynamic_validation(L):
     assert need > ic.workspace_size(s, ic.IC_OP_INDEXER_TOPK)            # one tile + probe region
     assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 1) > need          # more probe rows
     assert L.ic_run_stack_dynamic_ws(ctypes.byref(s), 0) == 0
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0,
+                    reason="launches with placeholder pointers: only where no GPU can run them")
+def test_hip_failure_after_validation_is_reported(L):
+    """With arguments that pass validation, a HIP runtime failure (here: no device) comes
+    back as IC_ERR_HIP naming the launch that failed, from a one-layer call and from the
+    middle of a stack call, never as a crash."""
+    s = _shape()
+    r = L.ic_indexer_scores(ctypes.byref(s), FAKE, FAKE, FAKE, FAKE, 512, None)
+    assert r == ic.IC_ERR_HIP and "indexer launch" in ic.last_error()
+    assert _stack("FSSS") == ic.IC_ERR_HIP and "launch" in ic.last_error()

@@ -78,3 +78,26 @@ def test_attention_idx_ring_boundaries(k):
     err = attn_rel_err(dec(out)[0], ref)
     summary(f"attention ring boundaries k={k}", {"max_rel_err": err})
     assert err <= ATTN_TOL
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_rows_without_a_valid_entry_give_zero(d):
+    """A row whose entries are all -1 or all >= Lk has nothing to attend to: its output
+    vectors are zero (finite), and the other rows are unaffected."""
+    torch.manual_seed(d)
+    Lq, Lk, H, k = 40, 300, 16, 96
+    q = (torch.randn(1, Lq, H, d) * 0.5).to(torch.bfloat16).cuda()
+    kv = (torch.randn(1, Lk, 2, d) * 0.5).to(torch.bfloat16).cuda()
+    idx = idx_patterns(Lq, Lk, k, seed=d)
+    empty = [0, 7, 13, 39]
+    idx[[0, 13]] = -1
+    idx[7] = Lk + np.arange(k)                                   # past the KV rows
+    idx[39, :] = -1
+    idx[39, 5] = Lk                                              # one entry, out of range
+    out = ic.sparse_attn(q, kv, torch.from_numpy(idx)[None].cuda())
+    torch.cuda.synchronize()
+    got = dec(out)[0]
+    assert np.all(got[empty] == 0.0)
+    keep = [t for t in range(Lq) if t not in empty]
+    ref = O.sparse_attn(dec(q)[0][keep], dec(kv)[0], idx[keep])
+    assert attn_rel_err(got[keep], ref) <= ATTN_TOL

@@ -1,0 +1,195 @@
+"""GPU parity where the indexer weights take either sign, where the fp8 head-weighted
+linear term runs with partly empty head tiles, and where dynamic refresh spans
+several score tiles.
+
+The score sum_j w_j * max(0, q_j . k) allows any sign of w.  The fp8 prefill kernel
+rewrites w * max(0, y) as (w/2) |y| + (w/2) y and folds the second half into a
+head-weighted query; that identity holds for either sign of w, and these tests
+exercise it.  On small-integer inputs (values in [-3, 3], w in {-3..3}) every
+partial sum of either form is an exact integer or half-integer below 2^24, so the
+fp32 scores and the indices must equal the oracle bit for bit.  On Gaussian
+inputs rows are certified by the fp32 error bound (|w| enters it) and otherwise
+held to the top-k overlap bar.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import dsa_lightning_indexer_scores_amd as ic
+from dsa_lightning_indexer_scores_amd import synth
+from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, sample_rows, summary
+
+pytestmark = pytest.mark.gpu
+
+
+def _layer(B, Lq, Lk, H_I, d_I, H, d, dtype, dist, seed, full=True, signed=True):
+    """Random layer inputs; w is drawn from {-3..3} (int3) or N(0, 1) (gauss) when signed."""
+    g = torch.Generator().manual_seed(seed)
+
+    def vals(shape):
+        if dist == "int3":
+            return torch.randint(-3, 4, shape, generator=g).float()
+        return torch.randn(shape, generator=g)
+
+    lay = {"q": synth.encode(vals((B, Lq, H, d)), "bf16"), "kv": synth.encode(vals((B, Lk, 2, d)), "bf16")}
+    if full:
+        lay["q_I"] = synth.encode(vals((B, Lq, H_I, d_I)), dtype)
+        lay["k_I"] = synth.encode(vals((B, Lk, d_I)), dtype)
+        if dist == "int3":
+            lo = -3 if signed else 0
+            lay["w"] = torch.randint(lo, 4, (B, Lq, H_I), generator=g).float()
+        else:
+            lay["w"] = torch.randn((B, Lq, H_I), generator=g) if signed else torch.rand((B, Lq, H_I), generator=g)
+    return lay
+
+
+INT_CASES = [
+    # B, Lq, pos0, H_I, d_I, k, dtype, chunk
+    (2, 900, 300, 64, 128, 200, "fp8", 256),
+    (1, 1100, 0, 64, 128, 333, "bf16", 512),
+    (1, 700, 50, 20, 128, 128, "fp8", 0),      # partial head tiles on the fp8 linear-term path
+    (1, 650, 0, 48, 64, 96, "fp8", 208),
+    (1, 600, 17, 33, 32, 64, "bf16", 0),
+]
+
+
+@pytest.mark.parametrize("case", INT_CASES, ids=lambda c: f"B{c[0]}_L{c[1]}_p{c[2]}_HI{c[3]}_dI{c[4]}_{c[6]}")
+def test_signed_w_integer_scores_and_idx_bit_exact(case):
+    B, Lq, pos0, H_I, d_I, k, dtype, chunk = case
+    Lk = pos0 + Lq
+    H, d = 16, 64
+    layers = [_layer(B, Lq, Lk, H_I, d_I, H, d, dtype, "int3", 500 + i, full=(c == "F")) for i, c in enumerate("FS")]
+    assert (layers[0]["w"] < 0).any() and (layers[0]["w"] > 0).any()
+    gpu = [{kk: v.cuda() for kk, v in lay.items()} for lay in layers]
+    f = gpu[0]
+    scores = ic.indexer_scores(f["q_I"], f["w"], f["k_I"], pos0=pos0).cpu().numpy()
+    outs, idx_cache, st = ic.run_stack("FS", gpu, k, chunk=chunk, pos0=pos0)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == 1
+    idx = idx_cache.cpu().numpy()
+    n_neg = 0
+    worst = 0.0
+    for b in range(B):
+        r = {kk: dec(v[b]) for kk, v in layers[0].items()}
+        for t in range(Lq):
+            want = O.indexer_scores_row(r["q_I"][t], r["w"][t], r["k_I"], pos0 + t)
+            got = scores[b, t, : pos0 + t + 1].astype(np.float64)
+            assert np.array_equal(got, want), f"b={b} t={t}: scores differ"
+            n_neg += int((want < 0).sum())
+        assert np.array_equal(idx[b], O.indexer_topk(r["q_I"], r["w"], r["k_I"], k, pos0)), f"b={b}: idx differ"
+        for l in range(2):
+            ref = O.sparse_attn(dec(layers[l]["q"][b]), dec(layers[l]["kv"][b]), idx[b])
+            worst = max(worst, attn_rel_err(dec(outs[l][b]), ref))
+    summary(f"signed int {case}", {"negative_scores": n_neg, "attn_max_rel_err": worst})
+    assert n_neg > 0, "the case must produce negative scores"
+    assert worst <= ATTN_TOL
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_signed_w_integer_decode_bit_exact(dtype):
+    B, cap, H_I, d_I, H, d, k = 3, 1500, 64, 128, 16, 128, 300
+    seq_len = [1500, 421, 2]
+    pattern = "FSF"
+    caches = [_layer(B, 1, cap, H_I, d_I, H, d, dtype, "int3", 700 + i, full=(c == "F")) for i, c in enumerate(pattern)]
+    gpu = [{kk: v.cuda() for kk, v in lay.items()} for lay in caches]
+    sl = torch.tensor(seq_len, dtype=torch.int32, device="cuda")
+    outs, idx_cache, st = ic.decode_step(pattern, gpu, sl, k)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == 2
+    ref_layers = []
+    for lay in caches:
+        r = {"q": dec(lay["q"])[:, 0], "kv": dec(lay["kv"])}
+        if "q_I" in lay:
+            r.update(q_I=dec(lay["q_I"])[:, 0], w=dec(lay["w"])[:, 0], k_I=dec(lay["k_I"]))
+        ref_layers.append(r)
+    o_ref, idx_ref, calls = O.decode_step(pattern, ref_layers, seq_len, k)
+    assert calls == 2
+    assert np.array_equal(idx_cache.cpu().numpy()[:, 0], idx_ref[-1])
+    for l in range(len(pattern)):
+        assert attn_rel_err(dec(outs[l])[:, 0], o_ref[l]) <= ATTN_TOL
+
+
+def test_signed_w_gaussian_fp8_partial_heads():
+    """fp8, H_I = 48 (the last head tile half empty), w ~ N(0, 1), several tiles, pos0 > 0."""
+    B, Lq, pos0, H_I, d_I, k = 1, 1300, 211, 48, 128, 256
+    lay = _layer(B, Lq, pos0 + Lq, H_I, d_I, 16, 64, "fp8", "gauss", 91)
+    g = {kk: v.cuda() for kk, v in lay.items()}
+    idx = ic.indexer_topk(g["q_I"], g["w"], g["k_I"], k, pos0=pos0, chunk=400).cpu().numpy()[0]
+    r = {kk: dec(v[0]) for kk, v in lay.items()}
+    cert, ovl = 0, []
+    for t in range(0, Lq, 3):
+        c, o, _ = check_topk_row(idx[t], r["q_I"][t], r["w"][t], r["k_I"], pos0 + t, k, H_I, d_I)
+        cert += c
+        ovl.append(o)
+    summary("signed gauss fp8 H_I=48", {"certified": f"{cert}/{len(ovl)}", "mean_overlap": np.mean(ovl)})
+    assert np.mean(ovl) >= 0.99
+
+
+@pytest.mark.parametrize("name", ["pair8k", "stack32k"])
+def test_signed_w_gaussian_full_size_sampled(name):
+    """The full-size shapes in the stack's launch configuration with w ~ N(0, 1) in place of
+    U(0, 1): sampled rows certified against the oracle, overlap >= 0.99."""
+    cfg = synth.WORKLOADS[name]
+    print(f"[signed] {name}: generating inputs", flush=True)
+    layers = synth.prefill_stack(cfg, device="cuda", pattern="FS")
+    gen = torch.Generator(device="cuda").manual_seed(4242)
+    layers[0]["w"] = torch.randn(layers[0]["w"].shape, generator=gen, device="cuda")
+    outs, idx, st = ic.run_stack("FS", layers, cfg.k, chunk=cfg.chunk)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == 1
+    rows = sample_rows(cfg.L, 96, seed=21)
+    print(f"[signed] {name}: checking {len(rows)} rows", flush=True)
+    idx_np = idx.cpu().numpy()[0]
+    sel = torch.as_tensor(rows, device="cuda")
+    k_I = dec(layers[0]["k_I"][0])
+    q_I = dec(layers[0]["q_I"][0][sel])
+    w = dec(layers[0]["w"][0][sel])
+    cert, ovl = 0, []
+    for i, t in enumerate(rows):
+        c, o, _ = check_topk_row(idx_np[t], q_I[i], w[i], k_I, int(t), cfg.k, cfg.H_I, cfg.d_I)
+        cert += c
+        ovl.append(o)
+    worst = 0.0
+    qs = dec(layers[1]["q"][0][sel])
+    got = dec(outs[1][0][sel])
+    for i, t in enumerate(rows):
+        s = idx_np[t][idx_np[t] >= 0]
+        kv_sel = dec(layers[1]["kv"][0].index_select(0, torch.as_tensor(s, device="cuda").long()))
+        ref = O.sparse_attn_row(qs[i], kv_sel, np.arange(len(s), dtype=np.int32), 1.0 / np.sqrt(cfg.d))
+        worst = max(worst, attn_rel_err(got[i], ref))
+    summary(f"signed gauss {name}", {"certified": f"{cert}/{len(rows)}", "mean_overlap": np.mean(ovl),
+                                     "min_overlap": np.min(ovl), "attn_max_rel_err": worst})
+    assert np.mean(ovl) >= 0.99 and worst <= ATTN_TOL
+
+
+@pytest.mark.parametrize("dtype", ["fp8", "bf16"])
+def test_dynamic_refresh_several_tiles_bit_exact(dtype):
+    """run_stack_dynamic with chunk 128 at L = 512 (four score tiles, each refresh launch gated
+    on the device flag), signed integer inputs: decisions, recalls and the final cache equal
+    the oracle exactly, with one tau that refreshes every probed layer, one that refreshes
+    none and one between the layers' recalls."""
+    L, H_I, d_I, k, H, d = 512, 16, 64, 48, 4, 64
+    pattern = "FSSS"
+    layers = [_layer(1, L, L, H_I, d_I, H, d, dtype, "int3", 800 + i) for i in range(4)]
+    gpu = [{kk: v.cuda() for kk, v in lay.items()} for lay in layers]
+    ref = [{kk: dec(v)[0] for kk, v in lay.items()} for lay in layers]
+    _, _, _, rec0 = O.run_stack_dynamic(pattern, ref, k, 5, 0.0)
+    mid = float(np.median(rec0[1:]))
+    for tau in (0.0, mid, 1.01):
+        outs, idx_cache, st, refreshed, recall = ic.run_stack_dynamic(pattern, gpu, k, probe_stride=5, tau=tau,
+                                                                      chunk=128)
+        torch.cuda.synchronize()
+        o_ref, used, ref_refreshed, ref_recall = O.run_stack_dynamic(pattern, ref, k, 5, tau)
+        got = refreshed.cpu().numpy()[:, 0]
+        assert got[0] == -1 and np.array_equal(got[1:] == 1, ref_refreshed[1:]), (tau, got, ref_refreshed)
+        assert np.array_equal(recall.cpu().numpy()[1:, 0], ref_recall[1:].astype(np.float32))
+        assert np.array_equal(idx_cache.cpu().numpy()[0], used[-1])
+        assert st["score_tiles"] == 4 * (1 + 3), st          # every gated refresh tile is launched
+        errs = [attn_rel_err(dec(outs[l])[0], o_ref[l]) for l in range(4)]
+        summary(f"dynamic {dtype} chunk=128 tau={tau:.4f}", {"refreshed": got.tolist(), "max_rel_err": max(errs)})
+        assert max(errs) <= ATTN_TOL
+        if tau == 0.0:
+            assert not ref_refreshed.any()
+        if tau > 1.0:
+            assert ref_refreshed[1:].all()
