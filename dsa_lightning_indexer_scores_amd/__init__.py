@@ -18,6 +18,7 @@ Functions mirror the C entry points (without the ``ic_`` prefix):
   run_stack_dynamic(pattern, layers, k, probe_stride, tau)
                                         -> (outs, idx_cache, stats, refreshed, recall)
   decode_step(pattern, layers, seq_len, k) -> (outs, idx_cache, stats)
+  decode_step_static(pattern, layers, seq_len, k) -> (outs, idx_cache, stats), no workspace
   index_overlap(idx_a, idx_b)           -> (inter, jaccard, recall, means)
   overlap_matrix(idx_list)              -> (J [n, n], R [n, n]) mean Jaccard / recall of every pair
   distill_kl(q_I, w, k_I, idx, qs, kvs) -> (kl [B, Lq], mean)
@@ -101,12 +102,13 @@ def lib() -> ctypes.CDLL:
     L.ic_run_stack_dynamic_ws.restype = sz
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
+    L.ic_decode_step_static.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, P(Stats), vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
     for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
                "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen", "ic_distill_kl", "ic_run_stack_dynamic",
-               "ic_decode_step", "ic_get_stats"):
+               "ic_decode_step", "ic_decode_step_static", "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -553,6 +555,24 @@ def decode_step(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], seq_len
     st = Stats()
     _check(lib().ic_decode_step(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(seq_len), _ptr(idx_cache),
                                 _ptr(ws), 0 if ws is None else ws.numel(), ctypes.byref(st), _stream(stream)))
+    return outs, idx_cache, st.as_dict()
+
+
+def decode_step_static(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], seq_len: torch.Tensor, k: int,
+                       outs: Optional[List[torch.Tensor]] = None, idx_cache=None, stream=None):
+    """decode_step without a workspace: the library's fixed per-GPU scratch array serves
+    (IC_DECODE_STATIC_SCRATCH_BYTES); nothing is allocated when outs and idx_cache are
+    given.  Calls that overlap on one GPU race on that array."""
+    s = _stack_shape(pattern, layers, k, 0, 0)
+    s.pos0 = 0
+    if s.Lq != 1:
+        raise ValueError(f"decode takes one query per sequence; q has {s.Lq}")
+    _check_like(seq_len, "seq_len", torch.int32, (s.B,))
+    outs, idx_cache = _stack_outputs(layers, outs, idx_cache, (s.B, 1, k), extra=[("seq_len", seq_len)])
+    arr = _layers_struct(pattern, layers, outs)
+    st = Stats()
+    _check(lib().ic_decode_step_static(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(seq_len),
+                                       _ptr(idx_cache), ctypes.byref(st), _stream(stream)))
     return outs, idx_cache, st.as_dict()
 
 

@@ -340,6 +340,87 @@ ic_status check_stack(const char* pattern, int32_t n_layers, const ic_layer* lay
     return IC_OK;
 }
 
+// The decode step once its arguments are validated; ws holds decode_ws(shape) bytes.
+ic_status decode_step_run(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape& s,
+                          const int32_t* seq_len, int32_t* idx_cache, void* ws, ic_stats* stats, hipStream_t st) {
+    ic_status r = IC_OK;
+    const DecodeWs lay = decode_layout(s);
+    float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scores_off);
+    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.part_off);
+    const int nsplit = decode_splits(s);
+    ic_stats cnt = {0, 0, 0, 0};
+    bool cached = false;
+    for (int l = 0; l < n_layers; ++l) {
+        const ic_layer& L = layers[l];
+        if (pattern[l] == 'F' || pattern[l] == '1') {
+            ic_indexer_decode_args a;
+            a.q_I = L.q_I;
+            a.w = L.w;
+            a.k_I = L.k_I;
+            a.seq_len = seq_len;
+            a.scores = scores;
+            a.score_stride = lay.score_stride;
+            a.B = s.B;
+            a.Lk = s.Lk;
+            a.H_I = s.H_I;
+            a.d_I = s.d_I;
+            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+            hipError_t e = launch_indexer_decode(a, st);
+            if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
+            ic_topk_args t;
+            t.scores = scores;
+            t.row_stride = lay.score_stride;
+            t.rows = s.B;
+            t.first_len = 0;
+            t.seq_len = seq_len;
+            t.k = s.k;
+            t.idx = idx_cache;
+            t.max_len = s.Lk;
+            t.cand = lay.cand_off ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + lay.cand_off) : nullptr;
+            e = launch_topk(t, st);
+            if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
+            cached = true;
+            ++cnt.indexer_calls;
+            ++cnt.score_tiles;
+        } else if (!cached) {
+            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
+        }
+        r = run_attn(s, 1, L.q, L.kv, idx_cache, L.out, nsplit, part, st);
+        if (r != IC_OK) return r;
+        ++cnt.attn_calls;
+        ++cnt.layers;
+    }
+    g_stats = cnt;
+    if (stats) *stats = cnt;
+    return IC_OK;
+}
+
+// Scratch of ic_decode_step_static, for callers that cannot allocate a workspace: one
+// array per GPU (each device that loads the library holds its own copy until the process
+// ends).  Host code never uses the array's name as an address (on the host it names a
+// stand-in, not device memory): the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current.
+__device__ __align__(256) uint8_t scratch[IC_DECODE_STATIC_SCRATCH_BYTES];
+
+ic_status static_scratch(void** out) {
+    static std::mutex mu;
+    static void* ptrs[64] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= 64) return fail(IC_ERR_HIP, "device %d out of range for the static scratch", dev);
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptrs[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(IC_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        ptrs[dev] = p;
+    }
+    *out = ptrs[dev];
+    return IC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -732,57 +813,22 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!seq_len || !idx_cache) return fail(IC_ERR_ARG, "seq_len and idx_cache must be non-NULL");
     if ((r = check_ws(ws, ws_bytes, decode_ws(*shape))) != IC_OK) return r;
-    const ic_shape& s = *shape;
-    hipStream_t st = (hipStream_t)stream;
-    const DecodeWs lay = decode_layout(s);
-    float* scores = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.scores_off);
-    float* part = reinterpret_cast<float*>(static_cast<char*>(ws) + lay.part_off);
-    const int nsplit = decode_splits(s);
-    ic_stats cnt = {0, 0, 0, 0};
-    bool cached = false;
-    for (int l = 0; l < n_layers; ++l) {
-        const ic_layer& L = layers[l];
-        if (pattern[l] == 'F' || pattern[l] == '1') {
-            ic_indexer_decode_args a;
-            a.q_I = L.q_I;
-            a.w = L.w;
-            a.k_I = L.k_I;
-            a.seq_len = seq_len;
-            a.scores = scores;
-            a.score_stride = lay.score_stride;
-            a.B = s.B;
-            a.Lk = s.Lk;
-            a.H_I = s.H_I;
-            a.d_I = s.d_I;
-            a.fp8 = s.idx_dtype == IC_FP8_E4M3;
-            hipError_t e = launch_indexer_decode(a, st);
-            if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
-            ic_topk_args t;
-            t.scores = scores;
-            t.row_stride = lay.score_stride;
-            t.rows = s.B;
-            t.first_len = 0;
-            t.seq_len = seq_len;
-            t.k = s.k;
-            t.idx = idx_cache;
-            t.max_len = s.Lk;
-            t.cand = lay.cand_off ? reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) + lay.cand_off) : nullptr;
-            e = launch_topk(t, st);
-            if (e != hipSuccess) return hip_fail(e, "decode top-k launch");
-            cached = true;
-            ++cnt.indexer_calls;
-            ++cnt.score_tiles;
-        } else if (!cached) {
-            return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
-        }
-        r = run_attn(s, 1, L.q, L.kv, idx_cache, L.out, nsplit, part, st);
-        if (r != IC_OK) return r;
-        ++cnt.attn_calls;
-        ++cnt.layers;
-    }
-    g_stats = cnt;
-    if (stats) *stats = cnt;
-    return IC_OK;
+    return decode_step_run(pattern, n_layers, layers, *shape, seq_len, idx_cache, ws, stats, (hipStream_t)stream);
+}
+
+ic_status ic_decode_step_static(const char* pattern, int32_t n_layers, const ic_layer* layers, const ic_shape* shape,
+                                const int32_t* seq_len, int32_t* idx_cache, ic_stats* stats, void* stream) {
+    ic_status r = check_shape(shape, true, true);
+    if (r != IC_OK) return r;
+    if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
+    if (!seq_len || !idx_cache) return fail(IC_ERR_ARG, "seq_len and idx_cache must be non-NULL");
+    const size_t need = decode_ws(*shape);
+    if (need > (size_t)IC_DECODE_STATIC_SCRATCH_BYTES)
+        return fail(IC_ERR_WORKSPACE, "this decode shape needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(use ic_decode_step with a workspace)", need, (size_t)IC_DECODE_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    if ((r = static_scratch(&ws)) != IC_OK) return r;
+    return decode_step_run(pattern, n_layers, layers, *shape, seq_len, idx_cache, ws, stats, (hipStream_t)stream);
 }
 
 ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows, int32_t k, int32_t* inter,

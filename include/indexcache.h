@@ -262,6 +262,23 @@ IC_API ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_
                          const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
                          void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
 
+/* Scratch bytes ic_decode_step_static can use on each GPU (32 MiB). */
+#define IC_DECODE_STATIC_SCRATCH_BYTES (32u << 20)
+
+/* ic_decode_step for callers that cannot allocate or pass a workspace: code under HIP
+ * graph capture that may not call hipMalloc, tight serving loops, harnesses that forbid
+ * allocation.  Same arguments minus the workspace, same kernels, same results.  The
+ * scratch is a fixed array of IC_DECODE_STATIC_SCRATCH_BYTES inside the library, one per
+ * GPU, which that GPU holds from the library's first use on it until the process ends.
+ * A shape whose ic_workspace_size(shape, IC_OP_DECODE_STEP) exceeds it fails with
+ * IC_ERR_WORKSPACE before any launch (decode64k, B = 32 x 65600 keys, needs about 13 MB).
+ * Nothing is allocated.  Every call on a GPU shares that GPU's array and leaves its last
+ * contents there: calls that overlap on one GPU (on different streams, or from several
+ * threads) race on it, so the caller must order them. */
+IC_API ic_status ic_decode_step_static(const char* pattern, int32_t n_layers, const ic_layer* layers,
+                                       const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
+                                       ic_stats* stats, void* stream);
+
 /* Cross-layer overlap of two index caches, the diagnostic the agent skill page
  * (Step 1) uses to choose which layers may share indices: per row r of idx_a,
  * idx_b [rows, k] int32 (each row ascending and then -1 padded, as the top-k
