@@ -153,7 +153,7 @@ struct LinScratch {
     uint8_t scale[16][4];    // [row][scale block] E8M0
 };
 
-template <int D_I>
+template <int D_I, int HT>
 __device__ void build_lin_rows(LinScratch& ls, const uint8_t* __restrict__ qI, const float* __restrict__ w,
                                const int64_t (&qrow)[2], const bool (&valid)[2], int H_I, int lane) {
     const int c = 2 * lane;                                   // this lane's channels c, c+1
@@ -162,29 +162,24 @@ __device__ void build_lin_rows(LinScratch& ls, const uint8_t* __restrict__ qI, c
     for (int q = 0; q < 2; ++q) {
         float r0 = 0.f, r1 = 0.f;
         if (valid[q] && c < D_I) {
+            // every head's two channels in flight at once (one memory round trip), then the
+            // head-weighted sum in head order
             const uint8_t* base = qI + qrow[q] * D_I + c;
             const float* wq = w + qrow[q];
-            int j = 0;
-            for (; j + 4 <= H_I; j += 4) {
-                unsigned short v[4];
-                float wj[4];
+            unsigned short v[16 * HT];
+            float wj[16 * HT];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    v[u] = *reinterpret_cast<const unsigned short*>(base + (int64_t)(j + u) * D_I);
-                    wj[u] = wq[j + u];
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(v[u], false);
-                    r0 = fmaf(wj[u], f[0], r0);
-                    r1 = fmaf(wj[u], f[1], r1);
-                }
+            for (int j = 0; j < 16 * HT; ++j) {
+                v[j] = j < H_I ? *reinterpret_cast<const unsigned short*>(base + (int64_t)j * D_I) : (unsigned short)0;
+                wj[j] = j < H_I ? wq[j] : 0.f;
             }
-            for (; j < H_I; ++j) {
-                const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(
-                    *reinterpret_cast<const unsigned short*>(base + (int64_t)j * D_I), false);
-                r0 = fmaf(wq[j], f[0], r0);
-                r1 = fmaf(wq[j], f[1], r1);
+#pragma unroll
+            for (int j = 0; j < 16 * HT; ++j) {
+                const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(v[j], false);
+                if (j < H_I) {
+                    r0 = fmaf(wj[j], f[0], r0);
+                    r1 = fmaf(wj[j], f[1], r1);
+                }
             }
         }
 #pragma unroll
@@ -287,7 +282,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     i32x8 Alin = {0, 0, 0, 0, 0, 0, 0, 0};
     int sAlin = 0;
     if constexpr (LIN) {
-        build_lin_rows<D_I>(lin_lds[wv], qI, w, qrows, qvalid, H_I, lane);
+        build_lin_rows<D_I, HT>(lin_lds[wv], qI, w, qrows, qvalid, H_I, lane);
         __syncthreads();
         Alin = *reinterpret_cast<const i32x8*>(&lin_lds[wv].part[r][32 * g]);
         sAlin = lin_lds[wv].scale[r][g];
@@ -326,22 +321,27 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int buf = (kb - kb_begin) & 1;
         if (kb + 1 < kb_end) gload(kb + 1);
         // Software pipeline over the block's tiles: the MFMAs of tile kt are issued before
-        // the ReLU / head-sum epilogue of tile kt-1, so matrix and vector units overlap.
+        // the ReLU / head-sum epilogue of tile kt-1, so matrix and vector units overlap.  The
+        // key fragment of tile kt+1 is read from LDS one stage ahead, so no stage waits on
+        // LDS before its MFMAs (the scheduler would otherwise run the epilogue first and
+        // leave the matrix pipe idle behind it).
         float val[QW][NKT];
         f32x4 acc[2][QW][HT];
         f32x4 lin[2];
+        Frag<FP8, D_I> Bcur;
+        load_frag_lds<FP8, D_I>(Bcur, &lds[buf][r * G::LSTR], g);
 #pragma unroll
         for (int kt = 0; kt <= NKT; ++kt) {
+            Frag<FP8, D_I> Bnxt;
+            if (kt + 1 < NKT) load_frag_lds<FP8, D_I>(Bnxt, &lds[buf][((kt + 1) * 16 + r) * G::LSTR], g);
             if (kt < NKT) {
-                Frag<FP8, D_I> Bf;
-                load_frag_lds<FP8, D_I>(Bf, &lds[buf][(kt * 16 + r) * G::LSTR], g);
 #pragma unroll
                 for (int q = 0; q < QW; ++q)
 #pragma unroll
-                    for (int ht = 0; ht < HT; ++ht) acc[kt & 1][q][ht] = tile_mma<FP8, D_I>(A[q][ht], Bf);
+                    for (int ht = 0; ht < HT; ++ht) acc[kt & 1][q][ht] = tile_mma<FP8, D_I>(A[q][ht], Bcur);
                 if constexpr (LIN) {
                     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-                    lin[kt & 1] = mfma_fp8_k128_scale_a(Alin, sAlin, Bf.f8, z);
+                    lin[kt & 1] = mfma_fp8_k128_scale_a(Alin, sAlin, Bcur.f8, z);
                 }
             }
             if (kt > 0) {
@@ -354,6 +354,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                     for (int q = 0; q < QW; ++q) val[q][kt - 1] = head_partial<HT>(acc[(kt - 1) & 1][q], wr[q]);
                 }
             }
+            if constexpr (LIN && HT == 4) {
+                // Interleave within the stage: the next fragment's LDS reads first, then each
+                // MFMA followed by four of the epilogue's vector ops.
+                if (kt + 1 < NKT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                if (kt > 0 && kt < NKT) {
+#pragma unroll
+                    for (int i = 0; i < 9; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                    }
+                }
+            }
             // One pipeline stage per scheduling region.  The partials are consumed by an
             // empty asm so their VALU work stays in this stage: otherwise it sinks to the
             // stores, every tile's MFMAs issue first and the live accumulators spill.
@@ -362,6 +374,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                 for (int q = 0; q < QW; ++q) asm volatile("" : "+v"(val[q][kt - 1]));
             }
             __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < NKT) Bcur = Bnxt;
         }
         // Stage the next block first: its wait then covers only that load, not the stores.
         if (kb + 1 < kb_end) lstore(buf ^ 1);
@@ -447,14 +460,14 @@ __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8
     }
 }
 
-constexpr int PREFILL_KB = 64;                               // keys per LDS block
+constexpr int PREFILL_KB = 128;                              // keys per LDS block
 
 // Key blocks per work item: the longest query block splits into about four pieces,
-// and no piece is shorter than 16 blocks (1024 keys), which keeps the per-item set-up
-// (q_I slab, linear-term rows) small next to its key sweep.
+// and no piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
+// linear-term rows) small next to its key sweep.
 inline int prefill_seg_blocks(const ic_indexer_args& a) {
     const int nkb_max = (a.pos_begin + a.nq + PREFILL_KB - 1) / PREFILL_KB;
-    return std::max(16, (nkb_max + 3) / 4);
+    return std::max(1024 / PREFILL_KB, (nkb_max + 3) / 4);
 }
 
 // Work items (query block, key segment) that are not past the causal edge.

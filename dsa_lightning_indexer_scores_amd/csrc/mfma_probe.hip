@@ -10,6 +10,9 @@
 // that toggles draws more power, and the part clocks down to hold its power
 // limit, so the random stream sustains markedly less than the constant one.
 //
+// A third stream has the indexer's own operand pattern: fixed random q_I slabs, a fresh
+// random key tile from LDS every step and the scaled linear-term MFMA.
+//
 // This is measurement support only (built into libicprobe.so, loaded by the
 // benchmark); nothing on the indexer path uses it.
 #include "common.h"
@@ -58,6 +61,46 @@ __global__ __launch_bounds__(256) void mfma_stream_kernel(float* __restrict__ ou
         }
     }
     float s = 0.f;
+    for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
+    out[t] = s;                                      // keeps the stream live
+}
+
+// The indexer's operand pattern with none of its vector work: per 16-key tile, a B
+// fragment of fresh random e4m3 keys read from LDS (a 64-key table per wave, as the
+// indexer stages its keys), 8 score MFMAs against 8 fixed random A slabs (two queries x
+// four head tiles of q_I) and one scaled MFMA (the head-weighted linear term).  So it
+// draws the power the indexer's matrix work draws, and its rate is the ceiling the
+// indexer's MFMA stream can sustain on this GPU.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_indexer_operands_kernel(
+    float* __restrict__ out, int iters) {
+    constexpr int TABLE = 64 * 1024;                 // bytes of random keys per workgroup (16 KB per wave)
+    __shared__ __attribute__((aligned(32))) uint8_t keys[TABLE];
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    for (int i = threadIdx.x; i < TABLE / 4; i += 256)
+        reinterpret_cast<int*>(keys)[i] = random_e4m3x4(blockIdx.x * 65537u + (uint32_t)i * 3u + 11u);
+    i32x8 A[8], L;
+    for (int j = 0; j < 8; ++j)
+        for (int i = 0; i < 8; ++i) A[j][i] = random_e4m3x4(t * 131u + j * 17u + i);
+    for (int i = 0; i < 8; ++i) L[i] = random_e4m3x4(t * 313u + i + 5u);
+    const int scale = 120 + (int)(mix(t) & 7u);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint8_t* base = keys + wv * (TABLE / 4) + (lane & 15) * 160 + (lane >> 4) * 32;   // skewed rows
+    f32x4 c[8], cl = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 8; ++j) c[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // 16 keys x 128 bytes per tile; 6 tiles of distinct rows fit a wave's 16 KB.  The next
+    // tile is read while this one's MFMAs run, as the indexer's pipeline does.
+    i32x8 B = *reinterpret_cast<const i32x8*>(base);
+    for (int it = 0; it < iters; ++it) {
+        i32x8 Bn = *reinterpret_cast<const i32x8*>(base + ((it + 1) % 6) * 2560);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[j], B, c[j], 0, 0, 0, 0, 0, 0);
+        cl = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(L, B, cl, 0, 0, 0, scale, 0, 127);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("" : "+v"(Bn));                 // the next tile stays a register value read ahead
+        B = Bn;
+    }
+    float s = cl[0] + cl[1] + cl[2] + cl[3];
     for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
     out[t] = s;                                      // keeps the stream live
 }
@@ -193,11 +236,15 @@ extern "C" __attribute__((visibility("default"))) int icp_stream_read(const void
 }
 
 // Launches `blocks` workgroups of 4 waves, each wave issuing 8 * iters fp8 MFMAs of
-// 16x16x128 (65536 flop each); out needs blocks * 256 floats.  Returns a hipError_t.
+// 16x16x128 (65536 flop each), or 9 * iters with random = 2 (the indexer's operand
+// pattern: 8 score MFMAs plus the linear-term one per key tile); out needs blocks * 256
+// floats.  Returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int icp_mfma_stream(int random, int blocks, int iters, float* out,
                                                                      void* stream) {
     if (blocks < 1 || iters < 1 || out == nullptr) return (int)hipErrorInvalidValue;
-    if (random)
+    if (random == 2)
+        hipLaunchKernelGGL(mfma_indexer_operands_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
+    else if (random)
         hipLaunchKernelGGL(mfma_stream_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
     else
         hipLaunchKernelGGL(mfma_stream_kernel<false>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
