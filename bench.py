@@ -104,6 +104,7 @@ def parse():
     p.add_argument("--no-allf", action="store_true")
     p.add_argument("--no-long", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-share", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=640)
     p.add_argument("--only", choices=["indexer", "topk", "attention", "distill", "decode", "copy", "mfma"], default=None,
                    help="run just one kernel of the path a few times (for profiler counter runs)")
@@ -129,7 +130,7 @@ def only_kernel(which: str, reps: int):
             dst.copy_(src)
         info.update(bytes_read=n, bytes_written=n)
     elif which == "decode":
-        info.update(bench_decode(4, warm=1))
+        info.update(bench_decode(4, warm=1)[0])
     elif which == "mfma":
         info.update(mfma_ceiling() or {})
     else:
@@ -418,22 +419,32 @@ def cpu_baseline(cfg, layers, n_tokens: int, seed: int = 7):
                       f"{dt:.1f} s"}
 
 
-def bench_decode(n_steps: int, warm: int = 2):
-    """decode64k: the 64 steps replay one captured HIP graph of ic_decode_step.
+def bench_decode(n_steps: int, warm: int = 2, pattern: str = None, caches=None, kernels: bool = True):
+    """decode64k: the steps replay one captured HIP graph of ic_decode_step.
 
     Each step's new queries (q for every layer, q_I and w for F layers) and the
     sequence lengths live in one static input buffer; per step a single
     device-to-device copy loads that step's seeded inputs into it, then the
     graph replays.  Both the copy and the replay are inside the timed loop.
+    pattern overrides the workload's ('F' * 24 is the all-F stack on the same
+    caches, with indexer keys added for every layer); caches are reused if given.
+    Returns (result dict, caches).
     """
     import torch
     import dsa_lightning_indexer_scores_amd as ic
     from dsa_lightning_indexer_scores_amd import synth
     cfg = synth.WORKLOADS["decode64k"]
+    pattern = cfg.pattern if pattern is None else pattern
     total = warm + n_steps
-    caches = synth.decode_caches(cfg, device="cuda", steps=total)
+    steps_cap = max(total, cfg.decode_steps)
+    if caches is None:
+        caches = synth.decode_caches(cfg, device="cuda", steps=steps_cap, pattern=pattern)
+    cap_steps = caches[0]["kv"].shape[1] - cfg.L               # rows the caches hold past the context
+    for l, c in enumerate(pattern):
+        if c in "F1" and "k_I" not in caches[l]:
+            caches[l]["k_I"] = synth.decode_k_I(cfg, l, device="cuda", steps=cap_steps)
     # static input buffer layout: per layer q (+ q_I, w), then seq_len
-    first = synth.decode_queries(cfg, 0, device="cuda")
+    first = synth.decode_queries(cfg, 0, device="cuda", pattern=pattern)
     parts = []
     for lay in first:
         for name in ("q", "q_I", "w"):
@@ -452,30 +463,31 @@ def bench_decode(n_steps: int, warm: int = 2):
         return out
 
     for s_ in range(total):
-        qs = first if s_ == 0 else synth.decode_queries(cfg, s_, device="cuda")
+        qs = first if s_ == 0 else synth.decode_queries(cfg, s_, device="cuda", pattern=pattern)
         flat = [lay[name] for lay in qs for name in ("q", "q_I", "w") if name in lay]
         flat.append(torch.full((cfg.B,), cfg.L + s_ + 1, dtype=torch.int32, device="cuda"))
         for dst, src in zip(views(pregen[s_]), flat):
             dst.copy_(src)
     sv = views(static)
     layers, i = [], 0
-    for l, c in enumerate(cfg.pattern):
-        lay = dict(caches[l])
+    for l, c in enumerate(pattern):
+        lay = {"kv": caches[l]["kv"]}
         lay["q"] = sv[i]; i += 1
         if c in "F1":
+            lay["k_I"] = caches[l]["k_I"]
             lay["q_I"] = sv[i]; lay["w"] = sv[i + 1]; i += 2
         layers.append(lay)
     seq_len = sv[i]
     outs = [torch.empty_like(l["q"]) for l in layers]
     idx_cache = torch.empty((cfg.B, 1, cfg.k), dtype=torch.int32, device="cuda")
-    shape = ic._stack_shape(cfg.pattern, layers, cfg.k, 0, 0)
+    shape = ic._stack_shape(pattern, layers, cfg.k, 0, 0)
     ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_DECODE_STEP), dtype=torch.uint8, device="cuda")
     static.copy_(pregen[0])
-    ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+    ic.decode_step(pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+        ic.decode_step(pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
     for s_ in range(warm):
         static.copy_(pregen[s_])
         g.replay()
@@ -486,49 +498,93 @@ def bench_decode(n_steps: int, warm: int = 2):
         g.replay()
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    eager_t0 = time.perf_counter()
-    for s_ in range(warm, min(total, warm + 8)):
-        static.copy_(pregen[s_])
-        ic.decode_step(cfg.pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - eager_t0) * 1e3 / min(n_steps, 8)
     res = {"tokens_per_s": round(cfg.B * n_steps / dt, 1), "ms_per_step": round(dt * 1e3 / n_steps, 4),
-           "eager_ms_per_step": round(eager_ms, 4), "steps": n_steps,
-           "workload": "decode64k: B=32, 65536 cached tokens, 24 layers 'FSSS'x6, k=2048, fp8 indexer, H=16, "
-                       "d=128; one captured graph replayed per step"}
-    res["kernels"] = decode_kernel_rooflines(cfg, layers, seq_len, idx_cache, ws, int(seq_len[0].item()))
-    return res
+           "steps": n_steps,
+           "workload": f"decode64k: B=32, 65536 cached tokens, 24 layers '{pattern[:4]}'x6, k=2048, fp8 indexer, "
+                       f"H=16, d=128; one captured graph replayed per step"}
+    if kernels:
+        eager_t0 = time.perf_counter()
+        for s_ in range(warm, min(total, warm + 8)):
+            static.copy_(pregen[s_])
+            ic.decode_step(pattern, layers, seq_len, cfg.k, outs=outs, idx_cache=idx_cache, ws=ws)
+        torch.cuda.synchronize()
+        res["eager_ms_per_step"] = round((time.perf_counter() - eager_t0) * 1e3 / min(n_steps, 8), 4)
+        res["kernels"] = decode_kernel_rooflines(cfg, layers, seq_len, int(seq_len[0].item()))
+    del pregen, static, g
+    return res, caches
 
 
-def decode_kernel_rooflines(cfg, layers, seq_len, idx_cache, ws, n: int):
-    """Decode is the honest HBM test (its caches do not fit on chip).  The kernels have no
-    separate entry points, so they are timed by difference of single ABI calls on the same
-    caches (HIP events): one F layer ('F': indexer + top-k + attention), one F layer and
-    three S layers ('FSSS': + 3 attentions), and the top-k alone on scores of that shape."""
+def decode_kernel_rooflines(cfg, layers, seq_len, n: int):
+    """Decode is the honest HBM test (its caches do not fit on chip).  Each kernel of an F
+    layer and an S layer runs alone through its own entry point on the step's caches and
+    lengths (the launches ic_decode_step makes), timed with HIP events on the current stream:
+    the indexer scores, the top-k of those scores (segment ranking, then the candidates), and
+    the split-K attention with its merge."""
     import torch
     import dsa_lightning_indexer_scores_amd as ic
     B, k = cfg.B, cfg.k
-    outs = [torch.empty_like(l["q"]) for l in layers[:4]]
-    one = lambda pat, lay: ic.decode_step(pat, lay, seq_len, k, outs=outs[:len(lay)], idx_cache=idx_cache, ws=ws)
-    t_f = timed_events(lambda: one("F", layers[:1]), 10)
-    t_fsss = timed_events(lambda: one("FSSS", layers[:4]), 10)
-    sc = torch.randn((B, cfg.L + cfg.decode_steps), device="cuda") * 20 + 145
-    sl = seq_len.clone()
-    ws_t = torch.empty(max(ic.topk_rows_seq_ws(B, sc.shape[1], k), 256), dtype=torch.uint8, device="cuda")
+    f, s_lay = layers[0], layers[1]
+    cap = f["k_I"].shape[1]
+    scores = torch.empty((B, (cap + 3) // 4 * 4), dtype=torch.float32, device="cuda")
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
-    t_topk = timed_events(lambda: ic.topk_rows_seq(sc, sl, k, idx=idx, ws=ws_t), 10)
-    t_attn = (t_fsss - t_f) / 3
-    t_idx = t_f - t_attn - t_topk
+    ws_t = torch.empty(max(ic.topk_rows_seq_ws(B, cap, k), 256), dtype=torch.uint8, device="cuda")
+    run_idx = lambda: ic.decode_indexer_scores(f["q_I"], f["w"], f["k_I"], seq_len, scores=scores)
+    run_topk = lambda: ic.topk_rows_seq(scores, seq_len, k, max_len=cap, idx=idx, ws=ws_t)
+    run_idx()
+    run_topk()
+    idx3 = idx.view(B, 1, k)
+    out = torch.empty_like(s_lay["q"])
+    shape = ic.make_shape(B, 1, cap, k, cfg.H, cfg.d)
+    ws_a = torch.empty(max(ic.workspace_size(shape, ic.IC_OP_DECODE_ATTN), 256), dtype=torch.uint8, device="cuda")
+    run_attn = lambda: ic.decode_attn(s_lay["q"], s_lay["kv"], idx3, out=out, ws=ws_a)
+    run_attn()
+    t_idx = timed_events(run_idx, 20)
+    t_topk = timed_events(run_topk, 20)
+    t_attn = timed_events(run_attn, 20)
+    rows = int((idx >= 0).sum().item())
     by_idx = B * n * cfg.d_I * 1.0 + B * n * 4.0               # k_I rows read + scores written
     by_topk = B * n * 4.0 + B * k * 4.0                       # scores read + idx written
-    by_attn = B * k * 512.0 + B * (cfg.H * cfg.d * 2 * 2 + 4 * k)   # selected rows + q, out, idx
+    by_attn = rows * 512.0 + B * (cfg.H * cfg.d * 2 * 2 + 4 * k)   # selected rows + q, out, idx
     mk = lambda ms, by, what: {"bound": "hbm", "ms": round(ms, 5), "achieved": round(by / (ms * 1e-3) / 1e9, 1),
                                "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                "frac": round(by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "work": what}
     return {"indexer": mk(t_idx, by_idx, f"{by_idx:.4g} B = 128 B k_I + 4 B score per (sequence, visible key)"),
             "topk": mk(t_topk, by_topk, f"{by_topk:.4g} B = 4 B per visible score + 4k B idx per sequence"),
             "attention": mk(t_attn, by_attn, f"{by_attn:.4g} B = 512 B per selected row + q, out, idx"),
-            "method": "by difference: F-layer step minus attention (from FSSS) minus top-k alone"}
+            "method": "each kernel alone through its entry point, HIP events on the current stream"}
+
+
+def indexer_share_curve(lengths=(8192, 32768, 131072)):
+    """The indexer's share of a layer at several context lengths (the stack32k layer shapes:
+    fp8 indexer H_I=64, d_I=128, k=2048, 16 heads, d=128): one F layer through ic_run_stack
+    (indexer + top-k + attention, with the stack's overlap) against the same layer's attention
+    alone.  An all-F stack spends (F - A) / F of its time on indexer and top-k; the FSSS
+    pattern (F + 3 S) spends (F - A) / (F + 3 A)."""
+    import dataclasses
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+    base = synth.WORKLOADS["stack32k"]
+    out = []
+    for L in lengths:
+        cfg = dataclasses.replace(base, L=L, pattern="F")
+        lay = [synth.prefill_layer(cfg, 0, device="cuda")]
+        outs = [torch.empty_like(lay[0]["q"])]
+        idx = torch.empty((1, L, cfg.k), dtype=torch.int32, device="cuda")
+        shape = ic._stack_shape("F", lay, cfg.k, cfg.chunk, 0)
+        ws = torch.empty(ic.workspace_size(shape, ic.IC_OP_RUN_STACK), dtype=torch.uint8, device="cuda")
+        run_f = lambda: ic.run_stack("F", lay, cfg.k, chunk=cfg.chunk, outs=outs, idx_cache=idx, ws=ws)
+        run_a = lambda: ic.sparse_attn(lay[0]["q"], lay[0]["kv"], idx, out=outs[0])
+        run_f()
+        n = 3 if L <= 32768 else 2
+        t_f = timed_events(run_f, n)
+        t_a = timed_events(run_a, n)
+        out.append({"L": L, "f_layer_ms": round(t_f, 3), "attention_ms": round(t_a, 3),
+                    "indexer_share_all_f": round((t_f - t_a) / t_f, 4),
+                    "indexer_share_fsss": round((t_f - t_a) / (t_f + 3 * t_a), 4)})
+        del lay, outs, idx, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -660,13 +716,27 @@ def main():
     if not args.no_decode:
         log("timing decode64k")
         del outs
-        result["decode"] = bench_decode(args.decode_steps)
+        result["decode"], caches = bench_decode(args.decode_steps)
         result["decode_tokens_per_s"] = result["decode"]["tokens_per_s"]
         sgbs = result.get("hbm_stream_read_gbs")
         if sgbs:
             for v in result["decode"]["kernels"].values():
                 if isinstance(v, dict):
                     v["frac_of_stream"] = round(v["achieved"] / sgbs, 4)
+        if not args.no_allf:
+            # the same caches with indexer keys for every layer: the in-build analogue of the
+            # pages' decode speedup (standard DSA runs the indexer at every layer)
+            log("timing decode64k all-F")
+            allf, _ = bench_decode(16, pattern="F" * len(synth.WORKLOADS["decode64k"].pattern), caches=caches,
+                                   kernels=False)
+            result["decode"]["all_f_ms_per_step"] = allf["ms_per_step"]
+            result["decode"]["speedup_of_pattern"] = round(allf["ms_per_step"] / result["decode"]["ms_per_step"], 3)
+        del caches
+        torch.cuda.empty_cache()
+
+    if not args.no_share:
+        log("timing the indexer share at 8K / 32K / 128K")
+        result["indexer_share"] = indexer_share_curve()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

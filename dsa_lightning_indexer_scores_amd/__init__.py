@@ -19,6 +19,8 @@ Functions mirror the C entry points (without the ``ic_`` prefix):
                                         -> (outs, idx_cache, stats, refreshed, recall)
   decode_step(pattern, layers, seq_len, k) -> (outs, idx_cache, stats)
   decode_step_static(pattern, layers, seq_len, k) -> (outs, idx_cache, stats), no workspace
+  decode_indexer_scores(q_I, w, k_I, seq_len) -> scores [B, row_stride] fp32 (one decode F layer)
+  decode_attn(q, kv, idx)               -> out [B, 1, H, d] bf16 (one decode layer)
   index_overlap(idx_a, idx_b)           -> (inter, jaccard, recall, means)
   overlap_matrix(idx_list)              -> (J [n, n], R [n, n]) mean Jaccard / recall of every pair
   distill_kl(q_I, w, k_I, idx, qs, kvs) -> (kl [B, Lq], mean)
@@ -41,6 +43,7 @@ IC_BF16, IC_FP8_E4M3 = 0, 1
 IC_OP_INDEXER_TOPK, IC_OP_SPARSE_ATTN, IC_OP_RUN_STACK, IC_OP_DECODE_STEP, IC_OP_INDEXER_SCORES = 0, 1, 2, 3, 4
 IC_OP_RUN_STACK_VARLEN = 5
 IC_OP_DISTILL_KL = 6
+IC_OP_DECODE_ATTN = 7
 
 
 class Shape(ctypes.Structure):
@@ -103,12 +106,15 @@ def lib() -> ctypes.CDLL:
     L.ic_run_stack.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, sz, P(Stats), vp]
     L.ic_decode_step.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, vp, sz, P(Stats), vp]
     L.ic_decode_step_static.argtypes = [ctypes.c_char_p, i32, P(Layer), P(Shape), vp, vp, P(Stats), vp]
+    L.ic_decode_indexer_scores.argtypes = [P(Shape), vp, vp, vp, vp, vp, i64, vp]
+    L.ic_decode_attn.argtypes = [P(Shape), vp, vp, vp, vp, vp, sz, vp]
     L.ic_get_stats.argtypes = [P(Stats)]
     L.ic_last_error.restype = ctypes.c_char_p
     L.ic_version.restype = i32
     for fn in ("ic_indexer_topk", "ic_indexer_scores", "ic_topk_rows", "ic_topk_rows_seq", "ic_index_overlap",
                "ic_sparse_attn", "ic_run_stack", "ic_run_stack_varlen", "ic_distill_kl", "ic_run_stack_dynamic",
-               "ic_decode_step", "ic_decode_step_static", "ic_get_stats"):
+               "ic_decode_step", "ic_decode_step_static", "ic_decode_indexer_scores", "ic_decode_attn",
+               "ic_get_stats"):
         getattr(L, fn).restype = ctypes.c_int
     _lib = L
     return L
@@ -574,6 +580,40 @@ def decode_step_static(pattern: str, layers: Sequence[Dict[str, torch.Tensor]], 
     _check(lib().ic_decode_step_static(pattern.encode(), len(layers), arr, ctypes.byref(s), _ptr(seq_len),
                                        _ptr(idx_cache), ctypes.byref(st), _stream(stream)))
     return outs, idx_cache, st.as_dict()
+
+
+def decode_indexer_scores(q_I, w, k_I, seq_len, row_stride: Optional[int] = None, scores=None, stream=None):
+    """Indexer scores of one decode step's F layer: q_I [B,1,H_I,d_I], w [B,1,H_I] against
+    keys 0..seq_len[b]-1 of k_I [B,Lk,d_I] -> scores [B, row_stride] fp32 (row b valid for
+    its first seq_len[b] entries)."""
+    s = _indexer_shape(q_I, w, k_I, 1, 0, 0)
+    if s.Lq != 1:
+        raise ValueError(f"decode takes one query per sequence; q_I has {s.Lq}")
+    _need(seq_len, "seq_len", (torch.int32,), 1)
+    if seq_len.shape[0] != s.B:
+        raise ValueError(f"seq_len has {seq_len.shape[0]} entries for B = {s.B}")
+    row_stride = (s.Lk + 3) // 4 * 4 if row_stride is None else row_stride
+    if scores is None:
+        scores = torch.full((s.B, row_stride), float("nan"), dtype=torch.float32, device=q_I.device)
+    _check_like(scores, "scores", torch.float32, (s.B, row_stride))
+    _check(lib().ic_decode_indexer_scores(ctypes.byref(s), _ptr(q_I), _ptr(w), _ptr(k_I), _ptr(seq_len), _ptr(scores),
+                                          row_stride, _stream(stream)))
+    return scores
+
+
+def decode_attn(q, kv, idx, out=None, ws=None, stream=None):
+    """Sparse attention of one decode layer: q [B,1,H,d], kv [B,Lk,2,d], idx [B,1,k] -> out [B,1,H,d]."""
+    _need(idx, "idx", (torch.int32,), 3)
+    s = _attn_shape(q, kv, idx.shape[2])
+    if s.Lq != 1 or tuple(idx.shape[:2]) != (s.B, 1):
+        raise ValueError("decode attention takes q [B,1,H,d] and idx [B,1,k]")
+    if out is None:
+        out = torch.empty_like(q)
+    _check_like(out, "out", torch.bfloat16, q.shape)
+    ws = _workspace(workspace_size(s, IC_OP_DECODE_ATTN), q.device, ws)
+    _check(lib().ic_decode_attn(ctypes.byref(s), _ptr(q), _ptr(kv), _ptr(idx), _ptr(out), _ptr(ws),
+                                0 if ws is None else ws.numel(), _stream(stream)))
+    return out
 
 
 def get_stats() -> Dict[str, int]:

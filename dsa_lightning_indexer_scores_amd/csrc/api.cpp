@@ -446,6 +446,9 @@ size_t ic_workspace_size(const ic_shape* shape, int op) {
         case IC_OP_DISTILL_KL:
             if (check_shape(shape, true, false) != IC_OK) return 0;
             return indexer_ws(*shape);
+        case IC_OP_DECODE_ATTN:
+            if (check_shape(shape, false, true) != IC_OK) return 0;
+            return sparse_attn_ws_bytes(shape->B, shape->H, shape->d, decode_splits(*shape));
         default:
             fail(IC_ERR_ARG, "unknown op %d", op);
             return 0;
@@ -829,6 +832,42 @@ ic_status ic_decode_step_static(const char* pattern, int32_t n_layers, const ic_
     void* ws = nullptr;
     if ((r = static_scratch(&ws)) != IC_OK) return r;
     return decode_step_run(pattern, n_layers, layers, *shape, seq_len, idx_cache, ws, stats, (hipStream_t)stream);
+}
+
+ic_status ic_decode_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+                                   const int32_t* seq_len, float* scores, int64_t row_stride, void* stream) {
+    ic_status r = check_shape(shape, true, true);
+    if (r != IC_OK) return r;
+    if (!q_I || !w || !k_I || !seq_len || !scores)
+        return fail(IC_ERR_ARG, "q_I, w, k_I, seq_len and scores must be non-NULL");
+    const ic_shape& s = *shape;
+    if (row_stride < s.Lk) return fail(IC_ERR_SHAPE, "row_stride %lld < Lk %d", (long long)row_stride, s.Lk);
+    ic_indexer_decode_args a;
+    a.q_I = q_I;
+    a.w = w;
+    a.k_I = k_I;
+    a.seq_len = seq_len;
+    a.scores = scores;
+    a.score_stride = row_stride;
+    a.B = s.B;
+    a.Lk = s.Lk;
+    a.H_I = s.H_I;
+    a.d_I = s.d_I;
+    a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+    hipError_t e = launch_indexer_decode(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "decode indexer launch");
+    return IC_OK;
+}
+
+ic_status ic_decode_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+    ic_status r = check_shape(shape, false, true);
+    if (r != IC_OK) return r;
+    if (!q || !kv || !idx || !out) return fail(IC_ERR_ARG, "q, kv, idx and out must be non-NULL");
+    const ic_shape& s = *shape;
+    const int nsplit = decode_splits(s);
+    if ((r = check_ws(ws, ws_bytes, sparse_attn_ws_bytes(s.B, s.H, s.d, nsplit))) != IC_OK) return r;
+    return run_attn(s, 1, q, kv, idx, out, nsplit, static_cast<float*>(ws), (hipStream_t)stream);
 }
 
 ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t rows, int32_t k, int32_t* inter,

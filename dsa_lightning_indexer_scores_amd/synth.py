@@ -144,7 +144,7 @@ def prefill_stack(cfg: Workload, device="cpu", L: Optional[int] = None, B: Optio
 
 
 def decode_caches(cfg: Workload, device="cuda", N: Optional[int] = None, B: Optional[int] = None,
-                  steps: Optional[int] = None) -> List[Dict[str, torch.Tensor]]:
+                  steps: Optional[int] = None, pattern: Optional[str] = None) -> List[Dict[str, torch.Tensor]]:
     """Per-layer caches with capacity N + steps rows: k_I [B,cap,d_I] (F layers) and kv [B,cap,2,d].
 
     Rows N..N+steps-1 hold the tokens that the decode steps append (the
@@ -153,25 +153,37 @@ def decode_caches(cfg: Workload, device="cuda", N: Optional[int] = None, B: Opti
     N = cfg.L if N is None else N
     B = cfg.B if B is None else B
     steps = cfg.decode_steps if steps is None else steps
+    pattern = cfg.pattern if pattern is None else pattern
     cap = N + steps
     layers = []
-    for i, c in enumerate(cfg.pattern):
+    for i, c in enumerate(pattern):
         lay = {}
         if c in "F1":
-            lay["k_I"] = encode(_values((B, cap, cfg.d_I), cfg.dist, cfg.d_I,
-                                        seed_for(cfg, i, T_KI), device), cfg.idx_dtype)
+            lay["k_I"] = decode_k_I(cfg, i, device, N, B, steps)
         lay["kv"] = encode(_values((B, cap, 2, cfg.d), cfg.dist, cfg.d,
                                    seed_for(cfg, i, T_KV), device), "bf16")
         layers.append(lay)
     return layers
 
 
-def decode_queries(cfg: Workload, step: int, device="cuda", B: Optional[int] = None
-                   ) -> List[Dict[str, torch.Tensor]]:
+def decode_k_I(cfg: Workload, layer: int, device="cuda", N: Optional[int] = None, B: Optional[int] = None,
+               steps: Optional[int] = None) -> torch.Tensor:
+    """The indexer key cache k_I [B, N + steps, d_I] of one layer (its seeds do not depend on
+    whether the pattern makes the layer F, so a layer's keys are the same in every pattern)."""
+    N = cfg.L if N is None else N
+    B = cfg.B if B is None else B
+    steps = cfg.decode_steps if steps is None else steps
+    return encode(_values((B, N + steps, cfg.d_I), cfg.dist, cfg.d_I, seed_for(cfg, layer, T_KI), device),
+                  cfg.idx_dtype)
+
+
+def decode_queries(cfg: Workload, step: int, device="cuda", B: Optional[int] = None,
+                   pattern: Optional[str] = None) -> List[Dict[str, torch.Tensor]]:
     """The new token's queries at one decode step: q_I [B,1,H_I,d_I], w [B,1,H_I] (F layers), q [B,1,H,d]."""
     B = cfg.B if B is None else B
+    pattern = cfg.pattern if pattern is None else pattern
     layers = []
-    for i, c in enumerate(cfg.pattern):
+    for i, c in enumerate(pattern):
         lay = {}
         if c in "F1":
             lay["q_I"] = encode(_values((B, 1, cfg.H_I, cfg.d_I), cfg.dist, cfg.d_I,

@@ -138,7 +138,8 @@ enum {
     IC_OP_DECODE_STEP = 3,
     IC_OP_INDEXER_SCORES = 4,
     IC_OP_RUN_STACK_VARLEN = 5,
-    IC_OP_DISTILL_KL = 6
+    IC_OP_DISTILL_KL = 6,
+    IC_OP_DECODE_ATTN = 7
 };
 
 /* Bytes of workspace the operation needs for this shape (0 if none).
@@ -261,6 +262,25 @@ IC_API size_t ic_run_stack_dynamic_ws(const ic_shape* shape, int32_t probe_strid
 IC_API ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* layers,
                          const ic_shape* shape, const int32_t* seq_len, int32_t* idx_cache,
                          void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
+
+/* The decode step's kernels one at a time (the same launches ic_decode_step makes), so a
+ * caller can time or compose them.  Shapes as ic_decode_step (Lq = 1, Lk = cache capacity).
+ *
+ * Lightning-indexer scores of one F layer's new queries (arXiv abstract: the indexer
+ * scores every preceding token): sequence b's query q_I [B, 1, H_I, d_I], w [B, 1, H_I]
+ * against keys 0..seq_len[b]-1 of k_I [B, Lk, d_I]; scores [B, row_stride] fp32 (row_stride
+ * >= Lk), row b written for its first seq_len[b] entries (seq_len device int32 [B], values
+ * clamped to 1..Lk).  The top-k of these rows is ic_topk_rows_seq.  No workspace. */
+IC_API ic_status ic_decode_indexer_scores(const ic_shape* shape, const void* q_I, const float* w, const void* k_I,
+                                          const int32_t* seq_len, float* scores, int64_t row_stride, void* stream);
+
+/* Sparse attention of one decode layer (arXiv abstract: core attention over the k selected
+ * tokens): q [B, 1, H, d], kv [B, Lk, 2, d], idx [B, 1, k] -> out [B, 1, H, d] bf16, with
+ * the same entry rules as ic_sparse_attn.  Each query's rows are split over several waves
+ * and merged in a fixed order (deterministic); the partials need
+ * ic_workspace_size(shape, IC_OP_DECODE_ATTN) bytes of ws. */
+IC_API ic_status ic_decode_attn(const ic_shape* shape, const void* q, const void* kv, const int32_t* idx, void* out,
+                                void* ws, size_t ws_bytes, void* stream);
 
 /* Scratch bytes ic_decode_step_static can use on each GPU (32 MiB). */
 #define IC_DECODE_STATIC_SCRATCH_BYTES (32u << 20)
