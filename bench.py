@@ -105,6 +105,7 @@ def parse():
     p.add_argument("--no-long", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-share", action="store_true")
+    p.add_argument("--no-varlen", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=640)
     p.add_argument("--only", choices=["indexer", "topk", "attention", "distill", "decode", "copy", "mfma"], default=None,
                    help="run just one kernel of the path a few times (for profiler counter runs)")
@@ -303,6 +304,67 @@ def bench_long():
     del layers, outs, idx, ws
     torch.cuda.empty_cache()
     return out
+
+
+def bench_varlen(n_seq: int = 64, q_new: int = 512, Lk: int = 8192, seed: int = 77):
+    """Ragged batched prefill, the serving case: n_seq sequences each bring q_new queries that
+    continue a cached prefix of 0 .. Lk - q_new tokens, through the 16-layer FSSS stack with the
+    stack32k layer shapes.  One ic_run_stack_varlen call (consecutive sequences share
+    launches) against one ic_run_stack per sequence on the same tensors."""
+    import numpy as np
+    import torch
+    import dsa_lightning_indexer_scores_amd as ic
+    from dsa_lightning_indexer_scores_amd import synth
+    cfg = synth.WORKLOADS["stack32k"]
+    rng = np.random.default_rng(seed)
+    q_len = [q_new] * n_seq
+    pos0 = [int(x) for x in rng.integers(0, Lk - q_new + 1, size=n_seq)]
+    T = n_seq * q_new
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    layers = []
+    for c in cfg.pattern:
+        lay = {"q": torch.randn((T, cfg.H, cfg.d), generator=g, device="cuda").to(torch.bfloat16),
+               "kv": torch.randn((n_seq, Lk, 2, cfg.d), generator=g, device="cuda").to(torch.bfloat16)}
+        if c in "F1":
+            lay["q_I"] = synth.encode(torch.randn((T, cfg.H_I, cfg.d_I), generator=g, device="cuda"), "fp8")
+            lay["w"] = torch.rand((T, cfg.H_I), generator=g, device="cuda")
+            lay["k_I"] = synth.encode(torch.randn((n_seq, Lk, cfg.d_I), generator=g, device="cuda"), "fp8")
+        layers.append(lay)
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
+    grouped = lambda: ic.run_stack_varlen(cfg.pattern, layers, cfg.k, q_len, pos0, outs=outs, idx_cache=idx)
+    per_seq_layers = []
+    for b in range(n_seq):
+        q0 = b * q_new
+        one = []
+        for lay in layers:
+            o = {"q": lay["q"][q0:q0 + q_new].unsqueeze(0), "kv": lay["kv"][b:b + 1]}
+            if "q_I" in lay:
+                o.update(q_I=lay["q_I"][q0:q0 + q_new].unsqueeze(0), w=lay["w"][q0:q0 + q_new].unsqueeze(0),
+                         k_I=lay["k_I"][b:b + 1])
+            one.append(o)
+        per_seq_layers.append(one)
+    shape1 = ic._stack_shape(cfg.pattern, per_seq_layers[0], cfg.k, 0, 0)
+    ws1 = torch.empty(ic.workspace_size(ic.make_shape(1, q_new, Lk, cfg.k, cfg.H, cfg.d, cfg.H_I, cfg.d_I,
+                                                      ic.IC_FP8_E4M3, pos0=Lk - q_new), ic.IC_OP_RUN_STACK),
+                      dtype=torch.uint8, device="cuda")
+    del shape1
+    outs1 = [[o[b * q_new:(b + 1) * q_new].unsqueeze(0) for o in outs] for b in range(n_seq)]
+
+    def per_sequence():
+        for b in range(n_seq):
+            ic.run_stack(cfg.pattern, per_seq_layers[b], cfg.k, pos0=pos0[b], outs=outs1[b],
+                         idx_cache=idx[b * q_new:(b + 1) * q_new].unsqueeze(0), ws=ws1)
+    grouped()
+    per_sequence()
+    t_g = timed_events(grouped, 3)
+    t_p = timed_events(per_sequence, 3)
+    del layers, outs, idx, per_seq_layers, outs1, ws1
+    torch.cuda.empty_cache()
+    return {"workload": f"ragged prefill: {n_seq} sequences x {q_new} new tokens continuing prefixes of 0..{Lk - q_new}, "
+                        f"16 layers 'FSSS'x4, stack32k layer shapes",
+            "grouped_ms": round(t_g, 3), "tokens_per_s": round(T / (t_g * 1e-3), 1),
+            "per_sequence_ms": round(t_p, 3), "speedup_of_grouping": round(t_p / t_g, 3)}
 
 
 def gather_ceiling_ms(kv, idx3):
@@ -739,6 +801,10 @@ def main():
             result["decode"]["speedup_of_pattern"] = round(allf["ms_per_step"] / result["decode"]["ms_per_step"], 3)
         del caches
         torch.cuda.empty_cache()
+
+    if not args.no_varlen:
+        log("timing ragged prefill (64 sequences)")
+        result["varlen"] = bench_varlen()
 
     if not args.no_share:
         log("timing the indexer share at 8K / 32K / 128K")

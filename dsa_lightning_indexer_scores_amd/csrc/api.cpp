@@ -18,6 +18,7 @@
 #include <cstring>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/indexcache.h"
 #include "common.h"
@@ -759,42 +760,122 @@ ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, const ic_la
     if ((r = check_ws(ws, ws_bytes, indexer_ws_varlen(s))) != IC_OK) return r;
     hipStream_t st = (hipStream_t)stream;
     const size_t eb = elem_bytes(s.idx_dtype);
+    const int chunk = chunk_of(s);
+    // Plan: consecutive sequences of at most `chunk` queries in all (and at most IC_GROUP_MAX
+    // of them) share one launch per kernel, their score rows packed into one tile; a sequence
+    // longer than a chunk runs alone in chunks.  Empty sequences are skipped.
+    struct Piece {
+        bool grouped;
+        ic_seq_group g;       // grouped: the sequences, rows relative to q0
+        int64_t q0;           // first packed query row
+        int rows;             // packed rows of the piece
+        int b;                // single: the sequence
+        int max_keys;         // keys visible to the piece's longest row
+    };
+    std::vector<Piece> plan;
+    try {
+        plan.reserve((size_t)s.B);
+    } catch (...) {
+        return fail(IC_ERR_ARG, "cannot plan %d sequences", s.B);
+    }
+    {
+        Piece cur{};
+        cur.grouped = true;
+        auto flush = [&]() {
+            if (cur.g.n > 0) plan.push_back(cur);
+            cur = Piece{};
+            cur.grouped = true;
+        };
+        int64_t q0 = 0;
+        for (int b = 0; b < s.B; ++b) {
+            const int n = q_len[b];
+            if (n > chunk) {
+                flush();
+                Piece one{};
+                one.grouped = false;
+                one.q0 = q0;
+                one.rows = n;
+                one.b = b;
+                one.max_keys = pos0[b] + n;
+                plan.push_back(one);
+            } else if (n > 0) {
+                if (cur.g.n == IC_GROUP_MAX || cur.rows + n > chunk) flush();
+                if (cur.g.n == 0) cur.q0 = q0;
+                const int i = cur.g.n++;
+                cur.g.row0[i] = cur.rows;
+                cur.g.pos0[i] = pos0[b];
+                cur.g.seq[i] = b;
+                cur.rows += n;
+                cur.g.row0[i + 1] = cur.rows;
+                cur.max_keys = std::max(cur.max_keys, pos0[b] + n);
+            }
+            q0 += n;
+        }
+        flush();
+    }
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;                       // the index cache starts empty on every call
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const bool full = pattern[l] == 'F' || pattern[l] == '1';
         if (!full && !cached) return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
-        int64_t q0 = 0;                        // first packed row of sequence b
-        for (int b = 0; b < s.B; ++b) {
-            const int n = q_len[b];
-            if (n > 0) {
-                int32_t* idxb = idx_cache + q0 * s.k;
-                if (full) {
-                    r = run_indexer_topk_one(
-                        s, n, pos0[b], static_cast<const uint8_t*>(L.q_I) + q0 * s.H_I * s.d_I * eb, L.w + q0 * s.H_I,
-                        static_cast<const uint8_t*>(L.k_I) + (size_t)b * s.Lk * s.d_I * eb, idxb, ws, st,
-                        &cnt.score_tiles);
-                    if (r != IC_OK) return r;
-                }
-                ic_attn_args a;
-                a.q = static_cast<const uint16_t*>(L.q) + q0 * s.H * s.d;
-                a.kv = static_cast<const uint16_t*>(L.kv) + (size_t)b * s.Lk * 2 * s.d;
-                a.idx = idxb;
-                a.out = static_cast<uint16_t*>(L.out) + q0 * s.H * s.d;
-                a.kv_seq_stride = (int64_t)s.Lk * 2 * s.d;
-                a.Lk = s.Lk;
-                a.nq = n;
-                a.q_per_seq = n;
-                a.H = s.H;
-                a.d = s.d;
-                a.k = s.k;
-                a.nsplit = 1;
-                a.ws = nullptr;
-                hipError_t e = launch_sparse_attn(a, st);
-                if (e != hipSuccess) return hip_fail(e, "sparse attention launch");
+        for (const Piece& pc : plan) {
+            int32_t* idxp = idx_cache + pc.q0 * s.k;
+            hipError_t e;
+            if (full && pc.grouped) {
+                const int64_t stride = round_up(pc.max_keys, 4);
+                ic_indexer_args a;
+                a.q_I = L.q_I;
+                a.w = L.w;
+                a.k_I = L.k_I;
+                a.scores = static_cast<float*>(ws);
+                a.row_stride = stride;
+                a.q_begin = (int32_t)pc.q0;
+                a.nq = pc.rows;
+                a.pos_begin = 0;
+                a.H_I = s.H_I;
+                a.d_I = s.d_I;
+                a.fp8 = s.idx_dtype == IC_FP8_E4M3;
+                a.grp = &pc.g;
+                a.k_seq_bytes = (int64_t)s.Lk * s.d_I * eb;
+                if ((e = launch_indexer_prefill(a, st)) != hipSuccess) return hip_fail(e, "indexer launch");
+                ic_topk_args t{};
+                t.scores = static_cast<float*>(ws);
+                t.row_stride = stride;
+                t.rows = pc.rows;
+                t.first_len = 1;
+                t.seq_len = nullptr;
+                t.k = s.k;
+                t.idx = idxp;
+                t.max_len = pc.max_keys;
+                t.cand = nullptr;
+                t.grp = &pc.g;
+                if ((e = launch_topk(t, st)) != hipSuccess) return hip_fail(e, "top-k launch");
+                ++cnt.score_tiles;
+            } else if (full) {
+                r = run_indexer_topk_one(s, pc.rows, pos0[pc.b],
+                                         static_cast<const uint8_t*>(L.q_I) + pc.q0 * s.H_I * s.d_I * eb,
+                                         L.w + pc.q0 * s.H_I,
+                                         static_cast<const uint8_t*>(L.k_I) + (size_t)pc.b * s.Lk * s.d_I * eb, idxp,
+                                         ws, st, &cnt.score_tiles);
+                if (r != IC_OK) return r;
             }
-            q0 += n;
+            ic_attn_args a;
+            a.q = static_cast<const uint16_t*>(L.q) + pc.q0 * s.H * s.d;
+            a.kv = static_cast<const uint16_t*>(L.kv) + (pc.grouped ? 0 : (size_t)pc.b * s.Lk * 2 * s.d);
+            a.idx = idxp;
+            a.out = static_cast<uint16_t*>(L.out) + pc.q0 * s.H * s.d;
+            a.kv_seq_stride = (int64_t)s.Lk * 2 * s.d;
+            a.Lk = s.Lk;
+            a.nq = pc.rows;
+            a.q_per_seq = pc.rows;
+            a.H = s.H;
+            a.d = s.d;
+            a.k = s.k;
+            a.nsplit = 1;
+            a.ws = nullptr;
+            a.grp = pc.grouped ? &pc.g : nullptr;
+            if ((e = launch_sparse_attn(a, st)) != hipSuccess) return hip_fail(e, "sparse attention launch");
         }
         if (full) {
             cached = true;

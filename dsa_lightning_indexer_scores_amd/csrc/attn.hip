@@ -346,7 +346,7 @@ template <int D>
 __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))) void sparse_attn_dma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kv, const int32_t* __restrict__ idx,
     uint16_t* __restrict__ out, int64_t kv_seq_stride, int Lk, int nq, int q_per_seq, int H, int k,
-    float scale_log2) {
+    float scale_log2, const ic_seq_group grp) {
     using G = DmaGeom<D>;
     constexpr int CI = G::ICH / 64;                      // DMA instructions per idx chunk
     __shared__ __attribute__((aligned(1024))) uint8_t stage_all[DMA_NW][2][G::SB];   // K, V
@@ -363,7 +363,8 @@ __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     const uint8_t* vst = stage_all[wv][1];
     const int32_t* ring = ring_all[wv];
     const uint32_t k_lds = lds_addr(kst), v_lds = lds_addr(vst), ring_lds = lds_addr(ring);
-    const int seq = (int)(qi / q_per_seq);
+    // the query's sequence: a group entry's cache slot in a grouped launch, else qi / q_per_seq
+    const int seq = grp.n > 0 ? grp.seq[group_find(grp.row0, grp.n, (int)qi)] : (int)(qi / q_per_seq);
     const uint8_t* kvb = reinterpret_cast<const uint8_t*>(kv + (int64_t)seq * kv_seq_stride);
     const int32_t* irow = idx + qi * k;
     const int head = 16 * hg + n;
@@ -599,9 +600,11 @@ hipError_t attn_launch(const ic_attn_args& a, hipStream_t st) {
     if (a.nsplit == 1) {                                // prefill: one wave per (query, head group)
         if ((int64_t)a.Lk * DmaGeom<D>::RB > (int64_t)UINT32_MAX) return hipErrorInvalidValue;   // 32-bit row offsets
         const int64_t dblocks = (items + DMA_NW - 1) / DMA_NW;
+        ic_seq_group grp{};
+        if (a.grp) grp = *a.grp;
         hipLaunchKernelGGL((sparse_attn_dma_kernel<D>), dim3((unsigned)dblocks), dim3(DMA_NW * 64), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.kv, a.idx, (uint16_t*)a.out,
-                           a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2);
+                           a.kv_seq_stride, a.Lk, a.nq, a.q_per_seq, a.H, a.k, scale_log2, grp);
         return hipGetLastError();
     }
     hipLaunchKernelGGL((sparse_attn_split_kernel<D>), dim3((unsigned)blocks), dim3(ATT_NW * 64), 0, st,

@@ -125,6 +125,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }  // namespace ic
 
 // ---- host-side launchers implemented in the .hip files ----
+
+// A group of consecutive sequences of a ragged batch served by one launch.  Sequence i of
+// the group owns the launch's packed query rows [row0[i], row0[i+1]); its row r sits at
+// position pos0[i] + r - row0[i] and sees that sequence's own keys, cache slot seq[i] of the
+// k_I / kv arrays.  For the indexer, its query blocks are [blk0[i], blk0[i+1]).  Passed to the
+// kernels by value (about 1 KB of kernel arguments), so a launch needs no table in memory.
+constexpr int IC_GROUP_MAX = 64;
+struct ic_seq_group {
+    int32_t n;                          // sequences in the group; 0: the launch is not grouped
+    int32_t row0[IC_GROUP_MAX + 1];
+    int32_t pos0[IC_GROUP_MAX];
+    int32_t seq[IC_GROUP_MAX];
+    int32_t blk0[IC_GROUP_MAX + 1];
+};
+
+namespace ic {
+// The group entry i with start[i] <= x < start[i + 1] (start ascending, start[0] <= x).
+__device__ __forceinline__ int group_find(const int32_t* start, int n, int x) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (start[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+}  // namespace ic
+
 struct ic_indexer_args {
     const void* q_I;      // [Lq_total, H_I, d_I] of this sequence, row 0 = first query of the call
     const float* w;       // [Lq_total, H_I]
@@ -137,6 +164,11 @@ struct ic_indexer_args {
     int32_t H_I, d_I;
     int32_t fp8;
     const int32_t* run_if = nullptr;   // optional device flag: the launch does nothing while it is 0
+    // Grouped launch (several sequences): q_I / w rows, score rows and row counts follow the
+    // group's packed rows (q_begin, nq and pos_begin are then unused); sequence i's keys start
+    // at k_I + grp->seq[i] * k_seq_bytes.
+    const ic_seq_group* grp = nullptr;
+    int64_t k_seq_bytes = 0;
 };
 hipError_t launch_indexer_prefill(const ic_indexer_args& a, hipStream_t st);
 
@@ -166,6 +198,7 @@ struct ic_topk_args {
     int32_t* cand;        // optional workspace of topk_ws_bytes(): few long rows run segmented
     int32_t len_step = 1; // without seq_len, row r has first_len + r * len_step visible entries
     const int32_t* run_if = nullptr;   // optional device flag: the launch does nothing while it is 0
+    const ic_seq_group* grp = nullptr; // grouped rows: row r of sequence i has pos0[i] + r - row0[i] + 1 entries
 };
 // Few long rows (decode) are ranked in TOPK_SEG-key segments first, then over the
 // segments' candidates; that needs topk_ws_bytes() of workspace (0 otherwise).
@@ -188,6 +221,7 @@ struct ic_attn_args {
     // combine kernel merges them
     int32_t nsplit;
     float* ws;
+    const ic_seq_group* grp = nullptr; // grouped queries: query r belongs to cache slot seq[i] (prefill only)
 };
 hipError_t launch_sparse_attn(const ic_attn_args& a, hipStream_t st);
 

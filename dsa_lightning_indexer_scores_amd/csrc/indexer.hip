@@ -225,9 +225,9 @@ __device__ __forceinline__ void load_w(float (&wr)[HT][4], const float* wrow, in
 // compiler from parking MFMA accumulators in AGPRs (each VALU read would then cost a copy).
 template <bool FP8, int D_I, int HT, int QW, int NW, int KB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_prefill_kernel(
-    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    float* __restrict__ scores, int64_t row_stride, int q_begin, int nq, int pos_begin, int H_I, int seg_blocks,
-    const int32_t* __restrict__ run_if) {
+    const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI_,
+    float* __restrict__ scores_, int64_t row_stride, int q_begin_, int nq_, int pos_begin_, int H_I, int seg_blocks,
+    const int32_t* __restrict__ run_if, const ic_seq_group grp, int64_t k_seq_bytes) {
     if (run_if != nullptr && *run_if == 0) return;            // a refresh that was not needed
     using G = IdxGeom<FP8, D_I>;
     static_assert(KB % 64 == 0, "a key block is stored 64 keys per instruction");
@@ -244,8 +244,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int tid = threadIdx.x;
     const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, g = lane >> 4;
-    const int nblk = (nq + QB - 1) / QB;
-    const int blk = nblk - 1 - (int)blockIdx.x;               // late (long) query blocks first
+    // Late (long) query blocks first.  In a grouped launch the block belongs to one sequence
+    // of the group: its rows, positions and keys are that sequence's.
+    int blk, nq = nq_, pos_begin = pos_begin_, q_begin = q_begin_;
+    const uint8_t* kI = kI_;
+    float* scores = scores_;
+    if (grp.n > 0) {
+        const int gb = grp.blk0[grp.n] - 1 - (int)blockIdx.x;
+        const int i = group_find(grp.blk0, grp.n, gb);
+        blk = gb - grp.blk0[i];
+        nq = grp.row0[i + 1] - grp.row0[i];
+        pos_begin = grp.pos0[i];
+        q_begin = q_begin_ + grp.row0[i];
+        kI = kI_ + (int64_t)grp.seq[i] * k_seq_bytes;
+        scores = scores_ + (int64_t)grp.row0[i] * row_stride;
+    } else {
+        blk = (nq + QB - 1) / QB - 1 - (int)blockIdx.x;
+    }
     const int t0 = blk * QB;
     const int t_last = min(t0 + QB, nq) - 1;
     const int nkeys = pos_begin + t_last + 1;                 // keys visible to the block
@@ -465,32 +480,53 @@ constexpr int PREFILL_KB = 128;                              // keys per LDS blo
 // Key blocks per work item: the longest query block splits into about four pieces,
 // and no piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
 // linear-term rows) small next to its key sweep.
+inline int prefill_max_keys(const ic_indexer_args& a);
 inline int prefill_seg_blocks(const ic_indexer_args& a) {
-    const int nkb_max = (a.pos_begin + a.nq + PREFILL_KB - 1) / PREFILL_KB;
+    const int nkb_max = (prefill_max_keys(a) + PREFILL_KB - 1) / PREFILL_KB;
     return std::max(1024 / PREFILL_KB, (nkb_max + 3) / 4);
 }
 
 // Work items (query block, key segment) that are not past the causal edge.
 inline int64_t prefill_items(const ic_indexer_args& a, int QB, int seg_blocks) {
     int64_t items = 0;
-    for (int t0 = 0; t0 < a.nq; t0 += QB) {
-        const int nkeys = a.pos_begin + std::min(t0 + QB, a.nq);
-        const int nkb = (nkeys + PREFILL_KB - 1) / PREFILL_KB;
-        items += (nkb + seg_blocks - 1) / seg_blocks;
+    const int nseq = a.grp ? a.grp->n : 1;
+    for (int i = 0; i < nseq; ++i) {
+        const int nq = a.grp ? a.grp->row0[i + 1] - a.grp->row0[i] : a.nq;
+        const int pos = a.grp ? a.grp->pos0[i] : a.pos_begin;
+        for (int t0 = 0; t0 < nq; t0 += QB) {
+            const int nkeys = pos + std::min(t0 + QB, nq);
+            const int nkb = (nkeys + PREFILL_KB - 1) / PREFILL_KB;
+            items += (nkb + seg_blocks - 1) / seg_blocks;
+        }
     }
     return items;
+}
+
+// Keys visible to the launch's longest row.
+inline int prefill_max_keys(const ic_indexer_args& a) {
+    if (!a.grp) return a.pos_begin + a.nq;
+    int m = 1;
+    for (int i = 0; i < a.grp->n; ++i) m = std::max(m, a.grp->pos0[i] + a.grp->row0[i + 1] - a.grp->row0[i]);
+    return m;
 }
 
 template <bool FP8, int D_I, int HT, int NW>
 hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t st) {
     constexpr int QW = FP8 ? 2 : 1;
     constexpr int QB = QW * NW;
-    const int nblk = (a.nq + QB - 1) / QB;
-    const int nkb_max = (a.pos_begin + a.nq + PREFILL_KB - 1) / PREFILL_KB;
+    ic_seq_group grp{};
+    int nblk = (a.nq + QB - 1) / QB;
+    if (a.grp) {                                        // query blocks of each sequence, in order
+        grp = *a.grp;
+        grp.blk0[0] = 0;
+        for (int i = 0; i < grp.n; ++i) grp.blk0[i + 1] = grp.blk0[i] + (grp.row0[i + 1] - grp.row0[i] + QB - 1) / QB;
+        nblk = grp.blk0[grp.n];
+    }
+    const int nkb_max = (prefill_max_keys(a) + PREFILL_KB - 1) / PREFILL_KB;
     const dim3 grid(nblk, (nkb_max + seg_blocks - 1) / seg_blocks);
     hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D_I, HT, QW, NW, PREFILL_KB>), grid, dim3(NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.scores, a.row_stride,
-                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks, a.run_if);
+                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks, a.run_if, grp, a.k_seq_bytes);
     return hipGetLastError();
 }
 

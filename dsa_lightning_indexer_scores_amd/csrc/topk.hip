@@ -123,7 +123,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
                                                   int32_t* __restrict__ idx, int max_len, int seg, int nseg,
                                                   const int32_t* __restrict__ cand, int cand_len,
                                                   uint32_t* __restrict__ ckeys, int len_step,
-                                                  const int32_t* __restrict__ run_if) {
+                                                  const int32_t* __restrict__ run_if, const ic_seq_group grp) {
     if (run_if != nullptr && *run_if == 0) return;            // a refresh that was not needed
     constexpr int NR = EPT / 4;                      // rounds of 4 consecutive keys per lane
     constexpr int BLOCK = NT * EPT;                  // keys per block
@@ -148,8 +148,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
     int32_t* out = idx + (int64_t)row * k;
     const int srow = MODE == TOPK_SEGS ? row / nseg : row;   // score row
     // visible length of the score row, clamped to the allocated row (a bad seq_len cannot overrun)
-    const int len = max(1, min(seq_len ? seq_len[srow] : first_len + srow * len_step,
-                               (STREAM || MODE != TOPK_ROWS) ? max_len : min(max_len, BLOCK)));
+    int vis;
+    if (grp.n > 0) {                                 // grouped rows: the row's own sequence and position
+        const int i = group_find(grp.row0, grp.n, srow);
+        vis = grp.pos0[i] + srow - grp.row0[i] + 1;
+    } else {
+        vis = seq_len ? seq_len[srow] : first_len + srow * len_step;
+    }
+    const int len = max(1, min(vis, (STREAM || MODE != TOPK_ROWS) ? max_len : min(max_len, BLOCK)));
     int n = len, off = 0;                            // keys this workgroup ranks; position offset
     uint32_t* okey = ckeys + (int64_t)row * k;       // TOPK_SEGS: keys of the picks
     if constexpr (MODE == TOPK_SEGS) {
@@ -540,16 +546,18 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
 template <int MODE>
 hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int nseg, const int32_t* cand,
                        uint32_t* ckeys, int32_t* out, bool vec, hipStream_t st) {
+    ic_seq_group grp{};
+    if (a.grp && MODE == TOPK_ROWS) grp = *a.grp;
 #define IC_TOPK_GO(NT, EPT, STREAM)                                                                          \
     do {                                                                                                    \
         if (vec)                                                                                            \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, true, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,      \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len, ckeys, a.len_step, a.run_if);                               \
+                               nseg, cand, len, ckeys, a.len_step, a.run_if, grp);                          \
         else                                                                                                \
             hipLaunchKernelGGL((topk_kernel<NT, EPT, false, STREAM, MODE>), dim3(rows), dim3(NT), 0, st,     \
                                a.scores, a.row_stride, a.first_len, a.seq_len, a.k, out, a.max_len, seg,    \
-                               nseg, cand, len, ckeys, a.len_step, a.run_if);                               \
+                               nseg, cand, len, ckeys, a.len_step, a.run_if, grp);                          \
         return hipGetLastError();                                                                           \
     } while (0)
     if (len <= 2048) IC_TOPK_GO(256, 8, false);

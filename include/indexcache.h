@@ -223,7 +223,9 @@ IC_API ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_la
  *   k_I [B, Lk, d_I], kv [B, Lk, 2, d]                        (per-sequence caches)
  *   idx_cache [Lq, k] int32.
  * Pattern and cache rules as ic_run_stack; the workspace is
- * ic_workspace_size(shape, IC_OP_RUN_STACK_VARLEN). */
+ * ic_workspace_size(shape, IC_OP_RUN_STACK_VARLEN).  Consecutive sequences of at most
+ * shape.chunk queries in all (up to 64 of them) share one launch of each kernel per layer;
+ * a longer sequence runs alone, in chunks. */
 IC_API ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, const ic_layer* layers,
                                      const ic_shape* shape, const int32_t* q_len, const int32_t* pos0,
                                      int32_t* idx_cache, void* ws, size_t ws_bytes, ic_stats* stats, void* stream);
