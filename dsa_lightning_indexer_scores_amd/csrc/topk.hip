@@ -106,15 +106,22 @@ __device__ __forceinline__ uint32_t waves_scan(uint32_t wave_total, uint32_t* wt
 // segment; also writes the picks' keys to ckeys); or a row's candidates (TOPK_GATHER:
 // keys from ckeys, positions from cand).
 enum { TOPK_ROWS = 0, TOPK_SEGS = 1, TOPK_GATHER = 2 };
+constexpr int TOPK_MANY_ROWS = 1024;     // launches of this many rows use the several-rows-per-CU shapes
 
-// Many-row launches of the 1024 x 16 and 512 x 16 shapes are held to 64 VGPRs, so two
-// (four) rows' workgroups share a CU and one row's barriers and memory waits hide behind
-// the others' work.  Measured in the stack's chunked launches: 1024 x 16 loses 8% without
-// the cap; 1024 x 24 is about 0.5% faster with one row per CU (at two, the rows' phases
-// contend and each takes about twice as long); 32 keys per thread do not fit.  The decode
-// shapes (a few rows per launch) keep their registers.
+// A workgroup ranks one row through a chain of short phases separated by barriers, so a
+// CU is kept busy by several rows at once: one row's barriers and waits hide behind the
+// others' work.  Many-row launches therefore use shapes held to 64 VGPRs (two 1024-thread
+// or four 512-thread workgroups per CU) or 512 x 64 at 128 (two per CU).  Measured on the
+// stack's eight 4096-row launches over a 32K layer (ms per launch, largest rows last):
+// 1024 x 24 and 1024 x 32 at one row per CU 0.19-0.26; 512 x 32 / 1024 x 24 (capped) /
+// 512 x 64 at two to four rows per CU 0.083-0.19, 0.92 ms in all against 1.19.  (At the
+// cap 1024 x 24 spills five registers and still beats 768 x 32 and 512 x 48; 1024 x 32
+// capped spills more and loses to 512 x 64.)  The few-row shapes (decode) keep their
+// registers: with one row per CU, a row's latency is what counts.
 constexpr int topk_waves_per_eu(int NT, int EPT, int MODE) {
-    return (MODE == TOPK_ROWS && ((NT == 1024 && EPT <= 16) || (NT == 512 && EPT <= 16))) ? 8 : 1;
+    return MODE != TOPK_ROWS ? 1
+         : ((NT == 1024 && EPT <= 16) || (NT == 512 && EPT <= 32) || (NT == 1024 && EPT == 24)) ? 8
+         : (NT == 512 && EPT == 64) ? 4 : 1;
 }
 
 template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
@@ -382,7 +389,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
     auto emit = [&](auto&& sel_fn) {
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
-            const int b0 = blk * BLOCK + lane_base;
+            // positions are recomputed from an opaque base in every pass, so that no
+            // per-round position registers stay live through the whole kernel (spills)
+            int b0 = blk * BLOCK + lane_base;
+            asm volatile("" : "+v"(b0));
             uint32_t wcount = 0;
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
@@ -439,7 +449,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
                         const uint32_t at = atomicAdd(&ncand, 1u);
                         if (at < (uint32_t)CAND_CAP) {
                             cand_key[at] = kk;
-                            cand_idx[at] = blk * BLOCK + lane_base + 256 * j + e;
+                            int p0 = blk * BLOCK + lane_base;
+                            asm volatile("" : "+v"(p0));
+                            cand_idx[at] = p0 + 256 * j + e;
                         }
                     }
                 }
@@ -454,16 +466,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
             const uint32_t ck = cand_key[c];
             const int32_t ci = cand_idx[c];
             uint32_t rank = 0, same = 0;
-            for (int o = 0; o < ncp; o += 16) {
-                uint4 ok[4];
-                int4 oi[4];
+            constexpr int RU = EPT >= 32 ? 2 : 4;       // 16-byte reads per list per step (registers)
+            for (int o = 0; o < ncp; o += 4 * RU) {
+                uint4 ok[RU];
+                int4 oi[RU];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < RU; ++u) {
                     ok[u] = *reinterpret_cast<const uint4*>(&cand_key[o + 4 * u]);
                     oi[u] = *reinterpret_cast<const int4*>(&cand_idx[o + 4 * u]);
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < RU; ++u) {
                     const uint32_t kq[4] = {ok[u].x, ok[u].y, ok[u].z, ok[u].w};
                     const int32_t iq[4] = {oi[u].x, oi[u].y, oi[u].z, oi[u].w};
 #pragma unroll
@@ -498,7 +511,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
             uint32_t eq_run = 0;
             for (int blk = 0; blk < nblocks; ++blk) {
                 if (STREAM) load_block(blk);
-                const int b0 = blk * BLOCK + lane_base;
+                int b0 = blk * BLOCK + lane_base;
+                asm volatile("" : "+v"(b0));
                 uint32_t wcount = 0;
 #pragma unroll
                 for (int j = 0; j < NR; ++j) {
@@ -564,9 +578,14 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
     if (len <= 4096) IC_TOPK_GO(256, 16, false);
     if constexpr (MODE == TOPK_ROWS) {
         if (len <= 8192) IC_TOPK_GO(512, 16, false);
-        if (len <= 16384) IC_TOPK_GO(1024, 16, false);
-        if (len <= 24576) IC_TOPK_GO(1024, 24, false);
-        if (len <= 32768) IC_TOPK_GO(1024, 32, false);
+        if (rows >= TOPK_MANY_ROWS) {                 // several rows per CU
+            if (len <= 16384) IC_TOPK_GO(512, 32, false);
+            if (len <= 24576) IC_TOPK_GO(1024, 24, false);
+            if (len <= 32768) IC_TOPK_GO(512, 64, false);
+        } else {                                      // about one row per CU: all threads on a row
+            if (len <= 16384) IC_TOPK_GO(1024, 16, false);
+            if (len <= 32768) IC_TOPK_GO(1024, 32, false);
+        }
         IC_TOPK_GO(1024, 32, true);
     } else {
         // a segment, or a candidate list of at most TOPK_GATHER_MAX keys: one register-resident

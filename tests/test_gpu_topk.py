@@ -68,6 +68,27 @@ def test_topk_long_rows_largest_k(n0):
     _run(m, n0, 4096)
 
 
+@pytest.mark.parametrize("n_last,k,kind", [(8192, 2048, "random"), (16384, 2048, "ties"), (16384, 4096, "random"),
+                                           (24576, 2048, "random"), (24576, 2048, "threshold_tie"),
+                                           (32768, 2048, "ties"), (32768, 4096, "threshold_tie")])
+def test_topk_many_rows(n_last, k, kind):
+    """Launches of 1024 rows take the several-rows-per-CU shapes (512 x 16, 512 x 32,
+    1024 x 24 held to 64 VGPRs, 512 x 64); the last row fills its shape exactly.  Every row
+    against the oracle, with heavy integer ties, random scores, and ties straddling the
+    k-th key."""
+    rng = np.random.default_rng(n_last + k)
+    rows = 1024
+    first = n_last - rows + 1
+    if kind == "ties":
+        m = rng.integers(-3, 4, size=(rows, n_last)).astype(np.float32)
+    elif kind == "random":
+        m = (rng.standard_normal((rows, n_last)) * 50).astype(np.float32)
+    else:
+        m = np.abs(rng.standard_normal((rows, n_last)).astype(np.float32)) * 30
+        m[:, 3::11] = np.float32(40.0)
+    _run(m, first, k)
+
+
 def test_topk_k_larger_than_rows():
     m = np.random.default_rng(1).standard_normal((8, 40)).astype(np.float32)
     _run(m, 10, 64)
