@@ -49,8 +49,10 @@ constexpr int HIST_BITS = 11;
 constexpr int HIST_BINS = 1 << HIST_BITS;
 constexpr int CAND_CAP = 256;       // threshold-bin keys resolved by exact ranking in LDS
 
-__device__ __forceinline__ uint32_t lanes_below(uint64_t m) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+// acc + the number of lanes below this one whose bit is set in m (mbcnt adds its accumulator
+// operand for free, so running prefixes chain through it)
+__device__ __forceinline__ uint32_t lanes_below(uint64_t m, uint32_t acc = 0u) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, acc));
 }
 
 // Wave-wide sum / min / max, result in every lane: DPP pairs inside each 16-lane row
@@ -386,36 +388,42 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
     uint32_t pos_run = 0;
     // Emit in index order the keys that sel(key, position) picks: per block, wave counts
     // from ballots, a prefix over the waves, then ranks within the wave from ballots.
-    auto emit = [&](auto&& sel_fn) {
+    // With `counted` (a row held in registers), wtot already holds every wave's number of
+    // selected keys, and the counting sweep is skipped.
+    auto emit = [&](auto&& sel_fn, bool counted) {
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
             // positions are recomputed from an opaque base in every pass, so that no
             // per-round position registers stay live through the whole kernel (spills)
             int b0 = blk * BLOCK + lane_base;
             asm volatile("" : "+v"(b0));
-            uint32_t wcount = 0;
+            uint32_t sel_tot = 0, pos = 0;
+            if (!STREAM && counted) {
 #pragma unroll
-            for (int j = 0; j < NR; ++j) {
-                if (!round_live(blk, j)) continue;
+                for (int i = 0; i < NT / 64; ++i) pos += (i < wv) ? wtot[i] : 0u;
+            } else {
+                uint32_t wcount = 0;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    wcount += (uint32_t)__popcll(__ballot(sel_fn(key[4 * j + e], b0 + 256 * j + e)));
+                for (int j = 0; j < NR; ++j) {
+                    if (!round_live(blk, j)) continue;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        wcount += (uint32_t)__popcll(__ballot(sel_fn(key[4 * j + e], b0 + 256 * j + e)));
+                }
+                pos = pos_run + waves_scan<NT>(wcount, wtot, &sel_tot);
             }
-            uint32_t sel_tot;
-            uint32_t pos = pos_run + waves_scan<NT>(wcount, wtot, &sel_tot);
 #pragma unroll
             for (int j = 0; j < NR; ++j) {
                 if (!round_live(blk, j)) continue;
                 bool sel[4];
-                uint32_t before = 0, tot = 0;
+                uint32_t r = pos, tot = 0;                   // r: this lane's first output slot
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     sel[e] = sel_fn(key[4 * j + e], b0 + 256 * j + e);
                     const uint64_t b = __ballot(sel[e]);
-                    before += lanes_below(b);
+                    r = lanes_below(b, r);
                     tot += (uint32_t)__popcll(b);
                 }
-                uint32_t r = pos + before;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     if (sel[e]) {
@@ -436,7 +444,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
         // Gather the bin's keys (with their positions) into LDS and find the k_rem-th of
         // them in (key descending, position ascending) order: the exact threshold pair,
         // and how many keys share its value.  (ncand and the padded list were set up
-        // before the first pass.)
+        // before the first pass.)  A row held in registers also counts, per wave, the keys
+        // above the bin (all selected); the ranking adds each wave's selected bin keys, so
+        // the emit knows every wave's output offset without a counting sweep.
+        uint32_t n_above = 0;
         for (int blk = 0; blk < nblocks; ++blk) {
             if (STREAM) load_block(blk);
 #pragma unroll
@@ -445,6 +456,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const uint32_t kk = key[4 * j + e];
+                    if (!STREAM) n_above += (kk >> shift) > prefix ? 1u : 0u;   // key 0 is never above
                     if (kk != 0u && (kk >> shift) == prefix) {
                         const uint32_t at = atomicAdd(&ncand, 1u);
                         if (at < (uint32_t)CAND_CAP) {
@@ -456,6 +468,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
                     }
                 }
             }
+        }
+        if (!STREAM) {                               // wtot was last read before the pass's final barrier
+            const uint32_t wa = wave_sum(n_above);
+            if (lane == 0) wtot[wv] = wa;
         }
         __syncthreads();
         const int nc = (int)min(ncand, (uint32_t)CAND_CAP);
@@ -487,14 +503,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
                 }
             }
             if (rank == k_rem - 1u) { thr_key = ck; thr_idx = ci; thr_ties = same; }
+            if (!STREAM && rank < k_rem) atomicAdd(&wtot[ci / (64 * EPT)], 1u);   // selected: its wave's count
         }
         __syncthreads();
         const uint32_t tk = thr_key;
         const int32_t ti = thr_idx;
         if (thr_ties == 1u)                          // the threshold value is unique: a key test suffices
-            emit([&](uint32_t kk, int) { return kk >= tk; });
+            emit([&](uint32_t kk, int) { return kk >= tk; }, true);
         else
-            emit([&](uint32_t kk, int p) { return (kk > tk) || (kk == tk && p <= ti); });
+            emit([&](uint32_t kk, int p) { return (kk > tk) || (kk == tk && p <= ti); }, true);
     } else {
         // Digit above the prefix -> selected; equal -> the first k_rem of them in index
         // order (all of them when the bin is taken whole).  Empty candidate slots (key 0)
@@ -503,7 +520,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
         auto digit = [&](uint32_t kk) -> uint32_t { return shift >= 32 ? 0u : (kk >> shift); };
         auto is_eq = [&](uint32_t kk) -> bool { return digit(kk) == prefix && (MODE != TOPK_GATHER || kk != 0u); };
         if (whole) {
-            emit([&](uint32_t kk, int) { return digit(kk) > prefix || is_eq(kk); });
+            emit([&](uint32_t kk, int) { return digit(kk) > prefix || is_eq(kk); }, false);
         } else {
             // the k_rem-th equal key in index order is the last one taken: find its position
             // (per block: wave counts of equal keys, a prefix over the waves, ballot ranks)
@@ -526,15 +543,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
                 for (int j = 0; j < NR; ++j) {
                     if (!round_live(blk, j)) continue;
                     bool eq[4];
-                    uint32_t before = 0, tot = 0;
+                    uint32_t q = r, tot = 0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         eq[e] = is_eq(key[4 * j + e]);
                         const uint64_t b = __ballot(eq[e]);
-                        before += lanes_below(b);
+                        q = lanes_below(b, q);
                         tot += (uint32_t)__popcll(b);
                     }
-                    uint32_t q = r + before;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         if (eq[e]) {
@@ -548,7 +564,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_p
             }
             __syncthreads();
             const int32_t ti = thr_idx;
-            emit([&](uint32_t kk, int p) { return digit(kk) > prefix || (is_eq(kk) && p <= ti); });
+            emit([&](uint32_t kk, int p) { return digit(kk) > prefix || (is_eq(kk) && p <= ti); }, false);
         }
     }
     __syncthreads();
