@@ -477,29 +477,15 @@ __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8
 
 constexpr int PREFILL_KB = 128;                              // keys per LDS block
 
-// Key blocks per work item: the longest query block splits into about four pieces,
-// and no piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
-// linear-term rows) small next to its key sweep.
+// Key blocks per work item: the longest query block splits into two pieces, and no
+// piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
+// linear-term rows) small next to its key sweep.  Measured on the stack32k stack
+// (alternating runs, identical indices): two pieces 37.3 ms per step, one 37.3-37.9,
+// three 38.4, four 37.8, eight 39.1.
 inline int prefill_max_keys(const ic_indexer_args& a);
 inline int prefill_seg_blocks(const ic_indexer_args& a) {
     const int nkb_max = (prefill_max_keys(a) + PREFILL_KB - 1) / PREFILL_KB;
-    return std::max(1024 / PREFILL_KB, (nkb_max + 3) / 4);
-}
-
-// Work items (query block, key segment) that are not past the causal edge.
-inline int64_t prefill_items(const ic_indexer_args& a, int QB, int seg_blocks) {
-    int64_t items = 0;
-    const int nseq = a.grp ? a.grp->n : 1;
-    for (int i = 0; i < nseq; ++i) {
-        const int nq = a.grp ? a.grp->row0[i + 1] - a.grp->row0[i] : a.nq;
-        const int pos = a.grp ? a.grp->pos0[i] : a.pos_begin;
-        for (int t0 = 0; t0 < nq; t0 += QB) {
-            const int nkeys = pos + std::min(t0 + QB, nq);
-            const int nkb = (nkeys + PREFILL_KB - 1) / PREFILL_KB;
-            items += (nkb + seg_blocks - 1) / seg_blocks;
-        }
-    }
-    return items;
+    return std::max(1024 / PREFILL_KB, (nkb_max + 1) / 2);
 }
 
 // Keys visible to the launch's longest row.
@@ -530,15 +516,16 @@ hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t 
     return hipGetLastError();
 }
 
-// 8-wave workgroups share each k_I block among 16 queries (one workgroup per CU at two
-// waves per SIMD); when that leaves fewer than four work items per CU, 4-wave workgroups
-// (two per CU) keep the CUs fed.
+// 4-wave workgroups, two per CU (one wave of each on every SIMD): while one workgroup
+// waits at its per-block barrier, the other's MFMAs keep the SIMD's matrix pipe busy,
+// and the finer workgroups share CUs better with the top-k and attention launches that
+// run beside the indexer in the stack.  Measured on stack32k (alternating runs, identical
+// indices): one 32K-query launch 3.33 ms against 3.43 with 8-wave workgroups (one per CU,
+// both waves of a SIMD stopping at the same barrier); the 16-layer stack 37.5 ms against
+// 39.0.  2-wave workgroups (three per CU, LDS-bound) took 4.2 ms and 42.0 ms.
 template <bool FP8, int D_I, int HT>
 hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
-    constexpr int QW = FP8 ? 2 : 1;
-    const int seg = prefill_seg_blocks(a);
-    if (prefill_items(a, QW * 8, seg) >= 1024) return prefill_launch<FP8, D_I, HT, 8>(a, seg, st);
-    return prefill_launch<FP8, D_I, HT, 4>(a, seg, st);
+    return prefill_launch<FP8, D_I, HT, 4>(a, prefill_seg_blocks(a), st);
 }
 
 template <bool FP8, int D_I, int HT>
