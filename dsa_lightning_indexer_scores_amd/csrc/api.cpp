@@ -91,6 +91,9 @@ ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode, bool v
     if (!sp) return fail(IC_ERR_ARG, "shape is NULL");
     const ic_shape& s = *sp;
     if (s.B < 1 || s.Lq < 1 || s.Lk < 1) return fail(IC_ERR_SHAPE, "B, Lq, Lk must be >= 1 (got %d, %d, %d)", s.B, s.Lq, s.Lk);
+    // query rows are grid and row indices of 32 bits in the kernels
+    if ((int64_t)s.B * s.Lq > INT32_MAX)
+        return fail(IC_ERR_SHAPE, "B x Lq (%lld query rows) exceeds 2^31 - 1", (long long)s.B * s.Lq);
     if (decode) {
         if (s.Lq != 1) return fail(IC_ERR_SHAPE, "decode needs Lq == 1 (got %d)", s.Lq);
     } else if (varlen) {
@@ -136,8 +139,8 @@ size_t indexer_ws_varlen(const ic_shape& s) {
 // only add partials for the combine to merge, fewer leave CUs idle), at most one
 // 32-row tile per split, and a multiple of 4 (a workgroup merges 4 splits).
 int decode_splits(const ic_shape& s) {
-    const int HG = (s.H + 15) / 16;
-    const int want = (1024 + s.B * HG - 1) / (s.B * HG);
+    const int64_t groups = (int64_t)s.B * ((s.H + 15) / 16);   // (query, head group) pairs
+    const int want = (int)((1024 + groups - 1) / groups);
     const int tiles = (s.k + 31) / 32;
     const int ns = std::min(want, tiles);
     return ns < 4 ? 1 : ns / 4 * 4;
@@ -500,6 +503,8 @@ ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, in
     if ((int64_t)first_len + rows - 1 > row_stride)
         return fail(IC_ERR_SHAPE, "last row length %lld exceeds row_stride %lld",
                     (long long)first_len + rows - 1, (long long)row_stride);
+    if ((int64_t)first_len + rows - 1 > INT32_MAX)
+        return fail(IC_ERR_SHAPE, "last row length %lld exceeds 2^31 - 1", (long long)first_len + rows - 1);
     ic_topk_args t;
     t.scores = scores;
     t.row_stride = row_stride;

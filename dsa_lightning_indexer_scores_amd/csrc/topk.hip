@@ -616,9 +616,9 @@ hipError_t topk_launch(const ic_topk_args& a, int rows, int len, int seg, int ns
 
 int topk_segments(const ic_topk_args& a) {
     if (a.max_len <= 32768 || a.rows > TOPK_SEG_MAX_ROWS) return 0;
-    const int nseg = (a.max_len + TOPK_SEG - 1) / TOPK_SEG;
+    const int64_t nseg = ((int64_t)a.max_len + TOPK_SEG - 1) / TOPK_SEG;
     // the candidate list must fit one register-resident 1024 x 16 block
-    return (int64_t)nseg * a.k <= TOPK_GATHER_MAX ? nseg : 0;
+    return nseg * a.k <= TOPK_GATHER_MAX ? (int)nseg : 0;
 }
 
 size_t topk_ws_bytes(const ic_topk_args& a) {

@@ -88,8 +88,8 @@ typedef enum ic_dtype {
     IC_FP8_E4M3 = 1               /* q_I / k_I stored as OCP e4m3fn codes */
 } ic_dtype;
 
-/* Sizes of one call.  Limits: B >= 1; 1 <= Lq; pos0 >= 0; pos0 + Lq <= Lk
- * (prefill); H_I in 1..64; d_I in {32, 64, 128}; k in 1..4096; H in 1..4096;
+/* Sizes of one call.  Limits: B >= 1; 1 <= Lq; B * Lq <= 2^31 - 1 (query rows);
+ * pos0 >= 0; pos0 + Lq <= Lk (prefill); H_I in 1..64; d_I in {32, 64, 128}; k in 1..4096; H in 1..4096;
  * d in {64, 128}; Lk * 4 * d < 4 GiB (one sequence's KV rows, addressed with
  * 32-bit offsets); chunk 0 (= 4096) or 16..65536 in steps of 16. */
 typedef struct ic_shape {
@@ -164,7 +164,7 @@ IC_API ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const
 
 /* Top-k of caller-supplied score rows with the same rule as ic_indexer_topk:
  * scores [rows, row_stride] fp32, row r has n_r = first_len + r visible
- * entries (first_len >= 1, n_r <= row_stride); writes idx [rows, k] int32.
+ * entries (first_len >= 1, n_r <= row_stride and <= 2^31 - 1); writes idx [rows, k] int32.
  * Used to test the selection on chosen inputs (ties, -0.0, k >= n). */
 IC_API ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len,
                        int32_t k, int32_t* idx, void* stream);
