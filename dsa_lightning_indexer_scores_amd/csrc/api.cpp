@@ -689,24 +689,22 @@ ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_l
                 const float* wb = L.w + (size_t)b * s.Lq * s.H_I;
                 const uint8_t* kb = static_cast<const uint8_t*>(L.k_I) + (size_t)b * s.Lk * s.d_I * eb;
                 int32_t* idxb = idx_cache + (size_t)b * s.Lq * s.k;
-                // probe: this layer's own scores and top-k for every probe_stride-th query
-                ic_indexer_decode_args a{};
-                a.q_I = qb + (size_t)d.t0 * s.H_I * s.d_I * eb;
-                a.w = wb + (size_t)d.t0 * s.H_I;
+                // probe: this layer's own scores and top-k for every probe_stride-th query (the
+                // prefill indexer over strided query rows: the probe queries share each k_I block)
+                ic_indexer_args a;
+                a.q_I = qb;
+                a.w = wb;
                 a.k_I = kb;
-                a.seq_len = nullptr;
                 a.scores = pscores;
-                a.score_stride = d.score_stride;
-                a.B = d.P;
-                a.Lk = s.pos0 + s.Lq;
+                a.row_stride = d.score_stride;
+                a.q_begin = d.t0;
+                a.nq = d.P;
+                a.pos_begin = s.pos0 + d.t0;
+                a.q_step = probe_stride;
                 a.H_I = s.H_I;
                 a.d_I = s.d_I;
                 a.fp8 = s.idx_dtype == IC_FP8_E4M3;
-                a.q_rows = probe_stride;
-                a.k_rows = 0;
-                a.len0 = s.pos0 + d.t0 + 1;
-                a.len_step = probe_stride;
-                hipError_t e = launch_indexer_decode(a, st);
+                hipError_t e = launch_indexer_prefill(a, st);
                 if (e != hipSuccess) return hip_fail(e, "probe indexer launch");
                 ic_topk_args t{};
                 t.scores = pscores;

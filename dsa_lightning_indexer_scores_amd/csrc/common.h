@@ -163,6 +163,8 @@ struct ic_indexer_args {
     int32_t pos_begin;    // absolute position of query q_begin
     int32_t H_I, d_I;
     int32_t fp8;
+    int32_t q_step = 1;   // query t of the tile is q_I row q_begin + t * q_step at position
+                          // pos_begin + t * q_step (strided probe rows); score row t stays dense
     const int32_t* run_if = nullptr;   // optional device flag: the launch does nothing while it is 0
     // Grouped launch (several sequences): q_I / w rows, score rows and row counts follow the
     // group's packed rows (q_begin, nq and pos_begin are then unused); sequence i's keys start
@@ -173,16 +175,13 @@ struct ic_indexer_args {
 hipError_t launch_indexer_prefill(const ic_indexer_args& a, hipStream_t st);
 
 struct ic_indexer_decode_args {
-    const void* q_I;      // row b at q_I + b * q_rows query rows ([B, H_I, d_I] when q_rows = 1)
-    const float* w;       // row b at w + b * q_rows rows of H_I
-    const void* k_I;      // keys of row b at k_I + b * k_rows key rows ([B, Lk, d_I] when k_rows = Lk)
-    const int32_t* seq_len;  // [B] device; NULL: row b sees len0 + b * len_step keys
+    const void* q_I;      // [B, H_I, d_I]: one query per sequence
+    const float* w;       // [B, H_I]
+    const void* k_I;      // [B, Lk, d_I]
+    const int32_t* seq_len;  // [B] device: row b sees seq_len[b] keys
     float* scores;        // [B, score_stride]
     int64_t score_stride; // >= Lk
     int32_t B, Lk, H_I, d_I, fp8;
-    int64_t q_rows = 1;   // query rows between consecutive b (strided probe rows)
-    int64_t k_rows = -1;  // key rows between consecutive b; -1 means Lk, 0 shares one key set
-    int32_t len0 = 0, len_step = 0;
 };
 hipError_t launch_indexer_decode(const ic_indexer_decode_args& a, hipStream_t st);
 

@@ -227,7 +227,7 @@ template <bool FP8, int D_I, int HT, int QW, int NW, int KB>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void indexer_prefill_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI_,
     float* __restrict__ scores_, int64_t row_stride, int q_begin_, int nq_, int pos_begin_, int H_I, int seg_blocks,
-    const int32_t* __restrict__ run_if, const ic_seq_group grp, int64_t k_seq_bytes) {
+    const int32_t* __restrict__ run_if, const ic_seq_group grp, int64_t k_seq_bytes, int q_step) {
     if (run_if != nullptr && *run_if == 0) return;            // a refresh that was not needed
     using G = IdxGeom<FP8, D_I>;
     static_assert(KB % 64 == 0, "a key block is stored 64 keys per instruction");
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     const int t0 = blk * QB;
     const int t_last = min(t0 + QB, nq) - 1;
-    const int nkeys = pos_begin + t_last + 1;                 // keys visible to the block
+    const int nkeys = pos_begin + t_last * q_step + 1;        // keys visible to the block
     const int nkb = (nkeys + KB - 1) / KB;
     // Work item: this query block's key blocks [kb_begin, kb_end).  Scores need no sum
     // across keys, so splitting long rows into segments only balances the load.
@@ -283,9 +283,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int t = t0 + wv * QW + q;
         const bool valid = t < nq;
         qvalid[q] = valid;
-        pq[q] = valid ? pos_begin + t : -1;
+        pq[q] = valid ? pos_begin + t * q_step : -1;
         srow[q] = scores + (int64_t)(valid ? t : 0) * row_stride + 16 * g + r;
-        const int64_t qrow = (int64_t)(q_begin + (valid ? t : 0)) * H_I;
+        const int64_t qrow = (int64_t)(q_begin + (valid ? t : 0) * q_step) * H_I;
         qrows[q] = qrow;
 #pragma unroll
         for (int ht = 0; ht < HT; ++ht) {
@@ -423,17 +423,16 @@ constexpr int DEC_KEYS_PER_WG = DEC_NW * DEC_KEYS_PER_WAVE;
 template <bool FP8, int D_I, int HT>
 __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8 ? 3 : 2, FP8 ? 3 : 2))) void indexer_decode_kernel(
     const uint8_t* __restrict__ qI, const float* __restrict__ w, const uint8_t* __restrict__ kI,
-    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I,
-    int64_t q_rows, int64_t k_rows, int len0, int len_step) {
+    const int32_t* __restrict__ seq_len, float* __restrict__ scores, int64_t score_stride, int Lk, int H_I) {
     using G = IdxGeom<FP8, D_I>;
     const int b = blockIdx.y;
-    const int n = max(1, min(seq_len ? seq_len[b] : len0 + b * len_step, Lk));   // visible keys (clamped to the cache)
+    const int n = max(1, min(seq_len[b], Lk));              // visible keys (clamped to the cache)
     const int lane = threadIdx.x & 63, wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int r = lane & 15, g = lane >> 4;
     const int key0 = blockIdx.x * DEC_KEYS_PER_WG + wv * DEC_KEYS_PER_WAVE;
     if (key0 >= n) return;
 
-    const uint8_t* kbase = kI + (int64_t)b * k_rows * G::ROWB;
+    const uint8_t* kbase = kI + (int64_t)b * Lk * G::ROWB;
     Frag<FP8, D_I> Bf[2][DEC_TILES];
     auto load_chunk = [&](Frag<FP8, D_I> (&B)[DEC_TILES], int c) {
 #pragma unroll
@@ -449,9 +448,9 @@ __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8
 #pragma unroll
     for (int ht = 0; ht < HT; ++ht) {
         const int h = 16 * ht + r;
-        load_frag<FP8, D_I>(A[ht], h < H_I ? qI + ((int64_t)b * q_rows * H_I + h) * G::ROWB : nullptr, g);
+        load_frag<FP8, D_I>(A[ht], h < H_I ? qI + ((int64_t)b * H_I + h) * G::ROWB : nullptr, g);
     }
-    load_w<HT>(wr, w + (int64_t)b * q_rows * H_I, H_I, g);
+    load_w<HT>(wr, w + (int64_t)b * H_I, H_I, g);
     float* srow = scores + (int64_t)b * score_stride;
 #pragma unroll
     for (int c = 0; c < DEC_CHUNKS; ++c) {
@@ -477,27 +476,29 @@ __global__ __launch_bounds__(DEC_NW * 64) __attribute__((amdgpu_waves_per_eu(FP8
 
 constexpr int PREFILL_KB = 128;                              // keys per LDS block
 
-// Key blocks per work item: the longest query block splits into two pieces, and no
-// piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
+// Key blocks per work item: the longest query block splits into two pieces, or more when
+// the launch has few query blocks (at least 512 work items for the longest rows, two per
+// CU), and no piece is shorter than 1024 keys, which keeps the per-item set-up (q_I slab,
 // linear-term rows) small next to its key sweep.  Measured on the stack32k stack
 // (alternating runs, identical indices): two pieces 37.3 ms per step, one 37.3-37.9,
 // three 38.4, four 37.8, eight 39.1.
 inline int prefill_max_keys(const ic_indexer_args& a);
-inline int prefill_seg_blocks(const ic_indexer_args& a) {
+inline int prefill_seg_blocks(const ic_indexer_args& a, int nblk) {
     const int nkb_max = (prefill_max_keys(a) + PREFILL_KB - 1) / PREFILL_KB;
-    return std::max(1024 / PREFILL_KB, (nkb_max + 1) / 2);
+    const int pieces = std::max(2, (512 + nblk - 1) / std::max(nblk, 1));
+    return std::max(1024 / PREFILL_KB, (nkb_max + pieces - 1) / pieces);
 }
 
 // Keys visible to the launch's longest row.
 inline int prefill_max_keys(const ic_indexer_args& a) {
-    if (!a.grp) return a.pos_begin + a.nq;
+    if (!a.grp) return a.pos_begin + (a.nq - 1) * a.q_step + 1;
     int m = 1;
     for (int i = 0; i < a.grp->n; ++i) m = std::max(m, a.grp->pos0[i] + a.grp->row0[i + 1] - a.grp->row0[i]);
     return m;
 }
 
 template <bool FP8, int D_I, int HT, int NW>
-hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t st) {
+hipError_t prefill_launch(const ic_indexer_args& a, hipStream_t st) {
     constexpr int QW = FP8 ? 2 : 1;
     constexpr int QB = QW * NW;
     ic_seq_group grp{};
@@ -509,10 +510,12 @@ hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t 
         nblk = grp.blk0[grp.n];
     }
     const int nkb_max = (prefill_max_keys(a) + PREFILL_KB - 1) / PREFILL_KB;
+    const int seg_blocks = prefill_seg_blocks(a, nblk);
     const dim3 grid(nblk, (nkb_max + seg_blocks - 1) / seg_blocks);
     hipLaunchKernelGGL((indexer_prefill_kernel<FP8, D_I, HT, QW, NW, PREFILL_KB>), grid, dim3(NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.scores, a.row_stride,
-                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks, a.run_if, grp, a.k_seq_bytes);
+                       a.q_begin, a.nq, a.pos_begin, a.H_I, seg_blocks, a.run_if, grp, a.k_seq_bytes,
+                       a.grp ? 1 : a.q_step);
     return hipGetLastError();
 }
 
@@ -525,7 +528,7 @@ hipError_t prefill_launch(const ic_indexer_args& a, int seg_blocks, hipStream_t 
 // 39.0.  2-wave workgroups (three per CU, LDS-bound) took 4.2 ms and 42.0 ms.
 template <bool FP8, int D_I, int HT>
 hipError_t prefill_dispatch(const ic_indexer_args& a, hipStream_t st) {
-    return prefill_launch<FP8, D_I, HT, 4>(a, prefill_seg_blocks(a), st);
+    return prefill_launch<FP8, D_I, HT, 4>(a, st);
 }
 
 template <bool FP8, int D_I, int HT>
@@ -533,7 +536,7 @@ hipError_t decode_dispatch(const ic_indexer_decode_args& a, hipStream_t st) {
     dim3 grid((a.Lk + DEC_KEYS_PER_WG - 1) / DEC_KEYS_PER_WG, a.B);
     hipLaunchKernelGGL((indexer_decode_kernel<FP8, D_I, HT>), grid, dim3(DEC_NW * 64), 0, st,
                        (const uint8_t*)a.q_I, a.w, (const uint8_t*)a.k_I, a.seq_len, a.scores, a.score_stride,
-                       a.Lk, a.H_I, a.q_rows, a.k_rows < 0 ? (int64_t)a.Lk : a.k_rows, a.len0, a.len_step);
+                       a.Lk, a.H_I);
     return hipGetLastError();
 }
 
