@@ -101,3 +101,19 @@ def test_rows_without_a_valid_entry_give_zero(d):
     keep = [t for t in range(Lq) if t not in empty]
     ref = O.sparse_attn(dec(q)[0][keep], dec(kv)[0], idx[keep])
     assert attn_rel_err(got[keep], ref) <= ATTN_TOL
+
+
+def test_attention_largest_head_count():
+    """H = 4096 (the largest the boundary accepts): 256 head groups per query, each its own
+    wave, against the oracle on every query and head."""
+    torch.manual_seed(4096)
+    Lq, Lk, H, d, k = 4, 300, 4096, 64, 96
+    q = (torch.randn(1, Lq, H, d) * 0.5).to(torch.bfloat16).cuda()
+    kv = (torch.randn(1, Lk, 2, d) * 0.5).to(torch.bfloat16).cuda()
+    idx = idx_patterns(Lq, Lk, k, seed=7)
+    out = ic.sparse_attn(q, kv, torch.from_numpy(idx)[None].cuda())
+    torch.cuda.synchronize()
+    ref = O.sparse_attn(dec(q)[0], dec(kv)[0], idx)
+    err = attn_rel_err(dec(out)[0], ref)
+    summary("attention H=4096", {"max_rel_err": err})
+    assert err <= ATTN_TOL

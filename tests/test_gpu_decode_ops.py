@@ -101,3 +101,32 @@ def test_decode_ops_equal_decode_step():
     for l in range(2):
         o = ic.decode_attn(layers[l]["q"], layers[l]["kv"], idx)
         assert torch.equal(o, outs[l]), f"layer {l}"
+
+
+@pytest.mark.parametrize("B,H,d", [(96, 64, 128), (2, 4096, 64)])
+def test_decode_attn_one_split_per_query(B, H, d):
+    """With enough (sequence, head group) pairs the decode attention runs one wave per pair
+    and no split-K merge (fewer than four splits per query): 96 sequences x 4 head groups,
+    and the largest head count (4096 heads = 256 groups) with 2 sequences.  Against the
+    oracle, with holes, repeated entries and an empty row among the idx rows."""
+    rng = np.random.default_rng(B * 7 + H)
+    g = torch.Generator().manual_seed(B + H)
+    cap, k = 700, 160
+    seq_len = [int(x) for x in rng.integers(1, cap + 1, size=B)]
+    q = synth.encode(torch.randn((B, 1, H, d), generator=g) * 0.5, "bf16").cuda()
+    kv = synth.encode(torch.randn((B, cap, 2, d), generator=g) * 0.5, "bf16").cuda()
+    idx = _idx_rows(B, k, seq_len, cap, rng)
+    out = ic.decode_attn(q, kv, torch.from_numpy(idx)[:, None].cuda())
+    torch.cuda.synchronize()
+    got = dec(out)[:, 0]
+    qd, kvd = dec(q), dec(kv)
+    worst = 0.0
+    for b in range(B):
+        valid = idx[b][(idx[b] >= 0) & (idx[b] < cap)]
+        if valid.size == 0:
+            assert np.all(got[b] == 0.0), f"row {b} has no valid entry and must be zero"
+            continue
+        ref = O.sparse_attn_row(qd[b, 0], kvd[b], idx[b], 1.0 / np.sqrt(d))
+        worst = max(worst, attn_rel_err(got[b], ref))
+    summary(f"decode_attn one split B={B} H={H} d={d}", {"max_rel_err": worst})
+    assert worst <= ATTN_TOL
