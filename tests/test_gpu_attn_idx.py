@@ -117,3 +117,40 @@ def test_attention_largest_head_count():
     err = attn_rel_err(dec(out)[0], ref)
     summary("attention H=4096", {"max_rel_err": err})
     assert err <= ATTN_TOL
+
+
+def test_attention_at_the_largest_kv_capacity():
+    """Lk = 2^23 - 1 rows of 512 bytes (d = 128): the last row ends 512 bytes below 4 GiB,
+    the limit of the gather kernels' 32-bit row offsets.  Prefill (the last 8 queries) and
+    decode (split-K) attention over rows at both ends of the range, against the oracle on
+    the gathered rows."""
+    Lk, H, d, k, Lq = (1 << 23) - 1, 16, 128, 96, 8
+    g = torch.Generator(device="cuda").manual_seed(23)
+    kv = torch.empty((1, Lk, 2, d), dtype=torch.bfloat16, device="cuda")
+    step = 1 << 20
+    for r0 in range(0, Lk, step):                     # bounded temporaries
+        n = min(step, Lk - r0)
+        kv[0, r0:r0 + n] = (torch.randn((n, 2, d), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    q = (torch.randn((1, Lq, H, d), generator=g, device="cuda") * 0.5).to(torch.bfloat16)
+    rng = np.random.default_rng(23)
+    idx = np.empty((Lq, k), dtype=np.int32)
+    for t in range(Lq):
+        top = rng.choice(np.arange(Lk - 2000, Lk), size=k // 2, replace=False)
+        low = rng.choice(np.arange(0, 2000), size=k // 4, replace=False)
+        mid = rng.integers(0, Lk, size=k - k // 2 - k // 4)
+        idx[t] = np.sort(np.concatenate([low, mid, top]))
+    idx[0, -1] = Lk - 1                               # the very last row
+    idx_gpu = torch.from_numpy(idx).cuda()
+    out = ic.sparse_attn(q, kv, idx_gpu[None])
+    dq = ic.decode_attn(q[0, -1:].reshape(1, 1, H, d).contiguous(), kv, idx_gpu[-1:].reshape(1, 1, k).contiguous())
+    torch.cuda.synchronize()
+    worst = 0.0
+    for t in range(Lq):
+        rows = kv[0, idx_gpu[t].long()]               # the selected rows only
+        ref = O.sparse_attn_row(dec(q)[0, t], dec(rows), np.arange(k, dtype=np.int32), 1.0 / np.sqrt(d))
+        worst = max(worst, attn_rel_err(dec(out)[0, t], ref))
+        if t == Lq - 1:
+            worst = max(worst, attn_rel_err(dec(dq)[0, 0], ref))
+    del kv
+    summary("attention at Lk = 2^23 - 1", {"max_rel_err": worst})
+    assert worst <= ATTN_TOL
