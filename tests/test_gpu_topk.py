@@ -135,3 +135,17 @@ def test_topk_rows_seq_k(k):
     lens = [50000, 33000, 4096, 4097]
     m = rng.integers(-20, 20, size=(len(lens), 50000)).astype(np.float32)
     _run_seq(m, lens, k)
+
+
+@pytest.mark.parametrize("kind", ["random", "threshold_tie"])
+def test_topk_multi_million_key_rows(kind):
+    """Rows of about 4.2 million keys, streamed block by block through every pass, at the
+    largest k; the last row ends in a ragged block."""
+    rng = np.random.default_rng({"random": 5, "threshold_tie": 6}[kind])
+    n0, rows = (1 << 22) + 3, 2
+    if kind == "random":
+        m = (rng.standard_normal((rows, n0 + rows)) * 50).astype(np.float32)
+    else:
+        m = np.abs(rng.standard_normal((rows, n0 + rows)).astype(np.float32)) * 30
+        m[:, 3::11] = np.float32(120.0)               # ties straddling the k-th key
+    _run(m, n0, 4096)
