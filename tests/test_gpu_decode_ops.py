@@ -130,3 +130,27 @@ def test_decode_attn_one_split_per_query(B, H, d):
         worst = max(worst, attn_rel_err(got[b], ref))
     summary(f"decode_attn one split B={B} H={H} d={d}", {"max_rel_err": worst})
     assert worst <= ATTN_TOL
+
+
+def test_decode_lengths_out_of_range_are_clamped():
+    """seq_len values outside 1..Lk (0, negative, past the cache) come from device memory the
+    host cannot check; the decode indexer and top-k clamp them to 1..Lk, never reading or
+    writing past a row.  Scores and idx equal the oracle's at the clamped lengths."""
+    g = torch.Generator().manual_seed(77)
+    B, cap, H_I, d_I, k = 4, 3000, 16, 64, 256
+    seq_len = [0, -7, cap + 50, 1500]
+    clamped = [min(max(n, 1), cap) for n in seq_len]
+    q_I = synth.encode(_int((B, 1, H_I, d_I), g), "fp8").cuda()
+    k_I = synth.encode(_int((B, cap, d_I), g), "fp8").cuda()
+    w = _int((B, 1, H_I), g).cuda()
+    sl = torch.tensor(seq_len, dtype=torch.int32, device="cuda")
+    sc = ic.decode_indexer_scores(q_I, w, k_I, sl)
+    idx = ic.topk_rows_seq(sc, sl, k, max_len=cap)
+    torch.cuda.synchronize()
+    scn = sc.cpu().numpy().astype(np.float64)
+    got = idx.cpu().numpy()
+    for b in range(B):
+        n = clamped[b]
+        want = O.indexer_scores_row(dec(q_I[b, 0]), dec(w[b, 0]), dec(k_I[b]), n - 1)
+        assert np.array_equal(scn[b, :n], want), f"row {b}"
+        assert np.array_equal(got[b], O.topk_row(want.astype(np.float32), k)), f"row {b}"
