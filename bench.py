@@ -37,6 +37,8 @@ PEAK_TFLOPS = {"fp8": 5000.0, "bf16": 2500.0}
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "csrc")
 KERNEL_SOURCES = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "attn.hip", "distill": "distill.hip"}
+# launch grid of the whole-layer stack32k indexer in the kernel trace (8-query blocks x 2 key segments)
+INDEXER_WHOLE_GRID = "4096x2"
 
 
 def kernel_source_hash(kernel: str) -> str:
@@ -87,6 +89,24 @@ def profile_value(fname: str, kernel: str, key: str):
         return float(vals[key])
     except (KeyError, ValueError):
         return None
+
+
+def profile_grid_ms(fname: str, kernel: str, name_prefix: str, grid: str):
+    """Average duration (ms) of one kernel's launches of one grid in a committed kernel-trace
+    summary, or None if absent or taken on another source of the kernel."""
+    path = os.path.join(PROFILES, fname)
+    if not os.path.exists(path):
+        return None
+    ok, ms = False, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith(f"source_sha256.{kernel}:"):
+                ok = line.split(":", 1)[1].strip() == kernel_source_hash(kernel)
+            parts = line.split()
+            if line.startswith(name_prefix) and grid in parts:
+                i = parts.index(grid)
+                ms = float(parts[i + 2]) / 1e3            # grid, calls, avg_us
+    return ms if ok else None
 
 
 def log(msg: str):
@@ -720,6 +740,13 @@ def main():
                               "frac": ix["frac"], "kernel": "indexer", "ms": ix["ms"],
                               "traffic": measured_traffic("indexer"), "work": ix["work"],
                               "largest_share_kernel": dom}
+        # the same launch in the committed rocprofv3 trace (another box, another run): its
+        # average duration and the fraction it gives, for the comparison with `ms`
+        pms = profile_grid_ms("bench_stack32k_kernel_trace.txt", "indexer", "indexer_prefill_kernel<true",
+                              INDEXER_WHOLE_GRID)
+        if pms:
+            result["roofline"]["profile_ms"] = round(pms, 4)
+            result["roofline"]["profile_frac"] = round(ix["achieved"] * ix["ms"] / pms / ix["peak"], 4)
         for name in kr:
             t = measured_traffic(name)               # per dispatch; the distillation call makes one per tile
             kr[name]["traffic"] = None if t is None else t * kr[name].get("launches", 1)

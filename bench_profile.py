@@ -72,6 +72,8 @@ def cmd_trace(a):
     out = [f"# rocprofv3 kernel-trace summary: {a.title}"]
     out += [f"# command: {c}" for c in a.command]
     out += [f"# {x}" for x in a.note]
+    # the kernel sources the trace was taken on (bench.py reads a figure only while they match)
+    out += [f"source_sha256.{k}: {source_hash(k)}" for k in a.kernel_source]
     out.append("")
     out.append(f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s} {'pct':>6s}")
     for n, v in sorted(by.items(), key=lambda kv: -sum(kv[1])):
@@ -223,6 +225,7 @@ def main(argv=None):
     t = sub.add_parser("trace")
     t.add_argument("csv")
     t.add_argument("--grid", action="append", default=[])
+    t.add_argument("--kernel-source", action="append", default=[], choices=sorted(SOURCES))
     c = sub.add_parser("counters")
     c.add_argument("passes", nargs="+", help="TAG=counter_collection.csv, one per pass")
     c.add_argument("--kernel", required=True, help="substring of the kernel name")
