@@ -85,6 +85,52 @@ struct TileAttn {
     bool* forked;           // set once any work of the call went to the side stream
 };
 
+// One stack call's use of the side stream: an F layer's tile attentions (and, with room for
+// two score tiles in the workspace, its tile top-k) run there, forked from the caller's
+// stream by events of the call's own; join() makes the caller's stream wait for them.  The
+// caller joins after every F layer and on every return once work went there (an error
+// part-way through a layer included), so no work of the call is left running unordered
+// with its stream.
+class SideWork {
+public:
+    // ws / ws_bytes: the call's workspace; tile_bytes: one score tile (a second one after it
+    // moves the tile top-k to the side stream as well; tile_bytes 0: never a second tile)
+    SideWork(void* ws, size_t ws_bytes, size_t tile_bytes) {
+        side_ = side_stream();
+        for (int i = 0; side_ && i < 4; ++i)
+            if (hipEventCreateWithFlags(&ev_[i], hipEventDisableTiming) != hipSuccess) side_ = nullptr;
+        tile2_ = side_ && tile_bytes > 0 && ws_bytes >= 2 * tile_bytes
+                     ? reinterpret_cast<float*>(static_cast<char*>(ws) + tile_bytes) : nullptr;
+    }
+    ~SideWork() {
+        for (int i = 0; i < 4; ++i)
+            if (ev_[i]) (void)hipEventDestroy(ev_[i]);
+    }
+    SideWork(const SideWork&) = delete;
+    SideWork& operator=(const SideWork&) = delete;
+    bool active() const { return side_ != nullptr; }
+    // the F layer's tile-attention hand-off, or nullptr to keep everything on the caller's stream
+    const TileAttn* tile_attn(const ic_layer& L) {
+        if (!side_) return nullptr;
+        ta_ = {L.q, L.kv, L.out, side_, ev_[0], tile2_, {ev_[2], ev_[3]}, &ntiles_, &forked_};
+        return &ta_;
+    }
+    hipError_t join(hipStream_t st) {
+        if (!forked_) return hipSuccess;
+        forked_ = false;
+        hipError_t e = hipEventRecord(ev_[1], side_);
+        return e == hipSuccess ? hipStreamWaitEvent(st, ev_[1], 0) : e;
+    }
+
+private:
+    hipStream_t side_ = nullptr;
+    hipEvent_t ev_[4] = {nullptr, nullptr, nullptr, nullptr};   // fork, join, two tile-freed events
+    float* tile2_ = nullptr;
+    int64_t ntiles_ = 0;
+    bool forked_ = false;
+    TileAttn ta_{};
+};
+
 // Sizes the kernels support; `decode` relaxes the prefill position checks, and `varlen`
 // leaves them to the per-sequence check (Lq is then the packed query count).
 ic_status check_shape(const ic_shape* sp, bool need_indexer, bool decode, bool varlen = false) {
@@ -574,44 +620,17 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
     if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
     if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
     hipStream_t st = (hipStream_t)stream;
-    // An F layer's attention runs tile by tile on a side stream, overlapping the scoring of
-    // the layer's next tile; the caller's stream waits for it before the next layer.
-    hipStream_t side = side_stream();
-    hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};   // fork, join, two tile-freed events
-    for (int i = 0; side && i < 4; ++i)
-        if (hipEventCreateWithFlags(&ev[i], hipEventDisableTiming) != hipSuccess) side = nullptr;
-    struct Events {
-        hipEvent_t* e;
-        ~Events() {
-            for (int i = 0; i < 4; ++i)
-                if (e[i]) (void)hipEventDestroy(e[i]);
-        }
-    } release{ev};
     // With room for two score tiles, a tile's top-k also leaves the caller's stream.
-    const size_t tile_bytes = (size_t)round_up((int64_t)indexer_ws(*shape), 256);
-    float* tile2 = side && ws_bytes >= 2 * tile_bytes
-                       ? reinterpret_cast<float*>(static_cast<char*>(ws) + tile_bytes) : nullptr;
-    int64_t ntiles = 0;
-    bool forked = false;
-    // Joins the side stream back into the caller's: after every F layer, and on every
-    // return once work went there (an error part-way through a layer included), so no
-    // work of the call is left running on the library's stream unordered with `stream`.
-    auto join = [&]() -> hipError_t {
-        if (!forked) return hipSuccess;
-        forked = false;
-        hipError_t e = hipEventRecord(ev[1], side);
-        return e == hipSuccess ? hipStreamWaitEvent(st, ev[1], 0) : e;
-    };
+    SideWork side(ws, ws_bytes, (size_t)round_up((int64_t)indexer_ws(*shape), 256));
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;                       // the index cache starts empty on every call
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const bool full = pattern[l] == 'F' || pattern[l] == '1';
         if (full) {
-            const TileAttn ta = {L.q, L.kv, L.out, side, ev[0], tile2, {ev[2], ev[3]}, &ntiles, &forked};
-            r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side ? &ta : nullptr);
+            r = run_indexer_topk(*shape, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side.tile_attn(L));
             if (r != IC_OK) {
-                (void)join();                  // keeps the failure's own status and message
+                (void)side.join(st);           // keeps the failure's own status and message
                 return r;
             }
             cached = true;
@@ -619,8 +638,8 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
         } else if (!cached) {
             return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         }
-        if (full && side) {                    // join: the layer's tile attentions are done
-            hipError_t e = join();
+        if (full && side.active()) {           // join: the layer's tile attentions are done
+            hipError_t e = side.join(st);
             if (e != hipSuccess) return hip_fail(e, "stream join");
         } else {
             r = run_attn(*shape, shape->Lq, L.q, L.kv, idx_cache, L.out, 1, nullptr, st);
@@ -671,16 +690,29 @@ ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_l
     // own entries of the probe rows: every probe row is full once it sees k keys
     int64_t own = 0;
     for (int j = 0; j < d.P; ++j) own += std::min<int64_t>(s.k, (int64_t)s.pos0 + d.t0 + (int64_t)j * probe_stride + 1);
+    // As in ic_run_stack, an F layer's tile attentions run beside its next tiles' scoring (one
+    // score tile here: the rest of the workspace is the probe's, so the top-k stays put).
+    SideWork side(ws, 0, 0);
     ic_stats cnt = {0, 0, 0, 0};
     bool cached = false;
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const bool full = pattern[l] == 'F' || pattern[l] == '1';
         if (full) {
-            r = run_indexer_topk(s, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles);
-            if (r != IC_OK) return r;
+            r = run_indexer_topk(s, L.q_I, L.w, L.k_I, idx_cache, ws, st, &cnt.score_tiles, side.tile_attn(L));
+            if (r != IC_OK) {
+                (void)side.join(st);
+                return r;
+            }
             cached = true;
             ++cnt.indexer_calls;
+            if (side.active()) {               // the layer's tile attentions are done
+                hipError_t e = side.join(st);
+                if (e != hipSuccess) return hip_fail(e, "stream join");
+                ++cnt.attn_calls;
+                ++cnt.layers;
+                continue;
+            }
         } else if (!cached) {
             return fail(IC_ERR_NO_CACHED_INDICES, "no cached indices: S layer before any F layer");
         } else if (L.q_I) {
