@@ -149,3 +149,21 @@ def test_topk_multi_million_key_rows(kind):
         m = np.abs(rng.standard_normal((rows, n0 + rows)).astype(np.float32)) * 30
         m[:, 3::11] = np.float32(120.0)               # ties straddling the k-th key
     _run(m, n0, 4096)
+
+
+@pytest.mark.parametrize("n_last,kind", [(40000, "random"), (65536, "threshold_tie")])
+def test_topk_many_streamed_rows(n_last, kind):
+    """Launches of 1024 rows of 40K-64K keys stream 512-thread blocks, four rows per CU;
+    every 8th row, the first and the last are checked against the oracle."""
+    rng = np.random.default_rng(n_last)
+    rows, k = 1024, 2048
+    first = n_last - rows + 1
+    if kind == "random":
+        m = (rng.standard_normal((rows, n_last)) * 50).astype(np.float32)
+    else:
+        m = np.abs(rng.standard_normal((rows, n_last)).astype(np.float32)) * 30
+        m[:, 3::11] = np.float32(40.0)
+    got = ic.topk_rows(torch.from_numpy(m).cuda(), first, k).cpu().numpy()
+    for r in sorted(set(range(0, rows, 8)) | {rows - 1}):
+        want = O.topk_row(m[r, :first + r], k)
+        assert np.array_equal(got[r], want), f"row {r} (n={first + r})"
