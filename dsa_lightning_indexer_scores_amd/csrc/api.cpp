@@ -253,7 +253,12 @@ ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_
                                const int32_t* run_if = nullptr, const TileAttn* ta = nullptr, int b = 0) {
     const int chunk = chunk_of(s);
     const bool two = ta && ta->tile2;                       // top-k and attention both on the side stream
-    for (int c0 = 0; c0 < Lq; c0 += chunk) {
+    // Tiles are independent, so they run last first: the work left after the final tile is
+    // scored (that tile's top-k and attention) is then the shortest rows' (stack32k,
+    // alternating runs, identical indices: 37.3-37.6 against 37.6-38.1 ms per step).
+    const int nchunks = (int)(((int64_t)Lq + chunk - 1) / chunk);
+    for (int ci = nchunks - 1; ci >= 0; --ci) {
+        const int c0 = ci * chunk;
         const int nq = std::min(chunk, Lq - c0);
         const int64_t stride = round_up((int64_t)pos0 + c0 + nq, 4);
         float* tile = static_cast<float*>(ws);
