@@ -349,6 +349,8 @@ __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     float scale_log2, const ic_seq_group grp) {
     using G = DmaGeom<D>;
     constexpr int CI = G::ICH / 64;                      // DMA instructions per idx chunk
+    // the in-flight counts waited for below (NI, CI and their sum) must be exact vmcnt values
+    static_assert(G::NI % 4 == 0 && CI % 4 == 0 && G::NI + CI <= 28, "wait_vm_n takes multiples of 4 below 32");
     __shared__ __attribute__((aligned(1024))) uint8_t stage_all[DMA_NW][2][G::SB];   // K, V
     __shared__ __attribute__((aligned(16))) int32_t ring_all[DMA_NW][2 * G::ICH];
     const int lane = threadIdx.x & 63;

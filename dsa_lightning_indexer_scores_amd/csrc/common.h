@@ -80,7 +80,8 @@ __device__ __forceinline__ void dma_b32(const void* base, uint32_t voff, uint32_
 }
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory"); }
-// vmcnt(n) for a wave-uniform n that is a multiple of 4 up to 32.
+// vmcnt(n) for a wave-uniform n that is a multiple of 4 below 32; any other n waits for
+// every load (always safe: it only waits longer than asked).
 __device__ __forceinline__ void wait_vm_n(int n) {
     switch (n) {
     case 0: wait_vm<0>(); break;
@@ -91,7 +92,7 @@ __device__ __forceinline__ void wait_vm_n(int n) {
     case 20: wait_vm<20>(); break;
     case 24: wait_vm<24>(); break;
     case 28: wait_vm<28>(); break;
-    default: wait_vm<32>(); break;
+    default: wait_vm<0>(); break;
     }
 }
 // Slot permutation of a staged K or V half row r (only r % 16 matters): 16-byte slot j holds

@@ -119,15 +119,17 @@ constexpr int TOPK_MANY_ROWS = 1024;     // launches of this many rows use the s
 // 512 x 64 at two to four rows per CU 0.083-0.19, 0.92 ms in all against 1.19.  (At the
 // cap 1024 x 24 spills five registers and still beats 768 x 32 and 512 x 48; 1024 x 32
 // capped spills more and loses to 512 x 64.)  The few-row shapes (decode) keep their
-// registers: with one row per CU, a row's latency is what counts.
-constexpr int topk_waves_per_eu(int NT, int EPT, int MODE) {
+// registers: with one row per CU, a row's latency is what counts.  Streamed 512 x 32 rows
+// read with scalar (unaligned) loads need more than 64 VGPRs and run two per CU instead.
+constexpr int topk_waves_per_eu(int NT, int EPT, bool VEC, bool STREAM, int MODE) {
     return MODE != TOPK_ROWS ? 1
+         : (NT == 512 && EPT == 32 && STREAM && !VEC) ? 4
          : ((NT == 1024 && EPT <= 16) || (NT == 512 && EPT <= 32) || (NT == 1024 && EPT == 24)) ? 8
          : (NT == 512 && EPT == 64) ? 4 : 1;
 }
 
 template <int NT, int EPT, bool VEC, bool STREAM, int MODE>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_per_eu(NT, EPT, MODE)))) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(topk_waves_per_eu(NT, EPT, VEC, STREAM, MODE)))) void topk_kernel(const float* __restrict__ scores, int64_t row_stride,
                                                   int first_len, const int32_t* __restrict__ seq_len, int k,
                                                   int32_t* __restrict__ idx, int max_len, int seg, int nseg,
                                                   const int32_t* __restrict__ cand, int cand_len,

@@ -151,9 +151,10 @@ def test_topk_multi_million_key_rows(kind):
     _run(m, n0, 4096)
 
 
-@pytest.mark.parametrize("n_last,kind", [(40000, "random"), (65536, "threshold_tie")])
+@pytest.mark.parametrize("n_last,kind", [(40000, "random"), (65536, "threshold_tie"), (40001, "random")])
 def test_topk_many_streamed_rows(n_last, kind):
-    """Launches of 1024 rows of 40K-64K keys stream 512-thread blocks, four rows per CU;
+    """Launches of 1024 rows of 40K-64K keys stream 512-thread blocks, four rows per CU
+    (an odd row stride, 40001, takes the unaligned scalar-load variant, two rows per CU);
     every 8th row, the first and the last are checked against the oracle."""
     rng = np.random.default_rng(n_last)
     rows, k = 1024, 2048
