@@ -40,10 +40,10 @@
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    work and return; nothing synchronises the host.  All of a call's work is
  *    ordered on `stream`: work after the call on `stream` sees its results.
- *    ic_run_stack also runs part of its work on a second stream of the
- *    library's (one per device, default priority, created on first use),
- *    forked from and joined back to `stream` with events inside the call, so
- *    the call stays capturable in a HIP graph.  Concurrent calls on one device
+ *    ic_run_stack and ic_run_stack_dynamic also run part of their work on a
+ *    second stream of the library's (one per device, default priority,
+ *    created on first use), forked from and joined back to `stream` with
+ *    events inside the call, so the call stays capturable in a HIP graph.  Concurrent calls on one device
  *    share that stream: they may wait on each other there, never reorder.
  *  - Arguments are validated before any launch; a call that fails validation
  *    returns a non-zero ic_status, launches nothing and leaves outputs
@@ -246,7 +246,9 @@ IC_API ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, cons
  * and recall [n_layers, B] fp32 (device, each may be NULL) receive the
  * decision and hit / own of every probed (layer, sequence); entries of layers
  * without a probe are left untouched.  The workspace is
- * ic_run_stack_dynamic_ws(shape, probe_stride) bytes. */
+ * ic_run_stack_dynamic_ws(shape, probe_stride) bytes.  As in ic_run_stack, an F
+ * layer's own attention runs score tile by score tile on the library's second
+ * stream (its top-k stays on `stream`: the workspace holds one score tile). */
 IC_API ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_layer* layers,
                                       const ic_shape* shape, int32_t probe_stride, double tau, int32_t* idx_cache,
                                       int32_t* refreshed, float* recall, void* ws, size_t ws_bytes,
