@@ -410,8 +410,10 @@ __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
     for (int i = 0; i < G::NI; ++i)
         cof[i] = ((uint32_t)(lane % G::NCH) ^ G::swz(G::RPI * i + lane / G::NCH)) * 16u;
     uint32_t roff[G::NI];                                // row offsets of the step being fetched
-    // Row offsets of step s from the ring (entries outside [0, Lk) fetch row Lk - 1) and its
-    // valid keys as a wave-uniform 32-bit mask (entry in [0, Lk) and inside the idx row).
+    // Row offsets of step s from the ring and its valid keys as a wave-uniform 32-bit mask
+    // (entry in [0, Lk) and inside the idx row).  Entries outside [0, Lk) fetch row 0, a key
+    // every query sees: a masked entry's probability is 0, and 0 times its V row must stay
+    // 0, which rows past the context (capacity that may hold anything) would not guarantee.
     auto offsets = [&](int s) -> uint32_t {
         const int32_t* ir = ring + ((s / G::SPC) & 1) * G::ICH + (s % G::SPC) * KT;
         const int ev = ir[lane & 31];
@@ -419,7 +421,7 @@ __global__ __launch_bounds__(DMA_NW * 64) __attribute__((amdgpu_waves_per_eu(2))
 #pragma unroll
         for (int i = 0; i < G::NI; ++i) {
             const uint32_t v = (uint32_t)ir[G::RPI * i + lane / G::NCH];
-            roff[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)G::RB + cof[i];
+            roff[i] = (v < (uint32_t)Lk ? v : 0u) * (uint32_t)G::RB + cof[i];
         }
         return __builtin_amdgcn_readfirstlane(vm);
     };

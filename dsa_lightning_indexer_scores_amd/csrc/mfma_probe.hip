@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const int4* __restrict
 // halves of the named rows (row_bytes = 2 * HB) go straight into a K and a V stage of
 // the wave's LDS (global_load_lds_dwordx4, 64 lanes x 16 bytes), K(s+1) issued once K(s)
 // has landed and V(s+1) once V(s) has, and the idx row reaches LDS through a ring of two
-// 256-entry chunks the same way.  Entries outside [0, Lk) read row Lk - 1; steps past the
+// 256-entry chunks the same way.  Entries outside [0, Lk) read row 0; steps past the
 // row's last real entry are not run.  One LDS word per lane is written to out at the end.
 template <int HB>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restrict__ kv, const int32_t* __restrict__ idx,
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(const uint8_t* __restr
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const uint32_t v = (uint32_t)ir[RPI * i + lane / NCH];
-            roff[i] = min(v, (uint32_t)(Lk - 1)) * (uint32_t)(2 * HB) + (uint32_t)(lane % NCH) * 16u;
+            roff[i] = (v < (uint32_t)Lk ? v : 0u) * (uint32_t)(2 * HB) + (uint32_t)(lane % NCH) * 16u;
         }
     };
     auto issue_half = [&](uint32_t dst, uint32_t half_off) {
