@@ -115,3 +115,27 @@ def test_attention_entries_outside_the_cache_are_skipped():
     skipped = np.where((idx >= 0) & (idx < Lk), idx, -1)
     ref = O.sparse_attn(dec(lay["q"][0])[1:], dec(lay["kv"][0]), skipped[1:])
     assert attn_rel_err(got[1:], ref) <= ATTN_TOL
+
+
+def test_distill_ignores_rows_past_the_context():
+    """The distillation loss over the GPU's own top-k, plus entries naming poisoned rows
+    (visible to no query), which are ignored like any entry outside the visible keys."""
+    B, Lq, pos0, H_I, d_I, H, d, k, extra = 1, 160, 40, 8, 64, 16, 128, 48, 32
+    Lk = pos0 + Lq + extra
+    n_ctx = [pos0 + Lq]
+    lay = [_layer(B, Lq, Lk, n_ctx, H_I, d_I, H, d, "bf16", 970 + j, full=(j == 0)) for j in range(3)]
+    g = [{kk: v.cuda() for kk, v in l.items()} for l in lay]
+    idx = ic.indexer_topk(g[0]["q_I"], g[0]["w"], g[0]["k_I"], k, pos0=pos0).cpu().numpy()
+    idx[0, ::3, -1] = Lk - 1                             # a poisoned row, past every query's keys
+    kl, _ = ic.distill_kl(g[0]["q_I"], g[0]["w"], g[0]["k_I"], torch.from_numpy(idx).cuda(),
+                          [l["q"] for l in g], [l["kv"] for l in g], pos0=pos0, chunk=64)
+    torch.cuda.synchronize()
+    got = kl.cpu().numpy()[0]
+    assert np.isfinite(got).all()
+    clean = np.where(idx[0] >= n_ctx[0], -1, idx[0])
+    ref = O.distill_kl(dec(lay[0]["q_I"])[0], dec(lay[0]["w"])[0], dec(lay[0]["k_I"])[0], clean,
+                       [dec(l["q"])[0] for l in lay], [dec(l["kv"])[0] for l in lay], pos0=pos0)
+    err = np.abs(got - ref)
+    bound = 2e-3 + 1e-4 * np.abs(ref)
+    summary("capacity distill", {"worst_err_over_bound": float((err / bound).max())})
+    assert np.all(err <= bound)
