@@ -11,6 +11,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <cstdarg>
 #include <cstdio>
 #include <climits>
@@ -246,6 +247,22 @@ ic_status check_ws(const void* ws, size_t have, size_t need) {
 
 size_t elem_bytes(int dtype) { return dtype == IC_FP8_E4M3 ? 1 : 2; }
 
+// Tensor pointers must be aligned to what the kernels load at once: 16 bytes for q_I, k_I,
+// q, kv and out (vector and LDS-DMA loads of row pieces), 4 bytes for the fp32 and int32
+// arrays.  Every torch allocation is; a view starting at an odd element may not be.  NULL
+// entries are left to the callers' own checks.
+struct AlignReq {
+    const void* p;
+    const char* name;
+    unsigned align;
+};
+ic_status check_aligned(std::initializer_list<AlignReq> reqs) {
+    for (const AlignReq& a : reqs)
+        if (a.p && reinterpret_cast<uintptr_t>(a.p) % a.align != 0)
+            return fail(IC_ERR_ARG, "%s must be %u-byte aligned", a.name, a.align);
+    return IC_OK;
+}
+
 // a1 + a2 for one sequence: its Lq queries at positions pos0.. against its keys, in score
 // tiles of <= chunk queries, then top-k into idx [Lq, k].
 ic_status run_indexer_topk_one(const ic_shape& s, int Lq, int pos0, const uint8_t* qb, const float* wb,
@@ -391,6 +408,10 @@ ic_status check_stack(const char* pattern, int32_t n_layers, const ic_layer* lay
         }
         if (!layers[l].q || !layers[l].kv || !layers[l].out)
             return fail(IC_ERR_ARG, "layer %d needs q, kv and out", l);
+        const ic_layer& L = layers[l];
+        if (ic_status r = check_aligned({{L.q_I, "q_I", 16}, {L.k_I, "k_I", 16}, {L.w, "w", 4}, {L.q, "q", 16},
+                                         {L.kv, "kv", 16}, {L.out, "out", 16}}))
+            return r;
     }
     return IC_OK;
 }
@@ -515,6 +536,7 @@ ic_status ic_indexer_topk(const ic_shape* shape, const void* q_I, const float* w
     ic_status r = check_shape(shape, true, false);
     if (r != IC_OK) return r;
     if (!q_I || !w || !k_I || !idx) return fail(IC_ERR_ARG, "q_I, w, k_I and idx must be non-NULL");
+    if ((r = check_aligned({{q_I, "q_I", 16}, {k_I, "k_I", 16}, {w, "w", 4}, {idx, "idx", 4}})) != IC_OK) return r;
     if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
     return run_indexer_topk(*shape, q_I, w, k_I, idx, ws, (hipStream_t)stream, nullptr);
 }
@@ -524,6 +546,8 @@ ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float*
     ic_status r = check_shape(shape, true, false);
     if (r != IC_OK) return r;
     if (!q_I || !w || !k_I || !scores) return fail(IC_ERR_ARG, "q_I, w, k_I and scores must be non-NULL");
+    if ((r = check_aligned({{q_I, "q_I", 16}, {k_I, "k_I", 16}, {w, "w", 4}, {scores, "scores", 4}})) != IC_OK)
+        return r;
     const ic_shape& s = *shape;
     if (row_stride < (int64_t)s.pos0 + s.Lq) return fail(IC_ERR_SHAPE, "row_stride %lld < pos0 + Lq", (long long)row_stride);
     const size_t eb = elem_bytes(s.idx_dtype);
@@ -549,6 +573,7 @@ ic_status ic_indexer_scores(const ic_shape* shape, const void* q_I, const float*
 ic_status ic_topk_rows(const float* scores, int64_t row_stride, int32_t rows, int32_t first_len, int32_t k,
                        int32_t* idx, void* stream) {
     if (!scores || !idx) return fail(IC_ERR_ARG, "scores and idx must be non-NULL");
+    if (ic_status r = check_aligned({{scores, "scores", 4}, {idx, "idx", 4}})) return r;
     if (rows < 1 || first_len < 1 || k < 1 || k > kMaxK)
         return fail(IC_ERR_SHAPE, "need rows >= 1, first_len >= 1, 1 <= k <= %d", kMaxK);
     if ((int64_t)first_len + rows - 1 > row_stride)
@@ -583,6 +608,7 @@ size_t ic_topk_rows_seq_ws(int32_t rows, int32_t max_len, int32_t k) {
 ic_status ic_topk_rows_seq(const float* scores, int64_t row_stride, int32_t rows, const int32_t* seq_len,
                            int32_t max_len, int32_t k, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     if (!scores || !seq_len || !idx) return fail(IC_ERR_ARG, "scores, seq_len and idx must be non-NULL");
+    if (ic_status r = check_aligned({{scores, "scores", 4}, {seq_len, "seq_len", 4}, {idx, "idx", 4}})) return r;
     if (rows < 1 || max_len < 1 || k < 1 || k > kMaxK)
         return fail(IC_ERR_SHAPE, "need rows >= 1, max_len >= 1, 1 <= k <= %d", kMaxK);
     if (max_len > row_stride)
@@ -614,6 +640,7 @@ ic_status ic_sparse_attn(const ic_shape* shape, const void* q, const void* kv, c
     ic_status r = check_shape(shape, false, false);
     if (r != IC_OK) return r;
     if (!q || !kv || !idx || !out) return fail(IC_ERR_ARG, "q, kv, idx and out must be non-NULL");
+    if ((r = check_aligned({{q, "q", 16}, {kv, "kv", 16}, {out, "out", 16}, {idx, "idx", 4}})) != IC_OK) return r;
     return run_attn(*shape, shape->Lq, q, kv, idx, out, 1, nullptr, (hipStream_t)stream);
 }
 
@@ -623,6 +650,7 @@ ic_status ic_run_stack(const char* pattern, int32_t n_layers, const ic_layer* la
     if (r != IC_OK) return r;
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if ((r = check_aligned({{idx_cache, "idx_cache", 4}})) != IC_OK) return r;
     if ((r = check_ws(ws, ws_bytes, indexer_ws(*shape))) != IC_OK) return r;
     hipStream_t st = (hipStream_t)stream;
     // With room for two score tiles, a tile's top-k also leaves the caller's stream.
@@ -674,8 +702,10 @@ ic_status ic_run_stack_dynamic(const char* pattern, int32_t n_layers, const ic_l
     if (r != IC_OK) return r;
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if ((r = check_aligned({{idx_cache, "idx_cache", 4}})) != IC_OK) return r;
     if (probe_stride < 1) return fail(IC_ERR_ARG, "probe_stride must be >= 1 (got %d)", probe_stride);
     if (!(tau >= 0.0 && tau <= 2.0)) return fail(IC_ERR_ARG, "tau must be in [0, 2] (got %g)", tau);
+    if ((r = check_aligned({{refreshed, "refreshed", 4}, {recall, "recall", 4}})) != IC_OK) return r;
     for (int l = 0; l < n_layers; ++l) {
         const ic_layer& L = layers[l];
         const int have = (L.q_I != nullptr) + (L.w != nullptr) + (L.k_I != nullptr);
@@ -785,6 +815,7 @@ ic_status ic_run_stack_varlen(const char* pattern, int32_t n_layers, const ic_la
     if (r != IC_OK) return r;
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!idx_cache) return fail(IC_ERR_ARG, "idx_cache is NULL");
+    if ((r = check_aligned({{idx_cache, "idx_cache", 4}})) != IC_OK) return r;
     if (!q_len || !pos0) return fail(IC_ERR_ARG, "q_len and pos0 must be non-NULL host arrays");
     const ic_shape& s = *shape;
     int64_t total = 0;
@@ -936,6 +967,7 @@ ic_status ic_decode_step(const char* pattern, int32_t n_layers, const ic_layer* 
     if (r != IC_OK) return r;
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!seq_len || !idx_cache) return fail(IC_ERR_ARG, "seq_len and idx_cache must be non-NULL");
+    if ((r = check_aligned({{seq_len, "seq_len", 4}, {idx_cache, "idx_cache", 4}})) != IC_OK) return r;
     if ((r = check_ws(ws, ws_bytes, decode_ws(*shape))) != IC_OK) return r;
     return decode_step_run(pattern, n_layers, layers, *shape, seq_len, idx_cache, ws, stats, (hipStream_t)stream);
 }
@@ -946,6 +978,7 @@ ic_status ic_decode_step_static(const char* pattern, int32_t n_layers, const ic_
     if (r != IC_OK) return r;
     if ((r = check_stack(pattern, n_layers, layers)) != IC_OK) return r;
     if (!seq_len || !idx_cache) return fail(IC_ERR_ARG, "seq_len and idx_cache must be non-NULL");
+    if ((r = check_aligned({{seq_len, "seq_len", 4}, {idx_cache, "idx_cache", 4}})) != IC_OK) return r;
     const size_t need = decode_ws(*shape);
     if (need > (size_t)IC_DECODE_STATIC_SCRATCH_BYTES)
         return fail(IC_ERR_WORKSPACE, "this decode shape needs %zu bytes of scratch; the static scratch holds %zu "
@@ -961,6 +994,9 @@ ic_status ic_decode_indexer_scores(const ic_shape* shape, const void* q_I, const
     if (r != IC_OK) return r;
     if (!q_I || !w || !k_I || !seq_len || !scores)
         return fail(IC_ERR_ARG, "q_I, w, k_I, seq_len and scores must be non-NULL");
+    if ((r = check_aligned({{q_I, "q_I", 16}, {k_I, "k_I", 16}, {w, "w", 4}, {seq_len, "seq_len", 4},
+                            {scores, "scores", 4}})) != IC_OK)
+        return r;
     const ic_shape& s = *shape;
     if (row_stride < s.Lk) return fail(IC_ERR_SHAPE, "row_stride %lld < Lk %d", (long long)row_stride, s.Lk);
     ic_indexer_decode_args a;
@@ -985,6 +1021,7 @@ ic_status ic_decode_attn(const ic_shape* shape, const void* q, const void* kv, c
     ic_status r = check_shape(shape, false, true);
     if (r != IC_OK) return r;
     if (!q || !kv || !idx || !out) return fail(IC_ERR_ARG, "q, kv, idx and out must be non-NULL");
+    if ((r = check_aligned({{q, "q", 16}, {kv, "kv", 16}, {out, "out", 16}, {idx, "idx", 4}})) != IC_OK) return r;
     const ic_shape& s = *shape;
     const int nsplit = decode_splits(s);
     if ((r = check_ws(ws, ws_bytes, sparse_attn_ws_bytes(s.B, s.H, s.d, nsplit))) != IC_OK) return r;
@@ -997,6 +1034,9 @@ ic_status ic_index_overlap(const int32_t* idx_a, const int32_t* idx_b, int64_t r
     if (rows < 0 || rows > INT32_MAX || k < 1 || k > kMaxK)
         return fail(IC_ERR_SHAPE, "need 0 <= rows <= 2^31-1 and 1 <= k <= %d", kMaxK);
     if (means && (!jaccard || !recall)) return fail(IC_ERR_ARG, "means needs jaccard and recall");
+    if (ic_status r = check_aligned({{idx_a, "idx_a", 4}, {idx_b, "idx_b", 4}, {inter, "inter", 4},
+                                     {jaccard, "jaccard", 4}, {recall, "recall", 4}, {means, "means", 4}}))
+        return r;
     hipError_t e = launch_overlap(idx_a, idx_b, rows, k, inter, jaccard, recall, means, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "overlap launch");
     return IC_OK;
@@ -1012,8 +1052,13 @@ ic_status ic_distill_kl(const ic_shape* shape, const void* q_I, const float* w, 
     if (n_served < 1 || n_served > IC_DISTILL_MAX_SERVED)
         return fail(IC_ERR_ARG, "n_served must be in 1..%d (got %d)", IC_DISTILL_MAX_SERVED, n_served);
     if (!q || !kv) return fail(IC_ERR_ARG, "q and kv must be host arrays of n_served device pointers");
-    for (int j = 0; j < n_served; ++j)
+    for (int j = 0; j < n_served; ++j) {
         if (!q[j] || !kv[j]) return fail(IC_ERR_ARG, "served layer %d has a NULL q or kv", j);
+        if ((st = check_aligned({{q[j], "served q", 16}, {kv[j], "served kv", 16}})) != IC_OK) return st;
+    }
+    if ((st = check_aligned({{q_I, "q_I", 16}, {k_I, "k_I", 16}, {w, "w", 4}, {idx, "idx", 4}, {kl, "kl", 4},
+                             {kl_mean, "kl_mean", 4}})) != IC_OK)
+        return st;
     if ((st = check_ws(ws, ws_bytes, indexer_ws(s))) != IC_OK) return st;
     hipStream_t hs = (hipStream_t)stream;
     const size_t eb = elem_bytes(s.idx_dtype);

@@ -37,6 +37,10 @@
  *    ic_workspace_size() bytes, 256-byte aligned.
  *  - Tensors are dense and row-major in the layouts given below.
  *      bf16 = IEEE binary32 upper half; fp8 = OCP E4M3FN byte codes.
+ *    q_I, k_I, q, kv and out (and distillation's served q / kv) must be 16-byte
+ *    aligned, the fp32 and int32 arrays 4-byte aligned: every torch allocation
+ *    is, while a view that starts at an odd element may not be.  A misaligned
+ *    pointer fails with IC_ERR_ARG.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls enqueue
  *    work and return; nothing synchronises the host.  All of a call's work is
  *    ordered on `stream`: work after the call on `stream` sees its results.

@@ -261,6 +261,40 @@ int main(void) {
     EXPECT(ic_distill_kl(&b, FAKE, W, FAKE, I, 2, ptrs, ptrs, KL, NULL, FAKE_WS, BIG, NULL), IC_ERR_DTYPE);
     EXPECT(ic_distill_kl(&s, FAKE, W, FAKE, I, 2, ptrs, ptrs, KL, NULL, FAKE_WS, 16, NULL), IC_ERR_WORKSPACE);
 
+    /* misaligned tensor pointers (views starting at an odd element): 16 bytes for q_I, k_I,
+     * q, kv and out, 4 for the fp32 / int32 arrays */
+    const uintptr_t odd2 = 0x1002, odd8 = 0x1008;
+    make_layers("FSSS");
+    layers[1].kv = (const void*)odd2;
+    EXPECT(ic_run_stack("FSSS", 4, layers, &s, I, FAKE_WS, BIG, NULL, NULL), IC_ERR_ARG);
+    make_layers("FSSS");
+    layers[0].q_I = (const void*)odd8;
+    EXPECT(ic_run_stack("FSSS", 4, layers, &s, I, FAKE_WS, BIG, NULL, NULL), IC_ERR_ARG);
+    make_layers("FSSS");
+    layers[0].w = (const float*)odd2;
+    EXPECT(ic_run_stack("FSSS", 4, layers, &s, I, FAKE_WS, BIG, NULL, NULL), IC_ERR_ARG);
+    make_layers("FSSS");
+    layers[3].out = (void*)odd8;
+    EXPECT(ic_decode_step("FSSS", 4, layers, &d, (const int32_t*)FAKE, I, FAKE_WS, BIG, NULL, NULL), IC_ERR_ARG);
+    EXPECT(ic_run_stack("FSSS", 4, make_layers("FSSS"), &s, (int32_t*)odd2, FAKE_WS, BIG, NULL, NULL), IC_ERR_ARG);
+    EXPECT(ic_decode_step("FSSS", 4, make_layers("FSSS"), &d, (const int32_t*)odd2, I, FAKE_WS, BIG, NULL, NULL),
+           IC_ERR_ARG);
+    EXPECT(ic_indexer_topk(&s, FAKE, (const float*)FAKE, (const void*)odd8, I, FAKE_WS, BIG, NULL), IC_ERR_ARG);
+    EXPECT(ic_indexer_scores(&s, FAKE, (const float*)FAKE, FAKE, (float*)odd2, 512, NULL), IC_ERR_ARG);
+    EXPECT(ic_sparse_attn(&s, FAKE, FAKE, (const int32_t*)FAKE, (void*)odd2, NULL, 0, NULL), IC_ERR_ARG);
+    EXPECT(ic_decode_attn(&d, (const void*)odd8, FAKE, (const int32_t*)FAKE, FAKE, FAKE_WS, BIG, NULL), IC_ERR_ARG);
+    EXPECT(ic_decode_indexer_scores(&d, FAKE, (const float*)FAKE, (const void*)odd2, (const int32_t*)FAKE,
+                                    (float*)FAKE, 65600, NULL), IC_ERR_ARG);
+    EXPECT(ic_topk_rows((const float*)(uintptr_t)0x1001, 100, 4, 10, 8, I, NULL), IC_ERR_ARG);
+    EXPECT(ic_topk_rows_seq((const float*)FAKE, 100, 4, (const int32_t*)odd2, 100, 8, I, NULL, 0, NULL), IC_ERR_ARG);
+    EXPECT(ic_index_overlap((const int32_t*)odd2, (const int32_t*)FAKE, 4, 8, NULL, NULL, NULL, NULL, NULL),
+           IC_ERR_ARG);
+    const void* odd_kv[2] = {FAKE, (const void*)odd8};
+    EXPECT(ic_distill_kl(&s, FAKE, W, FAKE, I, 2, ptrs, odd_kv, KL, NULL, FAKE_WS, BIG, NULL), IC_ERR_ARG);
+    EXPECT(ic_distill_kl(&s, FAKE, W, FAKE, I, 2, ptrs, ptrs, (float*)odd2, NULL, FAKE_WS, BIG, NULL), IC_ERR_ARG);
+    EXPECT(ic_run_stack_dynamic("FSSS", 4, make_layers("FSSS"), &s, 16, 0.5, I, (int32_t*)odd2, NULL, FAKE_WS, BIG,
+                                NULL, NULL), IC_ERR_ARG);
+
     if (failures) fprintf(stderr, "%d unexpected results\n", failures);
     else printf("all argument checks behaved\n");
     return failures ? 1 : 0;
