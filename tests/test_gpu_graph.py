@@ -1,5 +1,8 @@
-"""A decode step captured in a HIP graph and replayed: every replay, with new inputs
-copied into the static buffers and eager work in between, must equal the eager call."""
+"""HIP graphs and streams: a decode step and a prefill stack (its side-stream tile work
+included) captured in HIP graphs and replayed, every replay, with new inputs copied into
+the static buffers and eager work in between, equal to the eager call; two prefill stacks
+in flight at once on two caller streams; and the one-tile workspace (every top-k on the
+caller's stream) equal to the two-tile one.  All comparisons are bitwise."""
 import pytest
 import torch
 
