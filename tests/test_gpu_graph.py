@@ -1,7 +1,8 @@
-"""HIP graphs and streams: a decode step and a prefill stack (its side-stream tile work
-included) captured in HIP graphs and replayed, every replay, with new inputs copied into
-the static buffers and eager work in between, equal to the eager call; two prefill stacks
-in flight at once on two caller streams; and the one-tile workspace (every top-k on the
+"""HIP graphs and streams: a decode step, a prefill stack (its side-stream tile work
+included), a ragged batch and a stack with drift-triggered refresh (its decisions on the
+device) captured in HIP graphs and replayed, every replay, with new inputs copied into the
+static buffers and eager work in between, equal to the eager call; two prefill stacks in
+flight at once on two caller streams; and the one-tile workspace (every top-k on the
 caller's stream) equal to the two-tile one.  All comparisons are bitwise."""
 import pytest
 import torch
@@ -140,3 +141,92 @@ def test_prefill_stack_one_tile_workspace_matches_two():
     torch.cuda.synchronize()
     assert torch.equal(res[0][1], res[1][1])
     assert all(torch.equal(a, b) for a, b in zip(res[0][0], res[1][0]))
+
+
+def _refill(lays, g):
+    """New small-integer inputs in place (the captured graph keeps the same buffers)."""
+    for lay in lays:
+        for name in ("q", "kv", "q_I", "k_I"):
+            if name in lay:
+                lay[name].copy_(torch.randint(-3, 4, lay[name].shape, generator=g, device="cuda").to(lay[name].dtype))
+        if "w" in lay:
+            lay["w"].copy_(torch.randint(0, 4, lay["w"].shape, generator=g, device="cuda").to(lay["w"].dtype))
+
+
+def test_varlen_stack_graph_replays_match_eager():
+    """run_stack_varlen (its sequence tables travel by value in the kernel arguments: one
+    group of two sequences, an empty sequence, one sequence longer than a chunk) captured in
+    a graph: every replay with new inputs equals the eager call, bitwise."""
+    q_len, pos0 = [100, 0, 37, 300], [0, 10, 200, 50]
+    B, T, Lk = len(q_len), sum(q_len), 400
+    H_I, d_I, k, H, d, chunk = 4, 32, 64, 4, 64, 128
+    pattern = "FSFS"
+    layers = []
+    for c in pattern:
+        lay = {"q": torch.zeros((T, H, d), dtype=torch.bfloat16, device="cuda"),
+               "kv": torch.zeros((B, Lk, 2, d), dtype=torch.bfloat16, device="cuda")}
+        if c == "F":
+            lay.update(q_I=torch.zeros((T, H_I, d_I), dtype=torch.bfloat16, device="cuda"),
+                       w=torch.zeros((T, H_I), dtype=torch.float32, device="cuda"),
+                       k_I=torch.zeros((B, Lk, d_I), dtype=torch.bfloat16, device="cuda"))
+        layers.append(lay)
+    g = torch.Generator(device="cuda").manual_seed(21)
+    _refill(layers, g)
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    run = lambda: ic.run_stack_varlen(pattern, layers, k, q_len, pos0, chunk=chunk, outs=outs, idx_cache=idx)
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(1, 4):
+        _refill(layers, g)
+        graph.replay()
+        torch.cuda.synchronize()
+        got = [o.clone() for o in outs]
+        got_idx = idx.clone()
+        ref_outs, ref_idx, _ = ic.run_stack_varlen(pattern, layers, k, q_len, pos0, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(got_idx, ref_idx), f"replay {rep}: idx differs"
+        for l in range(len(pattern)):
+            assert torch.equal(got[l], ref_outs[l]), f"replay {rep}: layer {l} differs"
+
+
+def test_dynamic_stack_graph_replays_follow_their_inputs():
+    """run_stack_dynamic captured in a graph.  The refresh decision stays on the device, so a
+    replay must take each layer's decision from its own inputs: replays whose first S layer
+    repeats the F layer's indexer inputs keep the cache there (its probe finds its own top-k),
+    the others refresh.  Every replay equals the eager call: outputs, cache, decisions and
+    recalls, bitwise."""
+    cfg = synth.WORKLOADS["tiny"]
+    pattern, chunk, stride, tau = "FSSS", 128, 16, 0.5
+    layers = synth.prefill_stack(cfg, device="cuda", pattern="FFFF")   # every layer can probe
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((1, cfg.L, cfg.k), dtype=torch.int32, device="cuda")
+    run = lambda: ic.run_stack_dynamic(pattern, layers, cfg.k, stride, tau, chunk=chunk, outs=outs, idx_cache=idx)
+    run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _, _, _, refreshed, recall = run()
+    g = torch.Generator(device="cuda").manual_seed(23)
+    seen = set()
+    for rep in range(1, 5):
+        _refill(layers, g)
+        if rep % 2:
+            for name in ("q_I", "w", "k_I"):
+                layers[1][name].copy_(layers[0][name])
+        graph.replay()
+        torch.cuda.synchronize()
+        got = ([o.clone() for o in outs], idx.clone(), refreshed.clone(), recall.clone())
+        ref_outs, ref_idx, _, ref_ref, ref_rec = ic.run_stack_dynamic(pattern, layers, cfg.k, stride, tau, chunk=chunk)
+        torch.cuda.synchronize()
+        assert torch.equal(got[1], ref_idx), f"replay {rep}: idx differs"
+        assert torch.equal(got[2], ref_ref), f"replay {rep}: decisions differ"
+        assert torch.equal(torch.nan_to_num(got[3], nan=-1.0), torch.nan_to_num(ref_rec, nan=-1.0))
+        for l in range(len(pattern)):
+            assert torch.equal(got[0][l], ref_outs[l]), f"replay {rep}: layer {l} differs"
+        seen.add(int(got[2][1, 0]))
+        assert int(got[2][1, 0]) == (0 if rep % 2 else 1), f"replay {rep}: layer 1 decision {int(got[2][1, 0])}"
+    assert seen == {0, 1}
