@@ -156,3 +156,38 @@ def test_decode_ragged_vs_oracle_and_prefill(dtype, dist, k):
     pre = ic.indexer_topk(q_pre, w_pre, f["k_I"][b:b + 1, :n].contiguous(), k)
     _, idx_f0, _ = ic.decode_step("F", [gpu[0]], sl, k)
     assert torch.equal(pre[0, n - 1], idx_f0[b, 0])
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_single_token_prompt_and_single_head(dtype):
+    """The smallest shapes: a one-token prompt (Lq = Lk = 1, so idx = [0, -1, ...]) and
+    one attention head (fifteen empty lanes in its head group), in prefill and in decode."""
+    H_I, d_I, H, d, k = 1, 32, 1, 64, 64
+    layers = [_rand_layer(1, 1, 1, H_I, d_I, H, d, dtype, "int3", 500 + i, full=(c == "F")) for i, c in enumerate("FS")]
+    gpu = [{kk: v.cuda() for kk, v in lay.items()} for lay in layers]
+    outs, idx_cache, _ = ic.run_stack("FS", gpu, k)
+    torch.cuda.synchronize()
+    want = np.full(k, -1, dtype=np.int32)
+    want[0] = 0
+    assert np.array_equal(idx_cache.cpu().numpy()[0, 0], want)
+    for l in range(2):
+        # one visible key: the output is that key's V row exactly (bf16 in, bf16 out)
+        v0 = layers[l]["kv"][0, 0, 1]
+        assert torch.equal(outs[l][0, 0, 0].cpu(), v0), f"layer {l}"
+    # decode: two sequences of one and three tokens, one head
+    cap = 3
+    caches = [_rand_layer(2, 1, cap, H_I, d_I, H, d, dtype, "int3", 520 + i, full=(c == "F")) for i, c in enumerate("FS")]
+    gpu = [{kk: v.cuda() for kk, v in lay.items()} for lay in caches]
+    seq_len = [1, 3]
+    outs, idx_cache, _ = ic.decode_step("FS", gpu, torch.tensor(seq_len, dtype=torch.int32, device="cuda"), k)
+    torch.cuda.synchronize()
+    ref_layers = []
+    for lay in caches:
+        r = {"q": dec(lay["q"])[:, 0], "kv": dec(lay["kv"])}
+        if "q_I" in lay:
+            r.update(q_I=dec(lay["q_I"])[:, 0], w=dec(lay["w"])[:, 0], k_I=dec(lay["k_I"]))
+        ref_layers.append(r)
+    o_ref, idx_ref, _ = O.decode_step("FS", ref_layers, seq_len, k)
+    assert np.array_equal(idx_cache.cpu().numpy()[:, 0], idx_ref[-1])
+    for l in range(2):
+        assert attn_rel_err(dec(outs[l])[:, 0], o_ref[l]) <= ATTN_TOL
