@@ -51,6 +51,7 @@ INT_CASES = [
     (1, 700, 50, 20, 128, 128, "fp8", 0),      # partial head tiles on the fp8 linear-term path
     (1, 650, 0, 48, 64, 96, "fp8", 208),
     (1, 600, 17, 33, 32, 64, "bf16", 0),
+    (1, 520, 10, 40, 32, 64, "fp8", 128),      # fp8 with d_I = 32 (zero-padded K) and four head tiles
 ]
 
 
