@@ -23,7 +23,7 @@ def _int(shape, g, lo=-3):
 
 
 @pytest.mark.parametrize("dtype", ["fp8", "bf16"])
-@pytest.mark.parametrize("H_I,d_I", [(64, 128), (20, 64), (1, 32), (40, 32)])
+@pytest.mark.parametrize("H_I,d_I", [(64, 128), (20, 64), (1, 32), (40, 32), (16, 128), (5, 64)])
 def test_decode_indexer_scores_bit_exact(dtype, H_I, d_I):
     g = torch.Generator().manual_seed(H_I * 7 + d_I)
     B, cap = 4, 3001

@@ -52,6 +52,11 @@ INT_CASES = [
     (1, 650, 0, 48, 64, 96, "fp8", 208),
     (1, 600, 17, 33, 32, 64, "bf16", 0),
     (1, 520, 10, 40, 32, 64, "fp8", 128),      # fp8 with d_I = 32 (zero-padded K) and four head tiles
+    # one head tile (H_I <= 16) at d_I = 64 and 128, both dtypes
+    (1, 300, 5, 16, 128, 64, "fp8", 0),
+    (1, 260, 0, 9, 64, 48, "fp8", 0),
+    (1, 280, 3, 12, 128, 32, "bf16", 0),
+    (1, 300, 0, 5, 64, 64, "bf16", 128),
 ]
 
 
