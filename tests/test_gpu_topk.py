@@ -89,6 +89,23 @@ def test_topk_many_rows(n_last, k, kind):
     _run(m, first, k)
 
 
+@pytest.mark.parametrize("n_last,kind", [(8192, "ties"), (16384, "random"), (24576, "threshold_tie"), (32768, "random")])
+def test_topk_many_rows_unaligned(n_last, kind):
+    """The same several-rows-per-CU shapes with an odd row stride (n_last + 1 floats), which
+    takes their scalar-load variants; every row against the oracle."""
+    rng = np.random.default_rng(n_last + 7)
+    rows, k = 1024, 2048
+    first = n_last - rows + 1
+    if kind == "ties":
+        m = rng.integers(-3, 4, size=(rows, n_last + 1)).astype(np.float32)
+    elif kind == "random":
+        m = (rng.standard_normal((rows, n_last + 1)) * 50).astype(np.float32)
+    else:
+        m = np.abs(rng.standard_normal((rows, n_last + 1)).astype(np.float32)) * 30
+        m[:, 3::11] = np.float32(40.0)
+    _run(m, first, k)
+
+
 def test_topk_k_larger_than_rows():
     m = np.random.default_rng(1).standard_normal((8, 40)).astype(np.float32)
     _run(m, 10, 64)
