@@ -60,3 +60,36 @@ def test_static_scratch_rejects_oversized_shapes():
     arr = (ic.Layer * 1)(ic.Layer(fake, fake, fake, fake, fake, fake))
     r = ic.lib().ic_decode_step_static(b"F", 1, arr, ctypes.byref(shape), fake, fake, None, None)
     assert r == ic.IC_ERR_WORKSPACE and "static scratch" in ic.last_error()
+
+
+def test_static_scratch_under_graph_capture():
+    """The static entry point captured in a HIP graph (outputs preallocated, so the capture
+    records kernel launches only) and replayed with new queries, caches and lengths: every
+    replay equals the workspace path called eagerly, bitwise."""
+    B, cap, H_I, d_I, H, d, k, pattern = 2, 900, 20, 64, 20, 64, 256, "FS"
+    layers = _decode_inputs(B, cap, H_I, d_I, H, d, "bf16", pattern, 950)
+    seq_len = torch.tensor([900, 77], dtype=torch.int32, device="cuda")
+    outs = [torch.empty_like(l["q"]) for l in layers]
+    idx = torch.empty((B, 1, k), dtype=torch.int32, device="cuda")
+    run = lambda: ic.decode_step_static(pattern, layers, seq_len, k, outs=outs, idx_cache=idx)
+    run()                                   # the first call on a device looks up the scratch address
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for rep, lens in enumerate(([450, 899], [1, 600], [900, 900])):
+        print(f"[no-alloc] graph replay {rep}: seq_len {lens}", flush=True)
+        for lay in layers:
+            for name in ("q", "kv", "q_I", "k_I", "w"):
+                if name in lay:
+                    lay[name].copy_(torch.randn(lay[name].shape, generator=g, device="cuda").to(lay[name].dtype))
+        seq_len.copy_(torch.tensor(lens, dtype=torch.int32))
+        graph.replay()
+        torch.cuda.synchronize()
+        got_o, got_i = [o.clone() for o in outs], idx.clone()
+        ref_o, ref_i, _ = ic.decode_step(pattern, layers, seq_len, k)
+        torch.cuda.synchronize()
+        assert torch.equal(got_i, ref_i), f"replay {rep}: indices differ"
+        for l in range(len(pattern)):
+            assert torch.equal(got_o[l], ref_o[l]), f"replay {rep}: layer {l} output differs"
