@@ -2,7 +2,7 @@
 included), a ragged batch and a stack with drift-triggered refresh (its decisions on the
 device) captured in HIP graphs and replayed, every replay, with new inputs copied into the
 static buffers and eager work in between, equal to the eager call; two prefill stacks in
-flight at once on two caller streams; and the one-tile workspace (every top-k on the
+flight at once on two caller streams, and from two host threads; and the one-tile workspace (every top-k on the
 caller's stream) equal to the two-tile one.  All comparisons are bitwise."""
 import pytest
 import torch
@@ -230,3 +230,44 @@ def test_dynamic_stack_graph_replays_follow_their_inputs():
         seen.add(int(got[2][1, 0]))
         assert int(got[2][1, 0]) == (0 if rep % 2 else 1), f"replay {rep}: layer 1 decision {int(got[2][1, 0])}"
     assert seen == {0, 1}
+
+
+def test_prefill_stacks_from_two_host_threads():
+    """Two host threads, each on its own stream, calling run_stack three times on their own
+    inputs at once (the library's error strings and counters are per thread; its second
+    stream and scratch lookups are created under a lock): every result equals the same call
+    made alone."""
+    import threading
+    cfg = synth.WORKLOADS["tiny"]
+    inputs = [synth.prefill_stack(cfg, device="cuda", pattern="FSSS"),
+              [{k: v.flip(1).contiguous() for k, v in lay.items()}
+               for lay in synth.prefill_stack(cfg, device="cuda", pattern="FSFS")]]
+    patterns, chunks = ("FSSS", "FSFS"), (128, 96)
+    refs = [ic.run_stack(p, lays, cfg.k, chunk=c) for p, lays, c in zip(patterns, inputs, chunks)]
+    torch.cuda.synchronize()
+    results, errors = [[], []], []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    outs, idx, stats = ic.run_stack(patterns[i], inputs[i], cfg.k, chunk=chunks[i], stream=s)
+                    results[i].append((outs, idx, stats))
+            s.synchronize()
+        except Exception as e:                                    # reported below, in the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for i in range(2):
+        assert len(results[i]) == 3
+        for outs, idx, stats in results[i]:
+            assert stats == refs[i][2]
+            assert torch.equal(idx, refs[i][1])
+            assert all(torch.equal(a, b) for a, b in zip(outs, refs[i][0]))
