@@ -5,7 +5,7 @@ operand) in a temporary copy of the oracle and runs the CPU pin suite against it
 every mutant must make a pin fail.  A line that recurs (the softmax scale, the
 S-before-F check of both stack drivers) is changed everywhere it occurs.  The repository's own oracle is never modified.
 
-    python tests/mutate_oracle.py
+    python tests/mutate_oracle.py [mutant ...]      (all mutants when none is named)
 """
 import os
 import shutil
@@ -53,13 +53,29 @@ MUTANTS = {
     # dynamic refresh
     "refresh_inclusive": ("if hit < tau * own:", "if hit <= tau * own:"),
     "recall_inverted": ("recall[l] = hit / own", "recall[l] = own / max(hit, 1)"),
+    "probe_from_zero": ("return np.arange((Lq - 1) % stride, Lq, stride)", "return np.arange(0, Lq, stride)"),
+    "probe_no_pos0": ('lay["k_I"], pos0 + int(t))', 'lay["k_I"], int(t))'),
+    "refresh_keeps_cache": ('                cache = indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k, pos0)\n                refreshed[l] = True', '                refreshed[l] = True'),
+    # codecs
+    "bf16_shift": ("u32 = bits.astype(np.uint32) << np.uint32(16)", "u32 = bits.astype(np.uint32) << np.uint32(15)"),
+    "e4m3_all_nan_top": ("return np.where((e == 15) & (m == 7), np.nan, val)", "return np.where(e == 15, np.nan, val)"),
+    "e4m3_no_sign": ("val = np.where(s == 1, -mag, mag)", "val = mag"),
+    # attention and distillation details
+    "skip_key_zero": ("sel = idx_t[idx_t >= 0]", "sel = idx_t[idx_t > 0]"),
+    "kl_unnormalised_r": ("log_r = log_r - math.log(np.exp(log_r).sum())", "log_r = log_r"),
+    "target_layer_mean": ("count += a.shape[0]", "count += 1"),
+    # decode
+    "decode_first_cache": ('one = {"q": lay["q"][b][None], "kv": lay["kv"][b]}',
+                           'one = {"q": lay["q"][b][None], "kv": lay["kv"][0]}'),
 }
 
 
-def main() -> int:
+def main(names=None) -> int:
     src = open(os.path.join(ROOT, ORACLE)).read()
     missed = []
     for name, (old, new) in MUTANTS.items():
+        if names and name not in names:
+            continue
         if src.count(old) < 1:
             print(f"{name:20s} PATTERN NOT IN THE ORACLE")
             missed.append(name)
@@ -84,4 +100,4 @@ def main() -> int:
 
 
 if __name__ == "__main__":
-    sys.exit(main())
+    sys.exit(main(set(sys.argv[1:])))

@@ -487,3 +487,16 @@ def test_dynamic_refresh_recall_by_hand():
         own += len(order)
     _, _, _, rec = O.run_stack_dynamic("FS", lay, k, stride=5, tau=0.0)
     assert rec[1] == hit / own
+
+
+def test_dynamic_refresh_probe_uses_absolute_positions():
+    """Queries continuing a cached prefix (pos0 > 0): the probe scores query t at its
+    absolute position pos0 + t, over keys 0..pos0 + t, exactly as the F layer did.  An S
+    layer whose indexer inputs are the F layer's therefore still has recall exactly 1."""
+    L, pos0, k = 12, 7, 4
+    rng = np.random.default_rng(3)
+    f = dict(q=rng.normal(size=(L, 1, 4)), kv=rng.normal(size=(pos0 + L, 2, 4)), q_I=rng.normal(size=(L, 2, 3)),
+             w=rng.uniform(size=(L, 2)), k_I=rng.normal(size=(pos0 + L, 3)))
+    _, used, ref, rec = O.run_stack_dynamic("FS", [f, dict(f)], k, stride=5, tau=1.0, pos0=pos0)
+    assert rec[1] == 1.0 and not ref[1]
+    assert np.array_equal(used[1], O.indexer_topk(f["q_I"], f["w"], f["k_I"], k, pos0))
