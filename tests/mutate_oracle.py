@@ -64,6 +64,9 @@ MUTANTS = {
     "skip_key_zero": ("sel = idx_t[idx_t >= 0]", "sel = idx_t[idx_t > 0]"),
     "kl_unnormalised_r": ("log_r = log_r - math.log(np.exp(log_r).sum())", "log_r = log_r"),
     "target_layer_mean": ("count += a.shape[0]", "count += 1"),
+    # query positions
+    "stack_no_pos0": ('indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k, pos0)', 'indexer_topk(lay["q_I"], lay["w"], lay["k_I"], k)'),
+    "row_pos_fixed": ("indexer_scores_row(q_I[t], w[t], k_I, pos0 + t)", "indexer_scores_row(q_I[t], w[t], k_I, pos0)"),
     # decode
     "decode_first_cache": ('one = {"q": lay["q"][b][None], "kv": lay["kv"][b]}',
                            'one = {"q": lay["q"][b][None], "kv": lay["kv"][0]}'),
