@@ -431,7 +431,9 @@ def gather_ceiling_ms(kv, idx3):
 def mfma_ceiling():
     """Sustained fp8 MFMA rate of this GPU, as fractions of the 5.0 PFLOP/s peak: a
     stream of independent 16x16x128 fp8 MFMAs (libicprobe.so) over constant operands,
-    and over random operands that change every iteration as the indexer's keys do."""
+    over random operands that change every iteration as the indexer's keys do, with the
+    indexer's own operand pattern, and with that pattern plus the indexer's vector
+    epilogue (its whole instruction mix without memory traffic)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "dsa_lightning_indexer_scores_amd", "libicprobe.so")
@@ -444,7 +446,7 @@ def mfma_ceiling():
     st = torch.cuda.current_stream()
     res = {}
     for name, rnd, per_iter in (("constant_operands", 0, 8), ("random_operands", 1, 8),
-                                ("indexer_operands", 2, 9)):
+                                ("indexer_operands", 2, 9), ("indexer_compute", 3, 9)):
         def launch():
             r = lib.icp_mfma_stream(rnd, blocks, iters, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(st.cuda_stream))
             if r != 0:
@@ -799,6 +801,10 @@ def main():
             # the indexer's own operand pattern (fixed q_I slabs, fresh keys from LDS each
             # tile, the linear-term MFMA): 8 of its 9 MFMAs per tile are the algorithmic work
             result["indexer_frac_of_sustained"] = round(kr["indexer"]["frac"] / (ceil["indexer_operands"] * 8 / 9), 4)
+            # the same stream with the indexer's vector epilogue (its whole arithmetic, no
+            # memory traffic, key-block loads or barriers): the ceiling of its instruction mix
+            if "indexer_compute" in ceil:
+                result["indexer_frac_of_compute_mix"] = round(kr["indexer"]["frac"] / (ceil["indexer_compute"] * 8 / 9), 4)
         sgbs = stream_read_gbs()
         if sgbs:
             result["hbm_stream_read_gbs"] = sgbs

@@ -11,7 +11,8 @@
 // limit, so the random stream sustains markedly less than the constant one.
 //
 // A third stream has the indexer's own operand pattern: fixed random q_I slabs, a fresh
-// random key tile from LDS every step and the scaled linear-term MFMA.
+// random key tile from LDS every step and the scaled linear-term MFMA; a fourth adds the
+// indexer's vector epilogue to it.
 //
 // This is measurement support only (built into libicprobe.so, loaded by the
 // benchmark); nothing on the indexer path uses it.
@@ -103,6 +104,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float s = cl[0] + cl[1] + cl[2] + cl[3];
     for (int j = 0; j < 8; ++j) s += c[j][0] + c[j][1] + c[j][2] + c[j][3];
     out[t] = s;                                      // keeps the stream live
+}
+
+// Lane row g of the result holds the sum of p_g over the four lane rows (three swaps, three
+// adds): four key tiles' head sums finished at once.
+__device__ __forceinline__ float lane_rows_sum4(float p0, float p1, float p2, float p3) {
+    const u32x2 a = __builtin_amdgcn_permlane16_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    const u32x2 b = __builtin_amdgcn_permlane16_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+    const float s01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const float s23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+    const u32x2 c = __builtin_amdgcn_permlane32_swap(__float_as_uint(s01), __float_as_uint(s23), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// The indexer's whole arithmetic with none of its memory traffic, per-block key loads or
+// barriers: the operand stream above (8 score MFMAs and the scaled linear-term MFMA per
+// 16-key tile, each tile's keys read from LDS one tile ahead) plus its vector epilogue,
+// pipelined the way the indexer runs it.  In stage t the MFMAs of tile t issue beside the
+// epilogue of tile t-1, each MFMA followed by four vector ops: per query the two linear-term
+// parts added, then one fma per head with |y| as a free input modifier (16 heads per lane).
+// After each block of 8 tiles the lane-row sums finish four tiles per query at once, and
+// their results are added into a register where the indexer stores its scores.  Its rate is
+// what the indexer's instruction mix sustains on this GPU.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void mfma_indexer_compute_kernel(
+    float* __restrict__ out, int nblocks) {
+    constexpr int TABLE = 64 * 1024;
+    constexpr int NKT = 8;                           // tiles per block, as the indexer's 128-key blocks
+    __shared__ __attribute__((aligned(32))) uint8_t keys[TABLE];
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    for (int i = threadIdx.x; i < TABLE / 4; i += 256)
+        reinterpret_cast<int*>(keys)[i] = random_e4m3x4(blockIdx.x * 65537u + (uint32_t)i * 3u + 11u);
+    i32x8 A[8], L;
+    for (int j = 0; j < 8; ++j)
+        for (int i = 0; i < 8; ++i) A[j][i] = random_e4m3x4(t * 131u + j * 17u + i);
+    for (int i = 0; i < 8; ++i) L[i] = random_e4m3x4(t * 313u + i + 5u);
+    float wr[2][16];                                 // head weights of the wave's two queries
+    for (int q = 0; q < 2; ++q)
+        for (int i = 0; i < 16; ++i) wr[q][i] = (float)(mix(t * 7u + q * 97u + i) & 0xffu) * (1.f / 512.f);
+    const int scale = 120 + (int)(mix(t) & 7u);
+    __syncthreads();
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const uint8_t* base = keys + wv * (TABLE / 4) + (lane & 15) * 160 + (lane >> 4) * 32;   // skewed rows
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    float sink = 0.f;
+    for (int b = 0; b < nblocks; ++b) {
+        f32x4 acc[2][8];
+        f32x4 lin[2];
+        float val[2][NKT];
+        i32x8 Bcur = *reinterpret_cast<const i32x8*>(base + (b % 6) * 2560);
+#pragma unroll
+        for (int kt = 0; kt <= NKT; ++kt) {
+            i32x8 Bnxt;
+            if (kt + 1 < NKT) Bnxt = *reinterpret_cast<const i32x8*>(base + ((b + kt + 1) % 6) * 2560);
+            if (kt < NKT) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    acc[kt & 1][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[j], Bcur, z, 0, 0, 0, 0, 0, 0);
+                lin[kt & 1] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(L, Bcur, z, 0, 0, 0, scale, 0, 127);
+            }
+            if (kt > 0) {
+                const f32x4& l = lin[(kt - 1) & 1];
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    float v = l[2 * q] + l[2 * q + 1];
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) v = fmaf(wr[q][4 * ht + e], fabsf(acc[(kt - 1) & 1][4 * q + ht][e]), v);
+                    val[q][kt - 1] = v;
+                }
+            }
+            if (kt + 1 < NKT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            if (kt > 0 && kt < NKT) {
+#pragma unroll
+                for (int i = 0; i < 9; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+                }
+            }
+            if (kt > 0) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) asm volatile("" : "+v"(val[q][kt - 1]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < NKT) Bcur = Bnxt;
+        }
+#pragma unroll
+        for (int grp = 0; grp < NKT / 4; ++grp)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                sink += lane_rows_sum4(val[q][4 * grp], val[q][4 * grp + 1], val[q][4 * grp + 2], val[q][4 * grp + 3]);
+    }
+    out[t] = sink;                                   // keeps the stream live
 }
 
 // Grid-stride 16-byte reads of n16 vectors; one word per thread keeps the loads live.
@@ -237,12 +330,16 @@ extern "C" __attribute__((visibility("default"))) int icp_stream_read(const void
 
 // Launches `blocks` workgroups of 4 waves, each wave issuing 8 * iters fp8 MFMAs of
 // 16x16x128 (65536 flop each), or 9 * iters with random = 2 (the indexer's operand
-// pattern: 8 score MFMAs plus the linear-term one per key tile); out needs blocks * 256
+// pattern: 8 score MFMAs plus the linear-term one per key tile) or random = 3 (the same
+// with the indexer's vector epilogue; iters a multiple of 8); out needs blocks * 256
 // floats.  Returns a hipError_t.
 extern "C" __attribute__((visibility("default"))) int icp_mfma_stream(int random, int blocks, int iters, float* out,
                                                                      void* stream) {
     if (blocks < 1 || iters < 1 || out == nullptr) return (int)hipErrorInvalidValue;
-    if (random == 2)
+    if (random == 3) {
+        if (iters % 8 != 0) return (int)hipErrorInvalidValue;
+        hipLaunchKernelGGL(mfma_indexer_compute_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters / 8);
+    } else if (random == 2)
         hipLaunchKernelGGL(mfma_indexer_operands_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
     else if (random)
         hipLaunchKernelGGL(mfma_stream_kernel<true>, dim3(blocks), dim3(256), 0, (hipStream_t)stream, out, iters);
