@@ -158,6 +158,15 @@ def cmd_counters(a):
             out.append(f"lds_bank_conflict: {allv['SQ_LDS_BANK_CONFLICT'] / xcd_cycles / N_CU:.4f}")
         if "SQ_BUSY_CYCLES" in allv:
             out.append(f"sq_busy: {allv['SQ_BUSY_CYCLES'] / xcd_cycles / N_XCD:.3f}")
+    if allv.get("SQ_WAVE_CYCLES"):
+        fracs = [(k, c) for k, c in (("wave_wait_any_frac", "SQ_WAIT_ANY"), ("wave_wait_inst_any_frac", "SQ_WAIT_INST_ANY"),
+                                     ("wave_valu_active_frac", "SQ_ACTIVE_INST_VALU"),
+                                     ("wave_lds_active_frac", "SQ_ACTIVE_INST_LDS")) if c in allv]
+        if fracs:
+            out.append("# fractions of the waves' resident cycles (SQ_WAVE_CYCLES): waiting (on a dependency or a"
+                       " barrier), waiting to issue, and issuing VALU or LDS work")
+        for key, c in fracs:
+            out.append(f"{key}: {allv[c] / allv['SQ_WAVE_CYCLES']:.3f}")
     if "TA_TA_BUSY_sum" in allv and "TA_FLAT_READ_WAVEFRONTS_sum" in allv and allv["TA_FLAT_READ_WAVEFRONTS_sum"]:
         out.append(f"address_unit_cycles_per_load_instruction: "
                    f"{allv['TA_TA_BUSY_sum'] / allv['TA_FLAT_READ_WAVEFRONTS_sum']:.2f}")
