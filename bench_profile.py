@@ -141,8 +141,11 @@ def cmd_counters(a):
     out.append("# derived (plain keys, read by bench.py)")
     if dur and xcd_cycles:
         out.append(f"duration_us: {dur:.1f}")
-        out.append(f"# clock = GRBM_GUI_ACTIVE / 8 / duration")
-        out.append(f"clock_ghz: {xcd_cycles / (dur * 1e3):.3f}")
+        if dur >= 100.0:
+            out.append(f"# clock = GRBM_GUI_ACTIVE / 8 / duration")
+            out.append(f"clock_ghz: {xcd_cycles / (dur * 1e3):.3f}")
+        else:
+            out.append("# no clock: GRBM_GUI_ACTIVE also counts the dispatch around a kernel this short")
     if xcd_cycles:
         if "SQ_VALU_MFMA_BUSY_CYCLES" in allv:
             out.append("# mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (per-XCD cycles * 1024 SIMDs) (rocprofv3 MfmaUtil)")
