@@ -8,7 +8,7 @@ import torch
 import oracle as O
 import dsa_lightning_indexer_scores_amd as ic
 from dsa_lightning_indexer_scores_amd import synth
-from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, summary
+from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, gpu_score_rows, summary
 
 pytestmark = pytest.mark.gpu
 
@@ -59,8 +59,11 @@ def test_stack_fs_vs_oracle(case):
     worst = 0.0
     for b in range(B):
         f = {kk: dec(v[b]) for kk, v in layers[0].items()}
+        g = {kk: v[b:b + 1] for kk, v in gpu[0].items()}
+        sc = gpu_score_rows(g["q_I"], g["w"], g["k_I"], range(Lq), chunk or 4096, pos0)
         for t in range(Lq):
-            c, o, _ = check_topk_row(idx[b, t], f["q_I"][t], f["w"][t], f["k_I"], pos0 + t, k, H_I, d_I)
+            c, o, _ = check_topk_row(idx[b, t], f["q_I"][t], f["w"][t], f["k_I"], pos0 + t, k, H_I, d_I,
+                                     gpu_scores=sc[t])
             n_cert += c
             n_rows += 1
             ovl.append(o)

@@ -18,7 +18,7 @@ import torch
 import oracle as O
 import dsa_lightning_indexer_scores_amd as ic
 from dsa_lightning_indexer_scores_amd import synth
-from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, sample_rows, summary
+from parity_helpers import ATTN_TOL, attn_rel_err, check_topk_row, dec, gpu_score_rows, sample_rows, summary
 
 pytestmark = pytest.mark.gpu
 
@@ -135,7 +135,8 @@ def test_signed_w_gaussian_fp8_partial_heads():
 @pytest.mark.parametrize("name", ["pair8k", "stack32k"])
 def test_signed_w_gaussian_full_size_sampled(name):
     """The full-size shapes in the stack's launch configuration with w ~ N(0, 1) in place of
-    U(0, 1): sampled rows certified against the oracle, overlap >= 0.99."""
+    U(0, 1): every sampled row through the two-stage check on the GPU's own scores, rows
+    certified against the oracle where its scores separate, overlap >= 0.99."""
     cfg = synth.WORKLOADS[name]
     print(f"[signed] {name}: generating inputs", flush=True)
     layers = synth.prefill_stack(cfg, device="cuda", pattern="FS")
@@ -151,9 +152,11 @@ def test_signed_w_gaussian_full_size_sampled(name):
     k_I = dec(layers[0]["k_I"][0])
     q_I = dec(layers[0]["q_I"][0][sel])
     w = dec(layers[0]["w"][0][sel])
+    scores = gpu_score_rows(layers[0]["q_I"], layers[0]["w"], layers[0]["k_I"], rows, cfg.chunk)
     cert, ovl = 0, []
     for i, t in enumerate(rows):
-        c, o, _ = check_topk_row(idx_np[t], q_I[i], w[i], k_I, int(t), cfg.k, cfg.H_I, cfg.d_I)
+        c, o, _ = check_topk_row(idx_np[t], q_I[i], w[i], k_I, int(t), cfg.k, cfg.H_I, cfg.d_I,
+                                 gpu_scores=scores[int(t)])
         cert += c
         ovl.append(o)
     worst = 0.0
