@@ -5,6 +5,7 @@ times, on sampled rows the oracle computes one by one:
   stack32k   L=32768, 16 layers 'FSSS'x4, fp8 indexer, k=2048, chunk 4096
   long128k   L=131072, 8 layers 'FSSSSSSS', fp8 indexer, 4096-query chunks
   decode64k  B=32, 65536 cached tokens, 24 layers 'FSSS'x6 (two steps)
+  dynamic    stack32k with a probe on every 64th query, at both refresh limits
 
 Inputs are the seeded tensors the benchmark uses, generated on the GPU by the
 input module and copied back for the oracle.  Every sampled F-layer row is checked
@@ -155,3 +156,46 @@ def test_decode64k_sampled():
                                                                 "attn_max_rel_err": worst})
             assert np.mean(ovl) >= 0.99 and worst <= ATTN_TOL
         del outs, layers, qs
+
+
+def test_stack32k_dynamic_refresh_limits():
+    """Dynamic refresh in the benchmark's configuration (stack32k, a probe on every 64th query,
+    the last query included), every layer bringing its own indexer inputs.  tau = 0 never
+    refreshes and must reproduce the static FSSS stack bit for bit; tau = 1.01 refreshes every
+    S layer and must reproduce the all-F stack bit for bit.  Each S layer's recall (taken before
+    its refresh) must equal, bit for bit, the pooled overlap sum |cached & own| / sum |own| over
+    the probe rows, counted here from each layer's own top-k (one F run per layer)."""
+    cfg = synth.WORKLOADS["stack32k"]
+    stride = 64
+    print("[full] stack32k dynamic: generating inputs", flush=True)
+    layers = synth.prefill_stack(cfg, device="cuda", pattern="F" * cfg.n_layers)
+    o_s, i_s, _ = ic.run_stack(cfg.pattern, layers, cfg.k)
+    o0, i0, st0, r0, _ = ic.run_stack_dynamic(cfg.pattern, layers, cfg.k, probe_stride=stride, tau=0.0)
+    torch.cuda.synchronize()
+    s_layers = [l for l, c in enumerate(cfg.pattern) if c == "S"]
+    assert st0["indexer_calls"] == cfg.pattern.count("F")
+    assert (r0[s_layers] == 0).all() and torch.equal(i0, i_s)
+    assert all(torch.equal(a, b) for a, b in zip(o0, o_s)), "tau = 0 differs from the static stack"
+    del o0, o_s
+    o_f, i_f, _ = ic.run_stack("F" * cfg.n_layers, layers, cfg.k)
+    o1, i1, _, r1, rec1 = ic.run_stack_dynamic(cfg.pattern, layers, cfg.k, probe_stride=stride, tau=1.01)
+    torch.cuda.synchronize()
+    assert (r1[s_layers] == 1).all() and torch.equal(i1, i_f)
+    assert all(torch.equal(a, b) for a, b in zip(o1, o_f)), "tau = 1.01 differs from the all-F stack"
+    del o1, o_f
+    # each layer's own top-k on the probe rows
+    probe = torch.arange((cfg.L - 1) % stride, cfg.L, stride, device="cuda")
+    own = []
+    for lay in layers:
+        idx_l = ic.indexer_topk(lay["q_I"], lay["w"], lay["k_I"], cfg.k)
+        own.append(idx_l[0, probe].cpu().numpy())
+        del idx_l
+    got = rec1.cpu().numpy()[:, 0]
+    for l in s_layers:
+        hit = n_own = 0
+        for cached, mine in zip(own[l - 1], own[l]):     # the cache holds layer l - 1's own top-k
+            mine = mine[mine >= 0]
+            hit += np.intersect1d(cached[cached >= 0], mine, assume_unique=True).size
+            n_own += mine.size
+        assert got[l] == np.float32(hit / n_own), f"layer {l}: recall {got[l]} != {hit}/{n_own}"
+    summary("stack32k dynamic", {"probe_rows": int(probe.numel()), "recall": [round(float(got[l]), 4) for l in s_layers]})
