@@ -348,25 +348,12 @@ def bench_varlen(n_seq: int = 64, q_new: int = 512, Lk: int = 8192, seed: int = 
     continue a cached prefix of 0 .. Lk - q_new tokens, through the 16-layer FSSS stack with the
     stack32k layer shapes.  One ic_run_stack_varlen call (consecutive sequences share
     launches) against one ic_run_stack per sequence on the same tensors."""
-    import numpy as np
     import torch
     import dsa_lightning_indexer_scores_amd as ic
     from dsa_lightning_indexer_scores_amd import synth
     cfg = synth.WORKLOADS["stack32k"]
-    rng = np.random.default_rng(seed)
-    q_len = [q_new] * n_seq
-    pos0 = [int(x) for x in rng.integers(0, Lk - q_new + 1, size=n_seq)]
+    layers, q_len, pos0 = synth.ragged_stack(cfg, n_seq, q_new, Lk, seed, device="cuda")
     T = n_seq * q_new
-    g = torch.Generator(device="cuda").manual_seed(seed)
-    layers = []
-    for c in cfg.pattern:
-        lay = {"q": torch.randn((T, cfg.H, cfg.d), generator=g, device="cuda").to(torch.bfloat16),
-               "kv": torch.randn((n_seq, Lk, 2, cfg.d), generator=g, device="cuda").to(torch.bfloat16)}
-        if c in "F1":
-            lay["q_I"] = synth.encode(torch.randn((T, cfg.H_I, cfg.d_I), generator=g, device="cuda"), "fp8")
-            lay["w"] = torch.rand((T, cfg.H_I), generator=g, device="cuda")
-            lay["k_I"] = synth.encode(torch.randn((n_seq, Lk, cfg.d_I), generator=g, device="cuda"), "fp8")
-        layers.append(lay)
     outs = [torch.empty_like(l["q"]) for l in layers]
     idx = torch.empty((T, cfg.k), dtype=torch.int32, device="cuda")
     grouped = lambda: ic.run_stack_varlen(cfg.pattern, layers, cfg.k, q_len, pos0, outs=outs, idx_cache=idx)

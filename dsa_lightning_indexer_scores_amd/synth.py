@@ -195,6 +195,31 @@ def decode_queries(cfg: Workload, step: int, device="cuda", B: Optional[int] = N
     return layers
 
 
+def ragged_stack(cfg: Workload, n_seq: int = 64, q_new: int = 512, Lk: int = 8192, seed: int = 77,
+                 device="cuda"):
+    """The ragged prefill workload: n_seq sequences each bring q_new queries continuing a cached
+    prefix of 0 .. Lk - q_new tokens (uniform), through cfg's pattern with cfg's layer shapes.
+    Queries are packed over the sequences ([T, ...], T = n_seq * q_new) and caches are per
+    sequence ([n_seq, Lk, ...]).  N(0,1) values, w ~ U(0,1), e4m3 indexer inputs.
+    Returns (layers, q_len, pos0)."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    q_len = [q_new] * n_seq
+    pos0 = [int(x) for x in rng.integers(0, Lk - q_new + 1, size=n_seq)]
+    T = n_seq * q_new
+    g = torch.Generator(device=device).manual_seed(seed)
+    layers = []
+    for c in cfg.pattern:
+        lay = {"q": torch.randn((T, cfg.H, cfg.d), generator=g, device=device).to(torch.bfloat16),
+               "kv": torch.randn((n_seq, Lk, 2, cfg.d), generator=g, device=device).to(torch.bfloat16)}
+        if c in "F1":
+            lay["q_I"] = encode(torch.randn((T, cfg.H_I, cfg.d_I), generator=g, device=device), "fp8")
+            lay["w"] = torch.rand((T, cfg.H_I), generator=g, device=device)
+            lay["k_I"] = encode(torch.randn((n_seq, Lk, cfg.d_I), generator=g, device=device), "fp8")
+        layers.append(lay)
+    return layers, q_len, pos0
+
+
 def bits_u16(x: torch.Tensor):
     """bf16 tensor -> numpy uint16 bit patterns (raw storage, no conversion)."""
     return x.detach().cpu().contiguous().view(torch.int16).numpy().view("uint16")

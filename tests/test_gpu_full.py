@@ -6,6 +6,7 @@ times, on sampled rows the oracle computes one by one:
   long128k   L=131072, 8 layers 'FSSSSSSS', fp8 indexer, 4096-query chunks
   decode64k  B=32, 65536 cached tokens, 24 layers 'FSSS'x6 (two steps)
   dynamic    stack32k with a probe on every 64th query, at both refresh limits
+  ragged     64 sequences x 512 new tokens on cached prefixes, 16 layers 'FSSS'x4
 
 Inputs are the seeded tensors the benchmark uses, generated on the GPU by the
 input module and copied back for the oracle.  Every sampled F-layer row is checked
@@ -199,3 +200,66 @@ def test_stack32k_dynamic_refresh_limits():
             n_own += mine.size
         assert got[l] == np.float32(hit / n_own), f"layer {l}: recall {got[l]} != {hit}/{n_own}"
     summary("stack32k dynamic", {"probe_rows": int(probe.numel()), "recall": [round(float(got[l]), 4) for l in s_layers]})
+
+
+def test_ragged_prefill_sampled():
+    """The ragged prefill the benchmark times (64 sequences x 512 new tokens continuing prefixes
+    of 0..7680, 16 layers 'FSSS'x4 with the stack32k shapes): the grouped call bitwise equal to
+    one run_stack per sequence, and sampled rows of four sequences through the two-stage check
+    and the attention bar against the oracle."""
+    cfg = synth.WORKLOADS["stack32k"]
+    print("[full] ragged: generating inputs", flush=True)
+    layers, q_len, pos0 = synth.ragged_stack(cfg, device="cuda")
+    outs, idx, st = ic.run_stack_varlen(cfg.pattern, layers, cfg.k, q_len, pos0)
+    torch.cuda.synchronize()
+    assert st["indexer_calls"] == cfg.pattern.count("F") and st["attn_calls"] == cfg.n_layers
+    n_seq, q_new = len(q_len), q_len[0]
+    per_seq = []
+    for b in range(n_seq):
+        q0 = b * q_new
+        one = []
+        for lay in layers:
+            o = {"q": lay["q"][q0:q0 + q_new].unsqueeze(0), "kv": lay["kv"][b:b + 1]}
+            if "q_I" in lay:
+                o.update(q_I=lay["q_I"][q0:q0 + q_new].unsqueeze(0), w=lay["w"][q0:q0 + q_new].unsqueeze(0),
+                         k_I=lay["k_I"][b:b + 1])
+            one.append(o)
+        o1, i1, _ = ic.run_stack(cfg.pattern, one, cfg.k, pos0=pos0[b])
+        torch.cuda.synchronize()
+        assert torch.equal(i1[0], idx[q0:q0 + q_new]), f"sequence {b}: idx differ from its own run"
+        for l in range(cfg.n_layers):
+            assert torch.equal(o1[l][0], outs[l][q0:q0 + q_new]), f"sequence {b} layer {l}: output differs"
+        per_seq.append(one)
+        del o1, i1
+    rng = np.random.default_rng(17)
+    cert = n_rows = 0
+    ovl, worst = [], 0.0
+    for b in (0, 21, 42, 63):
+        q0, one = b * q_new, per_seq[b]
+        rows = sorted({0, 1, q_new // 2, q_new - 1, *rng.integers(0, q_new, size=6).tolist()})
+        idx_b = idx[q0:q0 + q_new].cpu().numpy()
+        for g0 in (0, 12):                               # the first and the last F layer's group
+            f = one[g0]
+            scores = gpu_score_rows(f["q_I"], f["w"], f["k_I"], rows, cfg.chunk, pos0[b])
+            k_I = dec(f["k_I"][0])
+            # the F layer's idx: the stack's cache holds the last group's rows; rerun the first group
+            if g0 == 0:
+                _, ig, _ = ic.run_stack("FSSS", one[:4], cfg.k, pos0=pos0[b])
+                idx_g = ig[0].cpu().numpy()
+            else:
+                idx_g = idx_b
+            for t in rows:
+                c, o, _ = check_topk_row(idx_g[t], dec(f["q_I"][0, t]), dec(f["w"][0, t]), k_I, pos0[b] + t, cfg.k,
+                                         cfg.H_I, cfg.d_I, gpu_scores=scores[t])
+                cert += c
+                n_rows += 1
+                ovl.append(o)
+                sel = idx_g[t][idx_g[t] >= 0]
+                for l in range(g0, g0 + 4):
+                    kv_sel = dec(one[l]["kv"][0].index_select(0, torch.as_tensor(sel, device="cuda").long()))
+                    ref = O.sparse_attn_row(dec(one[l]["q"][0, t]), kv_sel, np.arange(len(sel), dtype=np.int32),
+                                            1.0 / np.sqrt(cfg.d))
+                    worst = max(worst, attn_rel_err(dec(outs[l][q0 + t]), ref))
+    summary("ragged prefill", {"two_stage_exact": f"{n_rows}/{n_rows}", "certified": f"{cert}/{n_rows}",
+                               "mean_overlap": float(np.mean(ovl)), "attn_max_rel_err": worst})
+    assert np.mean(ovl) >= 0.99 and worst <= ATTN_TOL
