@@ -131,6 +131,11 @@ def test_decode64k_sampled():
         outs, idx_last, st = ic.decode_step(cfg.pattern, layers, sl, cfg.k)
         torch.cuda.synchronize()
         assert st["indexer_calls"] == 6 and st["attn_calls"] == 24
+        if step == 0:                                    # the no-allocation entry point at full size
+            o_st, i_st, _ = ic.decode_step_static(cfg.pattern, layers, sl, cfg.k)
+            torch.cuda.synchronize()
+            assert torch.equal(i_st, idx_last) and all(torch.equal(a, b) for a, b in zip(o_st, outs))
+            del o_st, i_st
         for g0 in (0, 20):
             grp = layers[g0:g0 + 4]
             go, gidx, _ = ic.decode_step("FSSS", grp, sl, cfg.k)
@@ -140,6 +145,8 @@ def test_decode64k_sampled():
             idx_np = gidx.cpu().numpy()[:, 0]
             f = grp[0]
             sc = ic.decode_indexer_scores(f["q_I"], f["w"], f["k_I"], sl).cpu().numpy()   # the step's scores
+            for b in range(cfg.B):                       # every sequence: idx = the oracle's top-k of its scores
+                assert np.array_equal(idx_np[b], O.topk_row(sc[b, :n], cfg.k)), f"step {step} sequence {b}"
             cert, ovl, worst = 0, [], 0.0
             for b in (0, 17, 31):
                 c, o, _ = check_topk_row(idx_np[b], dec(f["q_I"][b, 0]), dec(f["w"][b, 0]), dec(f["k_I"][b, :n]),
